@@ -1,0 +1,39 @@
+// Internal launchers (host side).  The C ABI in kaio_abi.cpp validates every
+// argument before calling these; the launchers assume valid, non-empty problems.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/kaio.h"
+
+namespace kaio {
+
+struct QkvProblem {
+  const uint16_t* x;        // f16 [m, k]
+  const uint32_t* w[3];     // u32 [k/8, n]
+  const uint16_t* s[3];     // f16 [k/128, n]
+  uint16_t* out[3];         // f16 [m, n]
+  uint32_t m, n, k;
+};
+
+// Tile geometry, shared with the host-side grid-size checks.
+constexpr uint32_t kPrefillBM = 128;   // rows of x per workgroup
+constexpr uint32_t kPrefillBN = 64;    // columns of each output per workgroup
+constexpr uint32_t kDecodeMaxM = 8;    // m <= this runs the decode kernel
+constexpr uint32_t kDecodeBN = 64;     // columns of one output per decode workgroup
+constexpr uint32_t kGemmBM = 256;
+constexpr uint32_t kGemmBN = 256;
+constexpr uint64_t kMaxWorkgroups = (1ull << 24) - 1;  // 1-D grid limit at 256 threads
+
+hipError_t launch_qkv_prefill(const QkvProblem& p, hipStream_t stream);
+hipError_t launch_qkv_decode(const QkvProblem& p, hipStream_t stream);
+hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t stream);
+hipError_t launch_gemm_f16f32(const uint16_t* a, const uint16_t* b, float* c,
+                              uint32_t m, uint32_t n, uint32_t k, hipStream_t stream);
+hipError_t launch_dequant_group_bwd(kaio_dtype dtype, int64_t outer, int64_t axis,
+                                    int64_t group, const void* dy, const void* scale,
+                                    void* dq, hipStream_t stream);
+
+}  // namespace kaio

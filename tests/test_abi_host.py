@@ -1,0 +1,163 @@
+"""C-ABI boundary on the host: the library loads, exports every declared entry
+point, and rejects every invalid call before touching a device.
+
+Pointers here are fake addresses that are never dereferenced: each call is
+built to fail validation, or (without a GPU) the device check.  Tests that
+would pass validation are skipped when a GPU is visible.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import int4_group_quantized_w4a16_amd as kaio
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kaio.h")
+OK, ARG, PROB, UNSUP, DEVICE = 0, 1, 2, 3, 4
+A = 0x100000          # a fake, 16-byte aligned device address
+STEP = 0x10000000     # spacing that keeps fake buffers disjoint
+
+
+def gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+no_gpu_only = pytest.mark.skipif(gpu_visible(), reason="fake pointers would reach a real launch")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kaio_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) >= {"kaio_qkv_w4a16", "kaio_gemm_f16f32", "kaio_dequant_group_bwd", "kaio_last_error"}
+    L = ctypes.CDLL(kaio.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert kaio.kaio_version().startswith("kaio-mi355x")
+
+
+def qkv(x=A, w=(A + STEP, A + 2 * STEP, A + 3 * STEP), s=(A + 4 * STEP, A + 5 * STEP, A + 6 * STEP),
+        o=(A + 7 * STEP, A + 8 * STEP, A + 9 * STEP), m=4, n=64, k=256, g=128):
+    st = kaio.lib().kaio_qkv_w4a16(x, *w, *s, *o, m, n, k, g, None)
+    return st, kaio.kaio_last_error()
+
+
+def test_qkv_validation_order_and_messages():
+    st, msg = qkv(g=64)
+    assert st == UNSUP and msg.startswith("kaio::qkv_w4a16:") and "group_size" in msg
+    st, msg = qkv(k=200)
+    assert st == PROB and "multiple of group_size" in msg
+    st, msg = qkv(k=64)
+    assert st == PROB
+    assert qkv(m=0)[0] == OK and qkv(n=0)[0] == OK
+    assert qkv(m=0, o=(0, 0, 0))[0] == OK                       # empty: pointers not needed
+    st, msg = qkv(o=(0, A + 8 * STEP, A + 9 * STEP))
+    assert st == ARG and "output q is null" in msg
+    st, msg = qkv(x=0)
+    assert st == ARG and "input x is null" in msg
+    st, msg = qkv(w=(A + STEP, 0, A + 3 * STEP))
+    assert st == ARG and "w_k_packed" in msg
+    st, msg = qkv(s=(A + 4 * STEP, A + 5 * STEP, 0))
+    assert st == ARG and "scales_v" in msg
+    st, msg = qkv(x=A + 8)
+    assert st == ARG and "aligned" in msg
+    st, msg = qkv(o=(A + 7 * STEP, A + 7 * STEP, A + 9 * STEP))
+    assert st == ARG and "overlaps" in msg
+    st, msg = qkv(o=(A + 96, A + 8 * STEP, A + 9 * STEP))       # q inside x (x is 4*256*2 bytes)
+    assert st == ARG and "overlaps x" in msg
+    st, msg = qkv(m=2 ** 32 - 1, n=2 ** 32 - 1)
+    assert st == PROB and "too large" in msg
+
+
+@no_gpu_only
+def test_qkv_valid_call_without_gpu_reports_device():
+    st, msg = qkv()
+    assert st == DEVICE and "no CPU fallback" in msg
+    st, _ = qkv(k=0)            # k == 0 writes zeros: still needs the device
+    assert st == DEVICE
+
+
+def gemm(a=A, b=A + STEP, c=A + 2 * STEP, m=8, n=8, k=8):
+    return kaio.lib().kaio_gemm_f16f32(a, b, c, m, n, k, None), kaio.kaio_last_error()
+
+
+def test_gemm_validation():
+    assert gemm(m=0)[0] == OK and gemm(n=0, c=0)[0] == OK
+    st, msg = gemm(c=0)
+    assert st == ARG and msg.startswith("kaio::gemm_f16f32:") and "output c is null" in msg
+    assert gemm(a=0)[0] == ARG and gemm(b=0)[0] == ARG
+    assert gemm(c=A + 2 * STEP + 4)[0] == ARG
+    st, msg = gemm(c=A + 64)
+    assert st == ARG and "overlaps a" in msg
+    st, msg = gemm(m=2 ** 32 - 1, n=2 ** 32 - 1)
+    assert st == PROB
+
+
+@no_gpu_only
+def test_gemm_without_gpu_reports_device():
+    assert gemm()[0] == DEVICE
+    assert gemm(a=0, b=0, k=0)[0] == DEVICE   # k == 0: inputs unused, zeros still need the device
+
+
+def bwd(dt=0, outer=4, axis=256, g=128, dy=A, sc=A + STEP, dq=A + 2 * STEP):
+    return kaio.lib().kaio_dequant_group_bwd(dt, outer, axis, g, dy, sc, dq, None, 0, None), kaio.kaio_last_error()
+
+
+def test_dequant_validation():
+    st, msg = bwd(dt=7)
+    assert st == UNSUP and msg.startswith("kaio::dequant_group_bwd:")
+    assert bwd(outer=-1)[0] == PROB and bwd(axis=-128)[0] == PROB
+    st, msg = bwd(g=0)
+    assert st == PROB and "group_size" in msg
+    assert bwd(g=-4)[0] == PROB
+    st, msg = bwd(axis=200, g=128)
+    assert st == PROB and "multiple" in msg
+    assert bwd(outer=0, dy=0, sc=0, dq=0)[0] == OK
+    assert bwd(axis=0, dy=0, sc=0, dq=0)[0] == OK
+    assert bwd(dy=0)[0] == ARG and bwd(sc=0)[0] == ARG and bwd(dq=0)[0] == ARG
+    st, msg = bwd(dt=0, dy=A + 2)
+    assert st == ARG and "aligned" in msg
+    st, msg = bwd(dq=A + 64)
+    assert st == ARG and "overlaps d_output" in msg
+    st, msg = bwd(dq=A + STEP + 8)
+    assert st == ARG and "overlaps scale" in msg
+
+
+@no_gpu_only
+def test_dequant_without_gpu_reports_device():
+    for dt in (0, 1, 2, 3):
+        assert bwd(dt=dt)[0] == DEVICE
+    assert bwd(dt=1, dy=A + 2, dq=A + 2 * STEP + 2)[0] == DEVICE   # element-aligned bf16 is accepted
+
+
+def test_last_error_is_per_thread_and_cleared_on_success():
+    import threading
+    qkv(g=64)
+    assert "group_size" in kaio.kaio_last_error()
+    seen = []
+    th = threading.Thread(target=lambda: seen.append(kaio.kaio_last_error()))
+    th.start(); th.join()
+    assert seen == [""]
+    assert qkv(m=0)[0] == OK and kaio.kaio_last_error() == ""
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 128, dtype=torch.float16)
+    w = torch.zeros(16, 8, dtype=torch.int32)
+    s = torch.zeros(1, 8, dtype=torch.float16)
+    with pytest.raises(ValueError, match="no CPU fallback"):
+        kaio.kaio_qkv_w4a16(x, w, w, w, s, s, s)
+    with pytest.raises(ValueError, match="no CPU fallback"):
+        kaio.kaio_gemm_f16f32(torch.zeros(2, 2, dtype=torch.float16), torch.zeros(2, 2, dtype=torch.float16))
+    with pytest.raises(ValueError, match="no CPU fallback"):
+        kaio.kaio_dequant_group_bwd(torch.zeros(2, 4), torch.zeros(2, 1), 4)

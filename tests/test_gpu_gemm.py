@@ -1,0 +1,66 @@
+"""Dense f16 x f16 -> f32 GEMM on the GPU against the CPU oracle (through the C ABI).
+Tolerance: |c - C*| <= 1e-5 * sum_k |a_ik * b_kj|; exact cases bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import int4_group_quantized_w4a16_amd as kaio
+from int4_group_quantized_w4a16_amd import workloads
+from oracle import compare
+from oracle.gemm import gemm, gemm_at
+from tests.conftest import load_golden
+from tests.gpu_util import DEV, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def run(a, b):
+    c = kaio.kaio_gemm_f16f32(to_dev(a), to_dev(b))
+    torch.cuda.synchronize()
+    return to_host(c)
+
+
+def test_golden_handworked_bitwise():
+    for case in load_golden("gemm_handworked.json")["cases"]:
+        a = np.array(case["a"], dtype=np.float16)
+        b = np.array(case["b"], dtype=np.float16)
+        assert np.array_equal(run(a, b), np.array(case["c"], dtype=np.float32))
+
+
+def test_identity_and_exact_integers():
+    rng = np.random.default_rng(1)
+    a = rng.standard_normal((64, 96)).astype(np.float16)
+    assert np.array_equal(run(a, np.eye(96, dtype=np.float16)), a.astype(np.float32))
+    ai = rng.integers(-8, 9, size=(300, 1024)).astype(np.float16)
+    bi = rng.integers(-8, 9, size=(1024, 260)).astype(np.float16)
+    c, _ = gemm(ai, bi)
+    assert np.array_equal(run(ai, bi), c.astype(np.float32))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 7), (300, 200, 100), (257, 259, 72), (100, 100, 4096),
+                                   (513, 300, 520), (16, 1000, 33), (256, 256, 64)])
+def test_ragged_shapes(M, N, K):
+    a, b = workloads.gemm_inputs(M, N, K, seed=M + N + K)
+    c, t = gemm(a, b)
+    bad, ratio = compare.excess(run(a, b), c, compare.gemm_tolerance(t))
+    assert bad == 0, f"{bad} outside tolerance, max ratio {ratio:.3f}"
+
+
+def test_empty_reduction_writes_zeros():
+    c = torch.full((33, 17), float("nan"), dtype=torch.float32, device=DEV)
+    kaio.kaio_gemm_f16f32(torch.empty((33, 0), dtype=torch.float16, device=DEV),
+                          torch.empty((0, 17), dtype=torch.float16, device=DEV), c)
+    torch.cuda.synchronize()
+    assert (c == 0).all()
+
+
+def test_config_4096_sampled():
+    cfg = workloads.GEMM_4096
+    a, b = workloads.gemm_inputs(cfg["M"], cfg["N"], cfg["K"], cfg["seed"])
+    got = run(a, b)
+    rows, cols = workloads.gemm_check_positions(cfg["M"], cfg["N"], 4096, cfg["check_seed"])
+    c, t = gemm_at(a, b, rows, cols)
+    bad, ratio = compare.excess(got[rows, cols], c, compare.gemm_tolerance(t))
+    assert bad == 0, f"{bad} outside tolerance, max ratio {ratio:.3f}"
+    print(f"gemm 4096^3 ({rows.size} entries): max |d|/tol = {ratio:.4f}")
+    assert np.array_equal(run(a, b), got)          # run-to-run identical
