@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 fused-QKV hot path on one MI355X.
+
+A step is one kaio_qkv_w4a16 call on the prefill workload
+(x f16[2048,4096], three packed-INT4 u32[512,4096] weights, three
+f16[32,4096] scales, group 128 -> Q, K, V f16[2048,4096]); ``value`` is its
+throughput in TFLOP/s (2*M*N*K*3 algorithmic flops per call).  The same JSON
+line carries:
+
+* ``roofline``     the prefill kernel against the dense f16 MFMA peak;
+* ``secondary``    decode (8 rows, weights rotated over 21 sets so every call
+                   streams from HBM), the dense 4096^3 GEMM and the dequant
+                   backward (f32 and bf16, [16384, 8192], g=128), each against
+                   its own roof;
+* ``cpu_baseline`` the float64 CPU oracle timed on this host's cores over a
+                   bounded sample of the prefill rows.
+
+All inputs are seeded synthetic data already resident in device memory when
+a timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A16 QKV TFLOP/s (prefill), weight GB/s (decode), % of MI355X roofline"
+PEAK_F16_TFLOPS = 2500.0      # MI355X dense f16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(name: str) -> str:
+    path = os.path.join(ROOT, "int4_group_quantized_w4a16_amd", "csrc", name)
+    h = hashlib.sha256()
+    for p in (path, os.path.join(ROOT, "int4_group_quantized_w4a16_amd", "csrc", "common.hpp")):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def timed(fn, steps, warmup, stream):
+    """Average duration (ms) of fn() over `steps` back-to-back launches, HIP events on `stream`."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        fn(warmup + i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall
+
+
+def measured_traffic(kernel: str, src: str, algorithmic_bytes: float):
+    """HBM bytes per launch from committed rocprofv3 PMC counters, or None if absent/stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash(src):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s: float):
+    """The float64 oracle on a bounded sample of prefill rows, scaled to TFLOP/s."""
+    import numpy as np
+    from oracle.qkv import qkv_project
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    M, N, K = inp.shape
+    probe = min(M, 128)
+    t0 = time.perf_counter()
+    qkv_project(inp.x, inp.w, inp.s, rows=np.arange(probe), with_abs=False)
+    t_probe = time.perf_counter() - t0
+    # the probe's time includes the fixed cost of dequantizing the weights, so
+    # scaling it by rows over-estimates: a safe bound for the sample size
+    rows = M if t_probe * M / probe <= budget_s else max(probe, int(M * budget_s / (t_probe * M / probe)))
+    runs, spent = 0, 0.0
+    while runs == 0 or (spent < budget_s and runs < 50):
+        t0 = time.perf_counter()
+        qkv_project(inp.x, inp.w, inp.s, rows=np.arange(rows), with_abs=False)
+        spent += time.perf_counter() - t0
+        runs += 1
+    flops = 2.0 * rows * N * K * 3 * runs
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 oracle (numpy dequantize + f64 matmul), rows 0..{rows - 1} of the {M}-row "
+                      f"prefill workload, {runs} run(s), {spent:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "gemm", "bwd"], default="all")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library has no "
+              "multi-GPU path: the QKV projection would shard by output columns with no exchange)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import int4_group_quantized_w4a16_amd as kaio
+    from int4_group_quantized_w4a16_amd import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int32) if a.dtype == np.uint32 else a)).to(dev)
+    result = {}
+    secondary = {}
+
+    # ---- prefill: the step --------------------------------------------------------------
+    c = workloads.QKV_PREFILL
+    M, N, K = c["M"], c["N"], c["K"]
+    log(f"[bench] generating prefill inputs {M}x{N}x{K}")
+    inp = workloads.qkv_inputs(M, N, K, c["seed"])
+    x, w, s = t(inp.x), [t(a) for a in inp.w], [t(a) for a in inp.s]
+    outs = [torch.empty((M, N), dtype=torch.float16, device=dev) for _ in range(3)]
+    step = lambda i: kaio.kaio_qkv_w4a16(x, *w, *s, *outs)
+    flops = 2.0 * M * N * K * 3
+    ms, wall = timed(step, args.steps, args.warmup, stream)
+    tflops = flops / (ms * 1e-3) / 1e12
+    algo_bytes = inp.x.nbytes + sum(a.nbytes for a in inp.w) + sum(a.nbytes for a in inp.s) + 3 * M * N * 2
+    log(f"[bench] prefill: {ms * 1e3:.1f} us/call, {tflops:.1f} TFLOP/s ({tflops / PEAK_F16_TFLOPS:.1%} of peak)")
+    traffic = measured_traffic("qkv_prefill", "qkv_prefill.hip", algo_bytes)
+    result.update({
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "W4A16 fused QKV prefill: x f16[2048,4096], 3x packed int4 u32[512,4096], "
+                               "3x f16 scales [32,4096], group 128 -> Q,K,V f16[2048,4096]",
+                   "M": M, "N": N, "K": K, "group_size": 128},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_F16_TFLOPS, 4),
+                     "traffic": traffic, "algorithmic_flops": flops, "algorithmic_bytes": algo_bytes,
+                     "kernel": "qkv_prefill_kernel", "launch_us": round(ms * 1e3, 2)},
+    })
+    del x, w, s, outs
+
+    # ---- decode, rotated weights ---------------------------------------------------------
+    if args.only in ("all", "decode"):
+        c = workloads.QKV_DECODE
+        M, N, K, R = c["M"], c["N"], c["K"], c["rotate"]
+        log(f"[bench] generating {R} decode weight sets {M}x{N}x{K}")
+        dinp = workloads.qkv_inputs(M, N, K, c["seed"])
+        x = t(dinp.x)
+        sets = [(
+            [t(a) for a in dinp.w], [t(a) for a in dinp.s])]
+        for j in range(1, R):
+            wj, sj = workloads.qkv_weight_set(N, K, c["seed"] + j)
+            sets.append(([t(a) for a in wj], [t(a) for a in sj]))
+        outs = [torch.empty((M, N), dtype=torch.float16, device=dev) for _ in range(3)]
+        dstep = lambda i: kaio.kaio_qkv_w4a16(x, *sets[i % R][0], *sets[i % R][1], *outs)
+        dms, _ = timed(dstep, max(args.steps, 4 * R), 2 * R, stream)
+        dbytes = dinp.x.nbytes + sum(a.nbytes for a in dinp.w) + sum(a.nbytes for a in dinp.s) + 3 * M * N * 2
+        gbs = dbytes / (dms * 1e-3) / 1e9
+        log(f"[bench] decode: {dms * 1e3:.2f} us/call, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of HBM)")
+        secondary["qkv_decode"] = {
+            "workload": "x f16[8,4096], 3x u32[512,4096], 3x f16[32,4096]; 21 rotated weight sets",
+            "us_per_call": round(dms * 1e3, 3), "value": round(gbs, 1), "unit": "GB/s",
+            "bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": dbytes, "tflops": round(2.0 * M * N * K * 3 / (dms * 1e-3) / 1e12, 3),
+            "traffic": measured_traffic("qkv_decode", "qkv_decode.hip", dbytes)}
+        del sets, x, outs
+
+    # ---- dense GEMM ------------------------------------------------------------------------
+    if args.only in ("all", "gemm"):
+        c = workloads.GEMM_4096
+        M, N, K = c["M"], c["N"], c["K"]
+        a, b = workloads.gemm_inputs(M, N, K, c["seed"])
+        ad, bd = t(a), t(b)
+        cd = torch.empty((M, N), dtype=torch.float32, device=dev)
+        gms, _ = timed(lambda i: kaio.kaio_gemm_f16f32(ad, bd, cd), max(10, args.steps // 2), 3, stream)
+        gtf = 2.0 * M * N * K / (gms * 1e-3) / 1e12
+        log(f"[bench] gemm 4096^3: {gms * 1e3:.1f} us/call, {gtf:.1f} TFLOP/s")
+        secondary["gemm_f16f32"] = {"workload": "A f16[4096,4096] x B f16[4096,4096] -> C f32",
+                                    "us_per_call": round(gms * 1e3, 2), "value": round(gtf, 2),
+                                    "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_F16_TFLOPS,
+                                    "frac": round(gtf / PEAK_F16_TFLOPS, 4)}
+        del ad, bd, cd
+
+    # ---- dequant backward --------------------------------------------------------------------
+    if args.only in ("all", "bwd"):
+        c = workloads.DEQUANT_BWD
+        for dt, tdt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+            dy, sc = workloads.dequant_bwd_inputs(c["outer"], c["axis"], c["group"], c["seed"], dt)
+            if dt == "bf16":
+                dyd = torch.from_numpy(dy.view(np.int16)).to(dev).view(torch.bfloat16)
+                scd = torch.from_numpy(sc.view(np.int16)).to(dev).view(torch.bfloat16)
+            else:
+                dyd, scd = t(dy), t(sc)
+            dqd = torch.empty_like(dyd)
+            bms, _ = timed(lambda i: kaio.kaio_dequant_group_bwd(dyd, scd, c["group"], dqd),
+                           max(10, args.steps // 2), 3, stream)
+            nbytes = 2 * dy.nbytes + sc.nbytes
+            gbs = nbytes / (bms * 1e-3) / 1e9
+            log(f"[bench] dequant bwd {dt}: {bms * 1e3:.1f} us/call, {gbs:.0f} GB/s")
+            secondary[f"dequant_group_bwd_{dt}"] = {
+                "workload": f"dy, dq {dt}[16384,8192], scale [16384,64], g=128",
+                "us_per_call": round(bms * 1e3, 2), "value": round(gbs, 1), "unit": "GB/s", "bound": "hbm",
+                "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes}
+            del dyd, scd, dqd
+
+    result["secondary"] = secondary
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -15,8 +15,8 @@
 //   consecutive k per lane): stored as is, XOR-swizzled per 16-byte chunk.
 // * B [k,n] is N-contiguous; the B operand needs 8 consecutive k of one
 //   column.  Each thread loads an 8 (k) x 8 (n) block and transposes it in
-//   registers (16-bit lane shuffles), so LDS holds B^T [n][k] and the
-//   operand reads are plain 16-byte, conflict-free reads.
+//   registers (16-bit shuffles within the thread), so LDS holds B^T [n][k]
+//   and the operand reads are plain 16-byte, conflict-free reads.
 // * Epilogue: f32 stores straight from the accumulators.
 
 #include "common.hpp"
@@ -37,6 +37,11 @@ struct alignas(16) SmemGemm {
   uint4 a[BM * KCH];   // 32 KiB, [m][k-chunk] swizzled
   uint4 b[BN * KCH];   // 32 KiB, [n][k-chunk] swizzled (B transposed)
 };
+
+// B^T swizzle: chunk kc of column n lives in slot n*8 + (kc ^ bswz(n)).
+// Operand reads (8 lanes = 8 consecutive n) and the transposing writes
+// (8 lanes = 8 consecutive n-blocks, same j) both hit 8 distinct bank groups.
+__device__ __forceinline__ uint32_t bswz(uint32_t n) { return (n ^ (n >> 3)) & 7; }
 
 __device__ __forceinline__ uint32_t lo_pair(uint32_t r0, uint32_t r1) { return (r0 & 0xFFFFu) | (r1 << 16); }
 __device__ __forceinline__ uint32_t hi_pair(uint32_t r0, uint32_t r1) { return (r0 >> 16) | (r1 & 0xFFFF0000u); }
@@ -105,9 +110,8 @@ gemm_f16f32_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 8; ++i) { d[i][0] = rb[i].x; d[i][1] = rb[i].y; d[i][2] = rb[i].z; d[i][3] = rb[i].w; }
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const uint32_t j = (jj + nb) & 7;          // rotate so 8 adjacent lanes hit 8 bank groups
-      const uint32_t qd = j >> 1;
+    for (int j = 0; j < 8; ++j) {
+      const int qd = j >> 1;
       uint4 o;
       if (j & 1) {
         o = uint4{hi_pair(d[0][qd], d[1][qd]), hi_pair(d[2][qd], d[3][qd]),
@@ -117,7 +121,7 @@ gemm_f16f32_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
                   lo_pair(d[4][qd], d[5][qd]), lo_pair(d[6][qd], d[7][qd])};
       }
       const uint32_t n = nb * 8 + j;
-      sm.b[n * KCH + (kq ^ (n & 7))] = o;
+      sm.b[n * KCH + (kq ^ bswz(n))] = o;
     }
   };
 
@@ -141,7 +145,7 @@ gemm_f16f32_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
 #pragma unroll
       for (int c = 0; c < TT; ++c) {
         const uint32_t n = wn * WT + c * 16 + l16;
-        bf[c] = __builtin_bit_cast(half8_t, sm.b[n * KCH + (kc ^ (n & 7))]);
+        bf[c] = __builtin_bit_cast(half8_t, sm.b[n * KCH + (kc ^ bswz(n))]);
       }
 #pragma unroll
       for (int r = 0; r < TT; ++r) {

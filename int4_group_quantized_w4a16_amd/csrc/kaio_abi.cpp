@@ -123,7 +123,8 @@ kaio_status kaio_qkv_w4a16(const void* x, const uint32_t* w_q, const uint32_t* w
                               : (uint64_t)((m + kaio::kPrefillBM - 1) / kaio::kPrefillBM) *
                                     ((n + kaio::kPrefillBN - 1) / kaio::kPrefillBN);
   if (!bytes_of(m, n, 2, &out_bytes) || !bytes_of(m, k, 2, &x_bytes) || !bytes_of(k / 8, n, 4, &w_bytes) ||
-      !bytes_of(k / 128, n, 2, &s_bytes) || wgs > kaio::kMaxWorkgroups)
+      !bytes_of(k / 128, n, 2, &s_bytes) || wgs > kaio::kMaxWorkgroups || n >= kaio::kMaxN ||
+      k >= kaio::kMaxK)
     return fail(KAIO_ERR_INVALID_PROBLEM, op, "problem too large for one launch (m=%u, n=%u, k=%u)", m, n, k);
 
   const void* ins[7] = {x, w_q, w_k, w_v, s_q, s_k, s_v};

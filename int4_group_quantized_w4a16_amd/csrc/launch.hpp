@@ -20,7 +20,17 @@ struct QkvProblem {
 
 // Tile geometry, shared with the host-side grid-size checks.
 constexpr uint32_t kPrefillBM = 128;   // rows of x per workgroup
-constexpr uint32_t kPrefillBN = 64;    // columns of each output per workgroup
+#ifndef KAIO_PREFILL_WAVES
+#define KAIO_PREFILL_WAVES 8
+#endif
+#ifndef KAIO_PREFILL_STAGES
+#define KAIO_PREFILL_STAGES 2
+#endif
+constexpr int kPrefillWaves = KAIO_PREFILL_WAVES;    // waves per workgroup; each owns 16 columns of every output
+constexpr int kPrefillStages = KAIO_PREFILL_STAGES;  // depth of the LDS ring
+constexpr uint32_t kPrefillBN = 16 * kPrefillWaves;   // columns of each output per workgroup
+constexpr uint32_t kMaxN = 1u << 28;   // keeps 32-bit per-lane offsets in range
+constexpr uint32_t kMaxK = 1u << 24;
 constexpr uint32_t kDecodeMaxM = 8;    // m <= this runs the decode kernel
 constexpr uint32_t kDecodeBN = 64;     // columns of one output per decode workgroup
 constexpr uint32_t kGemmBM = 256;

@@ -7,23 +7,28 @@
 //
 // gfx950 design
 // -------------
-// * Workgroup = 4 waves, tile = 128 rows of x by 64 columns of EACH output.
-//   Wave w owns columns [16w, 16w+16) of all three outputs and all 128 rows,
-//   so the four waves share one x tile in LDS and never unpack the same
+// * Workgroup = WAVES waves, tile = 128 rows of x by 16*WAVES columns of EACH
+//   output.  Wave w owns columns [16w, 16w+16) of all three outputs and all
+//   128 rows, so the waves share one x tile in LDS and never unpack the same
 //   weight twice.
-// * x is staged per quantization group (128 k) into a double-buffered,
-//   XOR-swizzled LDS tile (16-byte chunk kc of row r lives in slot
-//   r*16 + (kc ^ (r & 15)), so the MFMA A reads are bank-conflict free).
-// * Weights go straight from global memory to registers: one u32 holds the
-//   eight consecutive k of one column that a lane feeds to one
-//   v_mfma_f32_16x16x32_f16 as its B operand, so each lane loads exactly the
-//   words it multiplies and unpacks them to exact f16 integers in registers.
+// * Everything a group needs -- the x tile, the packed weights, the scales --
+//   is staged into an NSTAGE-deep LDS ring with direct global->LDS loads (no
+//   registers, no VALU), NSTAGE-1 groups ahead of the MFMAs, one barrier per
+//   group.  No register ever waits on a global load, so the only waits on
+//   the vector-memory counter are the explicit ones at that barrier.
+// * x: chunk kc of row r lands in slot r*16 + (kc ^ (r & 15)), which makes
+//   the MFMA A-operand reads bank-conflict free.
+// * Weights: one u32 holds the eight consecutive k of one column that a lane
+//   feeds to one v_mfma_f32_16x16x32_f16 as its B operand.  Each lane's DMA
+//   fetches exactly the word it will multiply into its own LDS slot; the lane
+//   reads it back and unpacks it to exact f16 integers in registers.
 // * Scales are applied per group in f32: the four MFMAs of a group
 //   accumulate a fresh partial sum of x*q (exact small integers times f16
 //   activations), then acc += partial * scale.  Rounding q*scale to f16
 //   before the MFMA would cost up to 2^-12 relative per product, too much
 //   for the f16 output; the partial/scale split keeps every product exact.
-// * Epilogue: f32 -> f16 (RNE), transposed through LDS, 16-byte row stores.
+// * Epilogue: f32 -> f16 (RNE), transposed through LDS one output at a time,
+//   16-byte row stores.
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -31,31 +36,60 @@
 namespace kaio {
 namespace {
 
-constexpr int BM = kPrefillBM;          // 128
-constexpr int BN = kPrefillBN;          // 64
-constexpr int THREADS = 256;
+constexpr int BM = kPrefillBM;          // 128 rows per workgroup
 constexpr int RT = BM / 16;             // row tiles per wave
 constexpr int KC = kGroup / 8;          // 16-byte chunks per row per group
-constexpr int XPER = BM * KC / THREADS; // chunks staged per thread per group
-constexpr int OUT_LD = BN + 8;          // padded row of the epilogue tile (f16)
+constexpr int X_CHUNKS = BM * KC;       // 16-byte chunks of x per stage (32 KiB)
 
-static_assert(XPER * THREADS == BM * KC, "x tile must split evenly");
+#ifndef KAIO_PREFILL_TILE_MAJOR
+#define KAIO_PREFILL_TILE_MAJOR 2
+#endif
 
-struct alignas(16) SmemPrefill {
-  union {
-    uint4 x[2][BM * KC];
-    uint16_t out[3][BM][OUT_LD];
-  };
+#define KAIO_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define KAIO_GLOBAL(p) ((__attribute__((address_space(1))) const void*)(p))
+
+// Wait until at most N vector-memory operations of this wave are outstanding,
+// then barrier.  Unlike __syncthreads() this does not drain every in-flight
+// load (its release fence would wait for the prefetches too); the "memory"
+// clobber keeps the compiler from moving LDS accesses across it.  Loads
+// return in issue order, so "at most N outstanding" means everything but the
+// newest N has landed.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// One stage of the LDS ring, in 16-byte units:
+//   x     [X_CHUNKS]                       swizzled rows of x
+//   w     [3][4][WAVES][64] u32            word (q, ks) for lane l of wave w
+//   s     [3][WAVES][8] u32 pairs of f16   scales of the wave's 16 columns
+template <int WAVES>
+struct StageLayout {
+  static constexpr int kX = 0;
+  static constexpr int kW = X_CHUNKS;                          // uint4 offset
+  static constexpr int kS = kW + 3 * 4 * WAVES * 64 / 4;
+  static constexpr int kSize = kS + (3 * WAVES * 8 + 3) / 4;   // uint4 per stage
 };
 
-template <bool kVecOut>
-__global__ void __launch_bounds__(THREADS, 1)
+template <int WAVES, int NSTAGE, bool kAligned>
+__global__ void __launch_bounds__(WAVES * 64, 1)
 qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
-  __shared__ SmemPrefill sm;
+  constexpr int THREADS = WAVES * 64;
+  constexpr int BN = 16 * WAVES;
+  constexpr int XPER = X_CHUNKS / THREADS;       // x loads per thread per stage
+  constexpr int OUT_LD = BN + 8;                 // padded f16 row of the epilogue tile
+  using L = StageLayout<WAVES>;
+  // vector-memory operations per thread per stage: x, 12 weight words, 1 scale pair
+  constexpr int VM_PER_STAGE = XPER + 12 + (kAligned ? 1 : 0);
+  static_assert(XPER * THREADS == X_CHUNKS, "x stage must split evenly");
+  static_assert(BM * OUT_LD * 2 <= NSTAGE * L::kSize * 16, "epilogue tile must fit in the ring");
+  static_assert((NSTAGE - 2) * VM_PER_STAGE < 64, "vmcnt range");
+  extern __shared__ uint4 smem[];
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
-  const uint32_t wave = tid >> 6;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t kb = lane >> 4;          // 8-k block of the 32-k MFMA step
   const uint32_t l16 = lane & 15;
 
@@ -65,8 +99,51 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   const uint32_t M = p.m, N = p.n, K = p.k;
   const uint32_t G = K / kGroup;
 
+  // ---- per-lane DMA sources ---------------------------------------------------
+  const uint16_t* xblk = p.x + (size_t)m0 * K;
+  uint32_t xoff[XPER];         // element offset (within row block m0, group 0) of this lane's chunk
+#pragma unroll
+  for (int i = 0; i < XPER; ++i) {
+    const uint32_t slot = (i * WAVES + wave) * 64 + lane;
+    const uint32_t row = slot >> 4;
+    const uint32_t kc = (slot & 15) ^ (row & 15);
+    const uint32_t rowc = (m0 + row < M) ? row : (M - 1 - m0);   // rows past M: any valid row
+    xoff[i] = rowc * K + kc * 8;
+  }
   const uint32_t col = n0 + wave * 16 + l16;
-  const size_t colc = col < N ? col : N - 1;   // clamp: columns past N are computed, never stored
+  const uint32_t colc = col < N ? col : N - 1;   // columns past N are computed, never stored
+  const uint32_t woff = kb * N + colc;           // word offset inside a group's 16 packed rows
+  // scale pairs: lanes 0..23 fetch the f16 pair (2j, 2j+1) of output q = lane / 8
+  const uint32_t sq = lane >> 3, sj = lane & 7;
+  const uint32_t scol = n0 + wave * 16 + 2 * sj;
+  const uint32_t scolc = (scol < N) ? scol : (N >= 2 ? N - 2 : 0);   // N even on this path
+  // select (not index) the scale tensor: a lane-dependent index into the
+  // kernel arguments would be fetched from memory
+  const uint16_t* s_lane = sq == 0 ? p.s[0] : (sq == 1 ? p.s[1] : p.s[2]);
+
+  auto issue_stage = [&](uint32_t g, int buf) {
+    uint4* st = smem + buf * L::kSize;
+    const uint16_t* xsrc = xblk + (size_t)g * kGroup;
+#pragma unroll
+    for (int i = 0; i < XPER; ++i)
+      __builtin_amdgcn_global_load_lds(KAIO_GLOBAL(xsrc + xoff[i]),
+                                       KAIO_LDS(st + L::kX + (i * WAVES + wave) * 64), 16, 0, 0);
+    uint32_t* wst = reinterpret_cast<uint32_t*>(st + L::kW);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const uint32_t* wg = p.w[q] + (size_t)g * 16 * N;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        __builtin_amdgcn_global_load_lds(KAIO_GLOBAL(wg + ks * 4 * N + woff),
+                                         KAIO_LDS(wst + ((q * 4 + ks) * WAVES + wave) * 64), 4, 0, 0);
+    }
+    if (kAligned) {
+      uint32_t* sst = reinterpret_cast<uint32_t*>(st + L::kS);
+      if (lane < 24)
+        __builtin_amdgcn_global_load_lds(KAIO_GLOBAL(s_lane + (size_t)g * N + scolc),
+                                         KAIO_LDS(sst + wave * 24), 4, 0, 0);
+    }
+  };
 
   floatx4 acc[RT][3];
 #pragma unroll
@@ -74,135 +151,185 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
 #pragma unroll
     for (int q = 0; q < 3; ++q) acc[r][q] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  if (G > 0) {
-    uint4 xr[XPER];
-    uint32_t wr[3][4], wn[3][4];
-    float sr[3], sn[3];
+  // prologue: stages 0 .. NSTAGE-2 (clamped past the end so every stage issues
+  // the same number of loads and the waits below stay exact)
+#pragma unroll
+  for (int st = 0; st < NSTAGE - 1; ++st) issue_stage((uint32_t)st < G ? st : G - 1, st);
 
-    auto load_x = [&](uint32_t g) {
-#pragma unroll
-      for (int i = 0; i < XPER; ++i) {
-        const uint32_t c = i * THREADS + tid;
-        const uint32_t row = c >> 4, kc = c & 15;
-        const uint32_t grow = (m0 + row < M) ? m0 + row : M - 1;
-        xr[i] = *reinterpret_cast<const uint4*>(p.x + (size_t)grow * K + (size_t)g * kGroup + kc * 8);
-      }
-    };
-    auto store_x = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < XPER; ++i) {
-        const uint32_t c = i * THREADS + tid;
-        const uint32_t row = c >> 4, kc = c & 15;
-        sm.x[buf][row * KC + (kc ^ (row & 15))] = xr[i];
-      }
-    };
-    auto load_w = [&](uint32_t g, uint32_t (&w)[3][4], float (&s)[3]) {
-#pragma unroll
-      for (int q = 0; q < 3; ++q) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const size_t r = (size_t)g * 16 + ks * 4 + kb;
-          w[q][ks] = p.w[q][r * N + colc];
-        }
-        s[q] = h2f(p.s[q][(size_t)g * N + colc]);
-      }
-    };
+  for (uint32_t g = 0; g < G; ++g) {
+    // stage g has landed for this wave; after the barrier, for every wave
+    wait_vm_barrier<(NSTAGE - 2) * VM_PER_STAGE>();
+    // A clamped stage past the end lands in the slot of group g-1, which
+    // nobody reads again.
+    issue_stage(g + NSTAGE - 1 < G ? g + NSTAGE - 1 : G - 1, (g + NSTAGE - 1) % NSTAGE);
 
-    load_x(0);
-    load_w(0, wr, sr);
-    store_x(0);
+    const uint4* st = smem + (g % NSTAGE) * L::kSize;
+    const uint4* xs = st + L::kX;
+    const uint32_t* wst = reinterpret_cast<const uint32_t*>(st + L::kW);
+    float sf[3];
+    if (kAligned) {
+      const uint16_t* sst = reinterpret_cast<const uint16_t*>(st + L::kS);
+#pragma unroll
+      for (int q = 0; q < 3; ++q) sf[q] = h2f(sst[wave * 48 + q * 16 + l16]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 3; ++q) sf[q] = h2f(p.s[q][(size_t)g * N + colc]);
+    }
 
-    for (uint32_t g = 0; g < G; ++g) {
-      __syncthreads();
-      const int buf = g & 1;
-      const bool more = g + 1 < G;
-      if (more) {
-        load_x(g + 1);
-        load_w(g + 1, wn, sn);
-      }
-      const uint4* xs = sm.x[buf];
-      floatx4 part[RT][3];
+#if KAIO_PREFILL_TILE_MAJOR == 2
+    // Software-pipelined tile-major order.  Unpack the group's 12 weight
+    // words once; then per row tile r: fetch the A fragments of tile r+1,
+    // run tile r's three 4-deep MFMA chains, and fold tile r-1's finished
+    // partials into acc while those MFMAs execute.  Scheduling barriers keep
+    // the compiler from hoisting every tile's LDS reads (register blow-up).
+    half8_t bq[3][4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        half8_t bq[3];
+    for (int q = 0; q < 3; ++q)
 #pragma unroll
-        for (int q = 0; q < 3; ++q) bq[q] = unpack_int4x8(wr[q][ks]);
+      for (int ks = 0; ks < 4; ++ks) bq[q][ks] = unpack_int4x8(wst[((q * 4 + ks) * WAVES + wave) * 64 + lane]);
+    auto load_a = [&](int r, half8_t (&a)[4]) {
+      const uint32_t row = r * 16 + l16;
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
-          const uint32_t row = r * 16 + l16;
-          const uint32_t kc = ks * 4 + kb;
-          const half8_t a = __builtin_bit_cast(half8_t, xs[row * KC + (kc ^ (row & 15))]);
+      for (int ks = 0; ks < 4; ++ks)
+        a[ks] = __builtin_bit_cast(half8_t, xs[row * KC + ((ks * 4 + kb) ^ (row & 15))]);
+    };
+    half8_t abuf[2][4];
+    floatx4 pbuf[2][3];
+    load_a(0, abuf[0]);
 #pragma unroll
-          for (int q = 0; q < 3; ++q) {
-            part[r][q] = mfma16x16x32(a, bq[q], ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : part[r][q]);
-          }
-        }
-      }
+    for (int r = 0; r < RT; ++r) {
+      if (r + 1 < RT) load_a(r + 1, abuf[(r + 1) & 1]);
 #pragma unroll
-      for (int r = 0; r < RT; ++r)
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+          pbuf[r & 1][q] = mfma16x16x32(abuf[r & 1][ks], bq[q][ks],
+                                        ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : pbuf[r & 1][q]);
+      if (r > 0) {
 #pragma unroll
         for (int q = 0; q < 3; ++q)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[r][q][i] = __builtin_fmaf(part[r][q][i], sr[q], acc[r][q][i]);
-      if (more) {
-        store_x(buf ^ 1);
-#pragma unroll
-        for (int q = 0; q < 3; ++q) {
-          sr[q] = sn[q];
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) wr[q][ks] = wn[q][ks];
-        }
+          for (int i = 0; i < 4; ++i)
+            acc[r - 1][q][i] = __builtin_fmaf(pbuf[(r - 1) & 1][q][i], sf[q], acc[r - 1][q][i]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[RT - 1][q][i] = __builtin_fmaf(pbuf[(RT - 1) & 1][q][i], sf[q], acc[RT - 1][q][i]);
+  }
+#elif KAIO_PREFILL_TILE_MAJOR
+    // Unpack the group's 12 weight words once (4 k-steps x 3 outputs), then
+    // run each row tile's three 4-deep MFMA chains to completion and fold the
+    // scale immediately: the partial sums live for one row tile only.
+    half8_t bq[3][4];
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) bq[q][ks] = unpack_int4x8(wst[((q * 4 + ks) * WAVES + wave) * 64 + lane]);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const uint32_t row = r * 16 + l16;
+      half8_t a[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        a[ks] = __builtin_bit_cast(half8_t, xs[row * KC + ((ks * 4 + kb) ^ (row & 15))]);
+      floatx4 part[3];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+          part[q] = mfma16x16x32(a[ks], bq[q][ks], ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : part[q]);
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[r][q][i] = __builtin_fmaf(part[q][i], sf[q], acc[r][q][i]);
     }
   }
-
-  __syncthreads();   // every wave is done with the x buffers
-  // D layout of a 16x16 MFMA tile: lane holds column (lane & 15), rows 4*(lane >> 4) + i.
+#else
+    floatx4 part[RT][3];
 #pragma unroll
-  for (int r = 0; r < RT; ++r)
+    for (int ks = 0; ks < 4; ++ks) {
+      half8_t bq[3];
 #pragma unroll
-    for (int q = 0; q < 3; ++q)
+      for (int q = 0; q < 3; ++q) bq[q] = unpack_int4x8(wst[((q * 4 + ks) * WAVES + wave) * 64 + lane]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t row = r * 16 + 4 * kb + i;
-        sm.out[q][row][wave * 16 + l16] = __builtin_bit_cast(uint16_t, (_Float16)acc[r][q][i]);
+      for (int r = 0; r < RT; ++r) {
+        const uint32_t row = r * 16 + l16;
+        const uint32_t kc = ks * 4 + kb;
+        const half8_t a = __builtin_bit_cast(half8_t, xs[row * KC + (kc ^ (row & 15))]);
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+          part[r][q] = mfma16x16x32(a, bq[q], ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : part[r][q]);
       }
-  __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[r][q][i] = __builtin_fmaf(part[r][q][i], sf[q], acc[r][q][i]);
+  }
+#endif
 
-  if (kVecOut) {
-    constexpr int CH = BM * BN / 8;   // 16-byte chunks per output tile
+  // ---- epilogue: one output at a time through LDS -----------------------------
+  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
-    for (int q = 0; q < 3; ++q)
+  for (int q = 0; q < 3; ++q) {
+    __syncthreads();   // ring (or the previous output's tile) no longer read
+    // D layout of a 16x16 MFMA tile: lane holds column (lane & 15), rows 4*(lane >> 4) + i
 #pragma unroll
-      for (int i = 0; i < CH / THREADS; ++i) {
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        tile[(r * 16 + 4 * kb + i) * OUT_LD + wave * 16 + l16] =
+            __builtin_bit_cast(uint16_t, (_Float16)acc[r][q][i]);
+    __syncthreads();
+    uint16_t* out = p.out[q];
+    if (kAligned) {
+      constexpr int CPR = BN / 8;                    // 16-byte chunks per tile row
+#pragma unroll
+      for (int i = 0; i < BM * CPR / THREADS; ++i) {
         const uint32_t c = i * THREADS + tid;
-        const uint32_t row = c >> 3, cc = c & 7;
+        const uint32_t row = c / CPR, cc = c % CPR;
         const uint32_t gr = m0 + row, gc = n0 + cc * 8;
         if (gr < M && gc < N)
-          *reinterpret_cast<uint4*>(p.out[q] + (size_t)gr * N + gc) =
-              *reinterpret_cast<const uint4*>(&sm.out[q][row][cc * 8]);
+          *reinterpret_cast<uint4*>(out + (size_t)gr * N + gc) =
+              *reinterpret_cast<const uint4*>(tile + row * OUT_LD + cc * 8);
       }
-  } else {
-    for (int q = 0; q < 3; ++q)
+    } else {
       for (uint32_t e = tid; e < (uint32_t)(BM * BN); e += THREADS) {
         const uint32_t row = e / BN, c = e % BN;
         const uint32_t gr = m0 + row, gc = n0 + c;
-        if (gr < M && gc < N) p.out[q][(size_t)gr * N + gc] = sm.out[q][row][c];
+        if (gr < M && gc < N) out[(size_t)gr * N + gc] = tile[row * OUT_LD + c];
       }
+    }
   }
+}
+
+template <int WAVES, int NSTAGE, bool kAligned>
+hipError_t launch_variant(const QkvProblem& p, hipStream_t stream) {
+  constexpr int BN = 16 * WAVES;
+  const uint32_t mtiles = (p.m + BM - 1) / BM;
+  const uint32_t ntiles = (p.n + BN - 1) / BN;
+  const size_t lds = (size_t)NSTAGE * StageLayout<WAVES>::kSize * 16;
+  const dim3 grid(mtiles * ntiles), block(WAVES * 64);
+  auto* kern = &qkv_prefill_kernel<WAVES, NSTAGE, kAligned>;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, grid, block, lds, stream, p, mtiles);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_qkv_prefill(const QkvProblem& p, hipStream_t stream) {
-  const uint32_t mtiles = (p.m + BM - 1) / BM;
-  const uint32_t ntiles = (p.n + BN - 1) / BN;
-  const dim3 grid(mtiles * ntiles), block(THREADS);
-  if (p.n % 8 == 0)
-    hipLaunchKernelGGL(qkv_prefill_kernel<true>, grid, block, 0, stream, p, mtiles);
-  else
-    hipLaunchKernelGGL(qkv_prefill_kernel<false>, grid, block, 0, stream, p, mtiles);
-  return hipGetLastError();
+  // 16-byte output rows and f16-pair scale loads need n % 8 == 0
+  if (p.n % 8 == 0) return launch_variant<kPrefillWaves, kPrefillStages, true>(p, stream);
+  return launch_variant<kPrefillWaves, kPrefillStages, false>(p, stream);
 }
 
 }  // namespace kaio
