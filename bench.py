@@ -67,6 +67,33 @@ def timed(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps, wall
 
 
+def timed_graph(fn, calls, replays, stream):
+    """Average duration (ms) per fn() call when `calls` calls are captured in one HIP graph
+    and the graph is replayed `replays` times (no host launch gaps between kernels)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for i in range(3):
+            fn(i)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(replays):
+        g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / (calls * replays)
+
+
 def measured_traffic(kernel: str, src: str, algorithmic_bytes: float):
     """HBM bytes per launch from committed rocprofv3 PMC counters, or None if absent/stale."""
     try:
@@ -108,6 +135,36 @@ def cpu_baseline(inp, budget_s: float):
                       f"prefill workload, {runs} run(s), {spent:.1f} s"}
 
 
+def summarize(dirs):
+    """Per-kernel summary of rocprofv3 CSV output (kernel_stats.csv or counter_collection.csv)."""
+    import csv
+    import collections
+    import glob
+    for d in dirs:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+            print(f"## {f}")
+            print("| kernel | calls | avg us | min us | max us | share |")
+            print("|---|---|---|---|---|---|")
+            for r in csv.DictReader(open(f)):
+                print(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            agg = collections.defaultdict(lambda: collections.defaultdict(float))
+            names = {}
+            for r in csv.DictReader(open(f)):
+                agg[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+                names[r["Dispatch_Id"]] = r["Kernel_Name"]
+            per_kernel = collections.defaultdict(list)
+            for dsp, vals in agg.items():
+                per_kernel[names[dsp]].append(vals)
+            print(f"## {f}")
+            for k, lst in per_kernel.items():
+                keys = sorted(lst[0])
+                avg = {c: sum(v[c] for v in lst) / len(lst) for c in keys}
+                print(f"- {k[:90]} ({len(lst)} dispatches): " +
+                      ", ".join(f"{c}={avg[c]:.6g}" for c in keys))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,7 +173,14 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "gemm", "bwd"], default="all")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 256 MiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--summarize", nargs="+", metavar="DIR",
+                    help="summarize rocprofv3 CSV output directories instead of benchmarking")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library has no "
               "multi-GPU path: the QKV projection would shard by output columns with no exchange)",
@@ -179,12 +243,14 @@ def main():
             sets.append(([t(a) for a in wj], [t(a) for a in sj]))
         outs = [torch.empty((M, N), dtype=torch.float16, device=dev) for _ in range(3)]
         dstep = lambda i: kaio.kaio_qkv_w4a16(x, *sets[i % R][0], *sets[i % R][1], *outs)
-        dms, _ = timed(dstep, max(args.steps, 4 * R), 2 * R, stream)
+        # a ~10 us kernel: time it inside a HIP graph so host launch gaps are not counted
+        dms = timed_graph(dstep, 4 * R, max(5, args.steps // 10), stream)
         dbytes = dinp.x.nbytes + sum(a.nbytes for a in dinp.w) + sum(a.nbytes for a in dinp.s) + 3 * M * N * 2
         gbs = dbytes / (dms * 1e-3) / 1e9
         log(f"[bench] decode: {dms * 1e3:.2f} us/call, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of HBM)")
         secondary["qkv_decode"] = {
-            "workload": "x f16[8,4096], 3x u32[512,4096], 3x f16[32,4096]; 21 rotated weight sets",
+            "workload": "x f16[8,4096], 3x u32[512,4096], 3x f16[32,4096]; 21 rotated weight sets, "
+                        "84 calls per HIP graph replay",
             "us_per_call": round(dms * 1e3, 3), "value": round(gbs, 1), "unit": "GB/s",
             "bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
             "algorithmic_bytes": dbytes, "tflops": round(2.0 * M * N * K * 3 / (dms * 1e-3) / 1e12, 3),
@@ -228,6 +294,14 @@ def main():
                 "us_per_call": round(bms * 1e3, 2), "value": round(gbs, 1), "unit": "GB/s", "bound": "hbm",
                 "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes}
             del dyd, scd, dqd
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 268435456 bytes read, 268435456 bytes written")
+        del src, dst
 
     result["secondary"] = secondary
     if not args.no_cpu_baseline:

@@ -52,6 +52,44 @@ __device__ __forceinline__ half8_t unpack_int4x8(uint32_t w) {
   return out;
 }
 
+// INT4 -> f16, exact, in nibble-interleaved order.
+//
+// Same exact integers as unpack_int4x8, but the eight results come out in the
+// k order [0, 4, 1, 5, 2, 6, 3, 7] (nibbles i and i+4 sit 16 bits apart, so
+// one bit-select builds both halves of an f16 pair).  An MFMA over these B
+// values needs its A values in the same k order: see permute_x_like_int4x8.
+// Cost: 4 bit-selects, 1 shift, 4 packed f16 ops per word (vs 12 ops).
+__device__ __forceinline__ uint32_t nibble_pair(uint32_t w, uint32_t sel_mask, uint32_t bits) {
+  // bits inside sel_mask: w with the nibble's top bit flipped (q -> q + 8);
+  // bits outside: the f16 exponent pattern of 1024 (0x6400)
+  return (sel_mask & (w ^ bits)) | (~sel_mask & bits);
+}
+__device__ __forceinline__ half8_t unpack_int4x8_interleaved(uint32_t w) {
+  const half2_t lo_add = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const half2_t hi_mul = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const half2_t hi_add = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const uint32_t w8 = w >> 8;
+  // (nibble i, nibble i+4) -> (1024 + q_i + 8, 1024 + q_{i+4} + 8)       for i = 0, 2
+  // (nibble i, nibble i+4) -> (1024 + 16(q_i + 8), 1024 + 16(q_{i+4} + 8)) for i = 1, 3
+  const half2_t p0 = __builtin_bit_cast(half2_t, nibble_pair(w, 0x000F000Fu, 0x64086408u)) + lo_add;
+  const half2_t p1 = __builtin_elementwise_fma(
+      __builtin_bit_cast(half2_t, nibble_pair(w, 0x00F000F0u, 0x64806480u)), hi_mul, hi_add);
+  const half2_t p2 = __builtin_bit_cast(half2_t, nibble_pair(w8, 0x000F000Fu, 0x64086408u)) + lo_add;
+  const half2_t p3 = __builtin_elementwise_fma(
+      __builtin_bit_cast(half2_t, nibble_pair(w8, 0x00F000F0u, 0x64806480u)), hi_mul, hi_add);
+  const uint4 d = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                   __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+  return __builtin_bit_cast(half8_t, d);
+}
+
+// Reorders eight consecutive f16 (k offsets 0..7) into [0, 4, 1, 5, 2, 6, 3, 7],
+// the k order of unpack_int4x8_interleaved.
+__device__ __forceinline__ half8_t permute_x_like_int4x8(uint4 v) {
+  const uint4 o = {(v.x & 0xFFFFu) | (v.z << 16), (v.x >> 16) | (v.z & 0xFFFF0000u),
+                   (v.y & 0xFFFFu) | (v.w << 16), (v.y >> 16) | (v.w & 0xFFFF0000u)};
+  return __builtin_bit_cast(half8_t, o);
+}
+
 __device__ __forceinline__ floatx4 mfma16x16x32(half8_t a, half8_t b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }

@@ -32,7 +32,10 @@ constexpr uint32_t kPrefillBN = 16 * kPrefillWaves;   // columns of each output 
 constexpr uint32_t kMaxN = 1u << 28;   // keeps 32-bit per-lane offsets in range
 constexpr uint32_t kMaxK = 1u << 24;
 constexpr uint32_t kDecodeMaxM = 8;    // m <= this runs the decode kernel
-constexpr uint32_t kDecodeBN = 64;     // columns of one output per decode workgroup
+#ifndef KAIO_DECODE_VEC
+#define KAIO_DECODE_VEC 4
+#endif
+constexpr uint32_t kDecodeBN = 16 * KAIO_DECODE_VEC;   // columns of one output per decode workgroup
 constexpr uint32_t kGemmBM = 256;
 constexpr uint32_t kGemmBN = 256;
 constexpr uint64_t kMaxWorkgroups = (1ull << 24) - 1;  // 1-D grid limit at 256 threads

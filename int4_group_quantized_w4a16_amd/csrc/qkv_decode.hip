@@ -9,38 +9,60 @@
 // arithmetic intensity (~31 flop/byte) is above the f32 VALU ridge of the
 // chip, so the products still run on MFMA: x is the A operand with its rows
 // padded to 16 by zeros, the weights the B operand.
-// * Workgroup = 8 waves on a 64-column strip of ONE output.  Lane (kb, c)
-//   loads one 128-bit vector = the words of columns 4c..4c+3 at packed row
-//   kb of a 32-k step: each word is the B operand of one of four MFMAs, whose
-//   column c stands for output column 4c + t.  A wave-wide load covers
-//   4 packed rows x 256 contiguous bytes.
-// * Split-K across the 8 waves (wave w takes groups [wG/8, (w+1)G/8)); every
-//   wave issues all its weight, activation and scale loads before its
-//   first MFMA, so the whole strip is in flight at once.
+// * Workgroup = WAVES waves on a strip of 16*VEC columns of ONE output.  Lane
+//   (kb, c) loads one VEC-word vector = the words of columns VEC*c .. VEC*c+VEC-1
+//   at packed row kb of a 32-k step: each word is the B operand of one of
+//   VEC MFMAs, whose column c stands for output column VEC*c + t.  A
+//   wave-wide load covers 4 packed rows x 64*VEC contiguous bytes.
+// * Split-K across the waves (wave w takes groups [wG/W, (w+1)G/W)); each
+//   wave streams its groups GCHUNK at a time through two register buffers,
+//   the next chunk's loads in flight while the current chunk computes.
+// * INT4 unpack in nibble-interleaved k order (9 VALU ops per word); the x
+//   fragments, tiny at m <= 8, are permuted to the same k order in registers.
 // * Per group: 4 chained MFMAs into a fresh partial, then acc += partial *
-//   scale in f32 (same exactness argument as the tile kernel).
-// * The 8 wave partial sums meet in LDS and are added in a fixed order, so
-//   results are deterministic; then f32 -> f16 (RNE) and 128-byte row stores.
+//   scale in f32 (every product exact, as in the tile kernel).
+// * The wave partial sums meet in LDS and are added in a fixed order, so
+//   results are deterministic; then f32 -> f16 (RNE) and row stores.
 
 #include "common.hpp"
 #include "launch.hpp"
 
+#ifndef KAIO_DECODE_WAVES
+#define KAIO_DECODE_WAVES 16
+#endif
+#ifndef KAIO_DECODE_GCHUNK
+#define KAIO_DECODE_GCHUNK 1
+#endif
+
 namespace kaio {
 namespace {
 
-constexpr int WAVES = 8;
+constexpr int WAVES = KAIO_DECODE_WAVES;
+constexpr int VEC = KAIO_DECODE_VEC;          // words per lane per load: 2 or 4
 constexpr int THREADS = WAVES * kWave;
-constexpr int BN = kDecodeBN;          // 64 columns per strip
-constexpr int GCHUNK = 4;              // groups loaded per pass of a wave
+constexpr int BN = 16 * VEC;                  // columns per strip
+constexpr int GCHUNK = KAIO_DECODE_GCHUNK;    // groups loaded per pass of a wave
+static_assert(BN == (int)kDecodeBN, "strip width must match the host-side grid computation");
+static_assert(VEC == 1 || VEC == 2 || VEC == 4, "vector width");
 
-template <bool kVec>
-__global__ void __launch_bounds__(THREADS)
+template <int V> struct WordVec;
+template <> struct WordVec<1> { using T = uint32_t; };
+template <> struct WordVec<2> { using T = uint2; };
+template <> struct WordVec<4> { using T = uint4; };
+template <int V> struct HalfVec { typedef uint16_t T __attribute__((ext_vector_type(V))); };
+template <> struct HalfVec<1> { typedef uint16_t T; };
+
+// kFull: n % BN == 0, so every strip is complete and the vector loads of
+// weights (VEC words) and scales (VEC halves) stay inside their rows.
+template <bool kFull>
+__global__ void __launch_bounds__(THREADS, 1)
 qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
+  using WV = typename WordVec<VEC>::T;
   __shared__ float red[WAVES][16][BN];
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
-  const uint32_t wave = tid >> 6;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t kb = lane >> 4;
   const uint32_t l16 = lane & 15;
 
@@ -51,97 +73,106 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   const uint32_t g_begin = (uint32_t)(((uint64_t)wave * G) / WAVES);
   const uint32_t g_end = (uint32_t)(((uint64_t)(wave + 1) * G) / WAVES);
 
-  const uint32_t* __restrict__ w = p.w[q];
-  const uint16_t* __restrict__ s = p.s[q];
-  const uint32_t col4 = n0 + 4 * l16;      // first of the lane's four columns
-  const bool row_ok = l16 < M;             // A-operand row of this lane is a real row of x
+  const uint32_t* __restrict__ w = q == 0 ? p.w[0] : (q == 1 ? p.w[1] : p.w[2]);
+  const uint16_t* __restrict__ s = q == 0 ? p.s[0] : (q == 1 ? p.s[1] : p.s[2]);
+  const uint32_t colv = n0 + VEC * l16;     // first of the lane's VEC columns
+  // A-operand rows past M repeat row M-1: their outputs are never stored, and
+  // MFMA rows do not mix, so no load needs a predicate.
+  const uint16_t* xrow = p.x + (size_t)(l16 < M ? l16 : M - 1) * K + kb * 8;
+  const uint32_t* wlane = w + (size_t)kb * N + colv;   // + (16g + 4ks) * N
 
-  floatx4 acc[4];
+  floatx4 acc[VEC];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < VEC; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  for (uint32_t g0 = g_begin; g0 < g_end; g0 += GCHUNK) {
-    uint4 wv[GCHUNK][4];
+  struct Chunk {
+    uint32_t wv[GCHUNK][4][VEC];
     uint4 xa[GCHUNK][4];
-    float sc[GCHUNK][4];
+    uint32_t sc[GCHUNK][VEC];
+  };
+  // Loads of GCHUNK groups starting at g0.  Groups past the wave's range are
+  // clamped to its last group (loaded, never used) so that every chunk issues
+  // the same loads and the compiler can keep the next chunk in flight.
+  auto load_chunk = [&](uint32_t g0, Chunk& c) {
 #pragma unroll
     for (int gi = 0; gi < GCHUNK; ++gi) {
-      const uint32_t g = g0 + gi;
-      const bool live = g < g_end;
+      const uint32_t g = (g0 + gi < g_end) ? g0 + gi : g_end - 1;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const size_t r = (size_t)g * 16 + ks * 4 + kb;
-        uint4 wq = uint4{0u, 0u, 0u, 0u};
-        if (live) {
-          if (kVec) {
-            if (col4 < N) wq = *reinterpret_cast<const uint4*>(w + r * N + col4);
-          } else {
-            uint32_t tmp[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) tmp[t] = (col4 + t < N) ? w[r * N + col4 + t] : 0u;
-            wq = uint4{tmp[0], tmp[1], tmp[2], tmp[3]};
-          }
-        }
-        wv[gi][ks] = wq;
-        uint4 xv = uint4{0u, 0u, 0u, 0u};
-        if (live && row_ok)
-          xv = *reinterpret_cast<const uint4*>(p.x + (size_t)l16 * K + (size_t)g * kGroup + ks * 32 + kb * 8);
-        xa[gi][ks] = xv;
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) sc[gi][t] = 0.f;
-      if (live) {
-        if (kVec) {
-          if (col4 < N) {
-            const uint2 sv = *reinterpret_cast<const uint2*>(s + (size_t)g * N + col4);
-            sc[gi][0] = h2f((uint16_t)(sv.x & 0xFFFFu));
-            sc[gi][1] = h2f((uint16_t)(sv.x >> 16));
-            sc[gi][2] = h2f((uint16_t)(sv.y & 0xFFFFu));
-            sc[gi][3] = h2f((uint16_t)(sv.y >> 16));
-          }
+        const size_t roff = ((size_t)g * 16 + ks * 4) * N;
+        if (kFull) {
+          const WV v = *reinterpret_cast<const WV*>(wlane + roff);
+          __builtin_memcpy(c.wv[gi][ks], &v, sizeof(v));
         } else {
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            if (col4 + t < N) sc[gi][t] = h2f(s[(size_t)g * N + col4 + t]);
+          for (int t = 0; t < VEC; ++t) c.wv[gi][ks][t] = (colv + t < N) ? wlane[roff + t] : 0u;
         }
+        c.xa[gi][ks] = *reinterpret_cast<const uint4*>(xrow + (size_t)g * kGroup + ks * 32);
+      }
+      if (kFull) {
+        using HV = typename HalfVec<VEC>::T;
+        const HV sv = *reinterpret_cast<const HV*>(s + (size_t)g * N + colv);
+        uint16_t sh[VEC];
+        __builtin_memcpy(sh, &sv, sizeof(sv));
+#pragma unroll
+        for (int t = 0; t < VEC; ++t) c.sc[gi][t] = sh[t];
+      } else {
+#pragma unroll
+        for (int t = 0; t < VEC; ++t) c.sc[gi][t] = (colv + t < N) ? (uint32_t)s[(size_t)g * N + colv + t] : 0u;
       }
     }
+  };
+  auto compute_chunk = [&](uint32_t g0, const Chunk& c) {
 #pragma unroll
     for (int gi = 0; gi < GCHUNK; ++gi) {
-      if (g0 + gi < g_end) {
-        floatx4 part[4];
+      if (g0 + gi < g_end) {   // wave-uniform
+        floatx4 part[VEC];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const half8_t a = __builtin_bit_cast(half8_t, xa[gi][ks]);
-          const uint32_t words[4] = {wv[gi][ks].x, wv[gi][ks].y, wv[gi][ks].z, wv[gi][ks].w};
+          const half8_t a = permute_x_like_int4x8(c.xa[gi][ks]);
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            part[t] = mfma16x16x32(a, unpack_int4x8(words[t]),
+          for (int t = 0; t < VEC; ++t)
+            part[t] = mfma16x16x32(a, unpack_int4x8_interleaved(c.wv[gi][ks][t]),
                                    ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : part[t]);
         }
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < VEC; ++t) {
+          const float sf = h2f((uint16_t)c.sc[gi][t]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(part[t][i], sc[gi][t], acc[t][i]);
+          for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(part[t][i], sf, acc[t][i]);
+        }
       }
+    }
+  };
+
+  if (g_begin < g_end) {
+    // two register buffers used ping-pong: chunk c+1 is in flight while chunk c computes
+    Chunk ca, cb;
+    load_chunk(g_begin, ca);
+    for (uint32_t g0 = g_begin; g0 < g_end; g0 += 2 * GCHUNK) {
+      load_chunk(g0 + GCHUNK, cb);
+      compute_chunk(g0, ca);
+      if (g0 + GCHUNK >= g_end) break;
+      load_chunk(g0 + 2 * GCHUNK, ca);
+      compute_chunk(g0 + GCHUNK, cb);
     }
   }
 
-  // lane holds rows 4*kb + i of MFMA column l16, i.e. output column 4*l16 + t
+  // lane holds rows 4*kb + i of MFMA column l16, i.e. output column VEC*l16 + t
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < VEC; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][4 * kb + i][4 * l16 + t] = acc[t][i];
+    for (int i = 0; i < 4; ++i) red[wave][4 * kb + i][VEC * l16 + t] = acc[t][i];
   __syncthreads();
 
-  uint16_t* __restrict__ out = p.out[q];
+  uint16_t* __restrict__ out = q == 0 ? p.out[0] : (q == 1 ? p.out[1] : p.out[2]);
   for (uint32_t e = tid; e < M * BN; e += THREADS) {
     const uint32_t row = e / BN, c = e % BN;
     float sum = 0.f;
 #pragma unroll
     for (int wv_ = 0; wv_ < WAVES; ++wv_) sum += red[wv_][row][c];
     const uint32_t gc = n0 + c;
-    if (gc < N) out[(size_t)row * N + gc] = __builtin_bit_cast(uint16_t, (_Float16)sum);
+    if (kFull || gc < N) out[(size_t)row * N + gc] = __builtin_bit_cast(uint16_t, (_Float16)sum);
   }
 }
 
@@ -150,7 +181,7 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
 hipError_t launch_qkv_decode(const QkvProblem& p, hipStream_t stream) {
   const uint32_t nstrips = (p.n + BN - 1) / BN;
   const dim3 grid(3 * nstrips), block(THREADS);
-  if (p.n % 4 == 0)
+  if (p.n % BN == 0)
     hipLaunchKernelGGL(qkv_decode_kernel<true>, grid, block, 0, stream, p, nstrips);
   else
     hipLaunchKernelGGL(qkv_decode_kernel<false>, grid, block, 0, stream, p, nstrips);
