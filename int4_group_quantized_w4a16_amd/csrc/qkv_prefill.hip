@@ -41,8 +41,11 @@ constexpr int RT = BM / 16;             // row tiles per wave
 constexpr int KC = kGroup / 8;          // 16-byte chunks per row per group
 constexpr int X_CHUNKS = BM * KC;       // 16-byte chunks of x per stage (32 KiB)
 
-#ifndef KAIO_PREFILL_TILE_MAJOR
-#define KAIO_PREFILL_TILE_MAJOR 2
+#ifndef KAIO_PREFILL_SM
+#define KAIO_PREFILL_SM 4
+#endif
+#ifndef KAIO_PREFILL_SN
+#define KAIO_PREFILL_SN 8
 #endif
 
 #define KAIO_LDS(p) ((__attribute__((address_space(3))) void*)(p))
@@ -93,9 +96,10 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   const uint32_t kb = lane >> 4;          // 8-k block of the 32-k MFMA step
   const uint32_t l16 = lane & 15;
 
-  const uint32_t b = xcd_remap(blockIdx.x, gridDim.x);
-  const uint32_t m0 = (b % mtiles) * BM;
-  const uint32_t n0 = (b / mtiles) * BN;
+  uint32_t tm, tn;
+  tile_of<KAIO_PREFILL_SM, KAIO_PREFILL_SN>(blockIdx.x, gridDim.x, mtiles, (p.n + BN - 1) / BN, tm, tn);
+  const uint32_t m0 = tm * BM;
+  const uint32_t n0 = tn * BN;
   const uint32_t M = p.m, N = p.n, K = p.k;
   const uint32_t G = K / kGroup;
 
@@ -176,7 +180,6 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
       for (int q = 0; q < 3; ++q) sf[q] = h2f(p.s[q][(size_t)g * N + colc]);
     }
 
-#if KAIO_PREFILL_TILE_MAJOR == 2
     // Software-pipelined tile-major order.  Unpack the group's 12 weight
     // words once; then per row tile r: fetch the A fragments of tile r+1,
     // run tile r's three 4-deep MFMA chains, and fold tile r-1's finished
@@ -220,59 +223,6 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
       for (int i = 0; i < 4; ++i)
         acc[RT - 1][q][i] = __builtin_fmaf(pbuf[(RT - 1) & 1][q][i], sf[q], acc[RT - 1][q][i]);
   }
-#elif KAIO_PREFILL_TILE_MAJOR
-    // Unpack the group's 12 weight words once (4 k-steps x 3 outputs), then
-    // run each row tile's three 4-deep MFMA chains to completion and fold the
-    // scale immediately: the partial sums live for one row tile only.
-    half8_t bq[3][4];
-#pragma unroll
-    for (int q = 0; q < 3; ++q)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) bq[q][ks] = unpack_int4x8(wst[((q * 4 + ks) * WAVES + wave) * 64 + lane]);
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const uint32_t row = r * 16 + l16;
-      half8_t a[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        a[ks] = __builtin_bit_cast(half8_t, xs[row * KC + ((ks * 4 + kb) ^ (row & 15))]);
-      floatx4 part[3];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int q = 0; q < 3; ++q)
-          part[q] = mfma16x16x32(a[ks], bq[q][ks], ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : part[q]);
-#pragma unroll
-      for (int q = 0; q < 3; ++q)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[r][q][i] = __builtin_fmaf(part[q][i], sf[q], acc[r][q][i]);
-    }
-  }
-#else
-    floatx4 part[RT][3];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      half8_t bq[3];
-#pragma unroll
-      for (int q = 0; q < 3; ++q) bq[q] = unpack_int4x8(wst[((q * 4 + ks) * WAVES + wave) * 64 + lane]);
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const uint32_t row = r * 16 + l16;
-        const uint32_t kc = ks * 4 + kb;
-        const half8_t a = __builtin_bit_cast(half8_t, xs[row * KC + (kc ^ (row & 15))]);
-#pragma unroll
-        for (int q = 0; q < 3; ++q)
-          part[r][q] = mfma16x16x32(a, bq[q], ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : part[r][q]);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < RT; ++r)
-#pragma unroll
-      for (int q = 0; q < 3; ++q)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[r][q][i] = __builtin_fmaf(part[r][q][i], sf[q], acc[r][q][i]);
-  }
-#endif
 
   // ---- epilogue: one output at a time through LDS -----------------------------
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
