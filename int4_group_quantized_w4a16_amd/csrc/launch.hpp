@@ -23,13 +23,9 @@ constexpr uint32_t kPrefillBM = 128;   // rows of x per workgroup
 #ifndef KAIO_PREFILL_WAVES
 #define KAIO_PREFILL_WAVES 8
 #endif
-#ifndef KAIO_PREFILL_STAGES
-#define KAIO_PREFILL_STAGES 2
-#endif
 constexpr int kPrefillWaves = KAIO_PREFILL_WAVES;    // waves per workgroup; each owns 16 columns of every output
-constexpr int kPrefillStages = KAIO_PREFILL_STAGES;  // depth of the LDS ring
 constexpr uint32_t kPrefillBN = 16 * kPrefillWaves;   // columns of each output per workgroup
-constexpr uint32_t kMaxN = 1u << 28;   // keeps 32-bit per-lane offsets in range
+constexpr uint32_t kMaxN = 1u << 26;   // keeps 32-bit per-lane byte offsets in range (16 rows x N x 4 B)
 constexpr uint32_t kMaxK = 1u << 24;
 constexpr uint32_t kDecodeMaxM = 8;    // m <= this runs the decode kernel
 #ifndef KAIO_DECODE_VEC

@@ -11,17 +11,20 @@
 //   output.  Wave w owns columns [16w, 16w+16) of all three outputs and all
 //   128 rows, so the waves share one x tile in LDS and never unpack the same
 //   weight twice.
-// * Everything a group needs -- the x tile, the packed weights, the scales --
-//   is staged into an NSTAGE-deep LDS ring with direct global->LDS loads (no
-//   registers, no VALU), NSTAGE-1 groups ahead of the MFMAs, one barrier per
-//   group.  No register ever waits on a global load, so the only waits on
-//   the vector-memory counter are the explicit ones at that barrier.
+// * Everything a group of 128 k needs is staged into LDS rings with direct
+//   global->LDS loads (no registers, no VALU): x two groups ahead, the packed
+//   weights and scales one group ahead.  Each address is a wave-uniform base
+//   in SGPRs plus a 32-bit lane offset.  One barrier per group; the only
+//   waits on the vector-memory counter are explicit.
 // * x: chunk kc of row r lands in slot r*16 + (kc ^ (r & 15)), which makes
-//   the MFMA A-operand reads bank-conflict free.
+//   the MFMA A-operand reads bank-conflict free.  A fragments are read two
+//   row tiles ahead of the MFMAs that use them.
 // * Weights: one u32 holds the eight consecutive k of one column that a lane
-//   feeds to one v_mfma_f32_16x16x32_f16 as its B operand.  Each lane's DMA
-//   fetches exactly the word it will multiply into its own LDS slot; the lane
-//   reads it back and unpacks it to exact f16 integers in registers.
+//   feeds to one v_mfma_f32_16x16x32_f16 as its B operand.  Each wave fetches
+//   the 16 packed rows x 16 columns it multiplies (one 16-byte load per lane
+//   and output when n % 8 == 0), reads its words back and unpacks them to
+//   exact f16 integers in registers -- during the last two row tiles of the
+//   previous group, so that the unpack overlaps MFMAs.
 // * Scales are applied per group in f32: the four MFMAs of a group
 //   accumulate a fresh partial sum of x*q (exact small integers times f16
 //   activations), then acc += partial * scale.  Rounding q*scale to f16
@@ -41,6 +44,9 @@ constexpr int RT = BM / 16;             // row tiles per wave
 constexpr int KC = kGroup / 8;          // 16-byte chunks per row per group
 constexpr int X_CHUNKS = BM * KC;       // 16-byte chunks of x per stage (32 KiB)
 
+#ifndef KAIO_PREFILL_XDIST
+#define KAIO_PREFILL_XDIST 2
+#endif
 #ifndef KAIO_PREFILL_SM
 #define KAIO_PREFILL_SM 4
 #endif
@@ -63,31 +69,120 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// One stage of the LDS ring, in 16-byte units:
-//   x     [X_CHUNKS]                       swizzled rows of x
-//   w     [3][4][WAVES][64] u32            word (q, ks) for lane l of wave w
-//   s     [3][WAVES][8] u32 pairs of f16   scales of the wave's 16 columns
-template <int WAVES>
-struct StageLayout {
-  static constexpr int kX = 0;
-  static constexpr int kW = X_CHUNKS;                          // uint4 offset
-  static constexpr int kS = kW + 3 * 4 * WAVES * 64 / 4;
-  static constexpr int kSize = kS + (3 * WAVES * 8 + 3) / 4;   // uint4 per stage
+// LDS rings, in 16-byte units.  x of a group is fetched XDIST groups ahead
+// (ring of XDIST+1 slots); the weights and scales one group ahead (2 slots):
+//   x  [XDIST+1][X_CHUNKS]           swizzled rows of x
+//   w  [2] x { [3][WAVES][16][16] u32   packed rows x columns of output q, wave w
+//              [3][WAVES][8] u32 }      pairs of f16 scales of the wave's 16 columns
+template <int WAVES, int XDIST>
+struct RingLayout {
+  static constexpr int kXSlots = XDIST + 1;
+  static constexpr int kWBase = kXSlots * X_CHUNKS;
+  static constexpr int kW = 0;                                   // within a weight slot
+  static constexpr int kS = 3 * WAVES * 256 / 4;
+  static constexpr int kWSize = kS + (3 * WAVES * 8 + 3) / 4;
+  static constexpr int kSize = kWBase + 2 * kWSize;              // uint4
 };
 
-template <int WAVES, int NSTAGE, bool kAligned>
+// A wave-uniform pointer the compiler must treat as opaque (kept in SGPRs):
+// stops it from folding the per-lane offsets into 64-bit vector addresses
+// hoisted out of the group loop.
+__device__ __forceinline__ const char* uniform(const char* p) {
+  asm volatile("" : "+s"(p));
+  return p;
+}
+// Same for a per-lane 32-bit offset: re-materialised where it is used, so
+// that base + offset matches the scalar-base load form.
+__device__ __forceinline__ uint32_t lane_offset(uint32_t o) {
+  asm volatile("" : "+v"(o));
+  return o;
+}
+
+__device__ __forceinline__ void load_a(half8_t (&a)[4], const uint4* __restrict__ xs, int r, uint32_t l16,
+                                       uint32_t kb) {
+  const uint32_t row = r * 16 + l16;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) a[ks] = __builtin_bit_cast(half8_t, xs[row * KC + ((ks * 4 + kb) ^ (row & 15))]);
+}
+
+__device__ __forceinline__ void fold(floatx4 (&acc)[3], const floatx4 (&pb)[3], const float (&sf)[3]) {
+#pragma unroll
+  for (int q = 0; q < 3; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[q][i] = __builtin_fmaf(pb[q][i], sf[q], acc[q][i]);
+}
+
+// The MFMA work of one group.
+//
+// Row tiles 0 .. RT-3 run software-pipelined in tile-major order: fetch the A
+// fragments of tile r+2 (three buffers), run tile r's three 4-deep MFMA
+// chains into a fresh partial, and fold tile r-1's partials into acc
+// (acc += p * s) while those MFMAs execute.  Scheduling barriers keep the
+// compiler from hoisting every tile's LDS reads (register blow-up).
+//
+// The last two tiles run in k-step-major order: once the six MFMAs of step
+// ks are issued, the B fragments bq[*][ks] are dead and the next group's
+// words are unpacked into them, so the unpack overlaps MFMAs instead of
+// stalling the start of the next group.  `next_w` points at this wave's
+// next-group words in LDS, `next_s[q]` at its scales; the wait before the
+// tail covers them (XPENDING = the x loads issued after them).
+template <int WAVES, int XPENDING>
+__device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3][4], float (&sf)[3],
+                                          const uint4* __restrict__ xs, const uint32_t* __restrict__ next_w,
+                                          const uint16_t* const (&next_s)[3], uint32_t l16, uint32_t kb,
+                                          uint32_t lane) {
+  // A fragments two tiles ahead (three buffers); tiles RT-2 and RT-1 land
+  // in buffers (RT-2) % 3 and (RT-1) % 3 during tiles RT-4 and RT-3.
+  half8_t abuf[3][4];
+  floatx4 pbuf[2][3];
+  load_a(abuf[0], xs, 0, l16, kb);
+  load_a(abuf[1], xs, 1, l16, kb);
+#pragma unroll
+  for (int r = 0; r < RT - 2; ++r) {
+    load_a(abuf[(r + 2) % 3], xs, r + 2, l16, kb);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        pbuf[r & 1][q] = mfma16x16x32(abuf[r % 3][ks], bq[q][ks],
+                                      ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : pbuf[r & 1][q]);
+    if (r > 0) fold(acc[r - 1], pbuf[(r - 1) & 1], sf);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  constexpr int T0 = (RT - 2) % 3, T1 = (RT - 1) % 3;
+  fold(acc[RT - 3], pbuf[(RT - 3) & 1], sf);
+  // this wave's own weights and scales of the next group have landed (only
+  // its XPER x loads, issued after them, may still be in flight)
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(XPENDING) : "memory");
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        pbuf[t][q] = mfma16x16x32(abuf[t == 0 ? T0 : T1][ks], bq[q][ks],
+                                  ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : pbuf[t][q]);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) bq[q][ks] = unpack_int4x8(next_w[q * WAVES * 256 + ks * 64 + lane]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  fold(acc[RT - 2], pbuf[0], sf);
+  fold(acc[RT - 1], pbuf[1], sf);
+#pragma unroll
+  for (int q = 0; q < 3; ++q) sf[q] = h2f(*next_s[q]);
+}
+
+template <int WAVES, int XDIST, bool kAligned>
 __global__ void __launch_bounds__(WAVES * 64, 1)
 qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   constexpr int THREADS = WAVES * 64;
   constexpr int BN = 16 * WAVES;
   constexpr int XPER = X_CHUNKS / THREADS;       // x loads per thread per stage
   constexpr int OUT_LD = BN + 8;                 // padded f16 row of the epilogue tile
-  using L = StageLayout<WAVES>;
-  // vector-memory operations per thread per stage: x, 12 weight words, 1 scale pair
-  constexpr int VM_PER_STAGE = XPER + 12 + (kAligned ? 1 : 0);
+  using L = RingLayout<WAVES, XDIST>;
   static_assert(XPER * THREADS == X_CHUNKS, "x stage must split evenly");
-  static_assert(BM * OUT_LD * 2 <= NSTAGE * L::kSize * 16, "epilogue tile must fit in the ring");
-  static_assert((NSTAGE - 2) * VM_PER_STAGE < 64, "vmcnt range");
+  static_assert(BM * OUT_LD * 2 <= L::kSize * 16, "epilogue tile must fit in the ring");
+  static_assert(XPER < 64, "vmcnt range");
   extern __shared__ uint4 smem[];
 
   const uint32_t tid = threadIdx.x;
@@ -103,20 +198,28 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   const uint32_t M = p.m, N = p.n, K = p.k;
   const uint32_t G = K / kGroup;
 
-  // ---- per-lane DMA sources ---------------------------------------------------
-  const uint16_t* xblk = p.x + (size_t)m0 * K;
-  uint32_t xoff[XPER];         // element offset (within row block m0, group 0) of this lane's chunk
+  // ---- per-lane DMA sources -----------------------------------------------------
+  // Each source address is a wave-uniform base plus a 32-bit per-lane byte
+  // offset (the host-side size limits keep the offsets below 2^32), which the
+  // loads take in their scalar-base form: no per-lane 64-bit address math.
+  const char* xblk = reinterpret_cast<const char*>(p.x + (size_t)m0 * K);
+  uint32_t xoff[XPER];         // byte offset (within row block m0, group 0) of this lane's chunk
 #pragma unroll
   for (int i = 0; i < XPER; ++i) {
     const uint32_t slot = (i * WAVES + wave) * 64 + lane;
     const uint32_t row = slot >> 4;
     const uint32_t kc = (slot & 15) ^ (row & 15);
     const uint32_t rowc = (m0 + row < M) ? row : (M - 1 - m0);   // rows past M: any valid row
-    xoff[i] = rowc * K + kc * 8;
+    xoff[i] = (rowc * K + kc * 8) * 2;
   }
   const uint32_t col = n0 + wave * 16 + l16;
   const uint32_t colc = col < N ? col : N - 1;   // columns past N are computed, never stored
-  const uint32_t woff = kb * N + colc;           // word offset inside a group's 16 packed rows
+  // Weights, 16-byte path (n % 8 == 0): lane l fetches packed row l / 4,
+  // columns 4(l % 4) .. +3 of the wave's 16 -- one load per output per group.
+  // A group of four columns lies wholly inside or wholly past N here.
+  // 4-byte path: lane (kb, c) fetches packed row 4 ks + kb, column c.
+  const uint32_t c4 = n0 + wave * 16 + 4 * (lane & 3);
+  const uint32_t woff = kAligned ? ((lane >> 2) * N + (c4 < N ? c4 : N - 4)) * 4 : (kb * N + colc) * 4;
   // scale pairs: lanes 0..23 fetch the f16 pair (2j, 2j+1) of output q = lane / 8
   const uint32_t sq = lane >> 3, sj = lane & 7;
   const uint32_t scol = n0 + wave * 16 + 2 * sj;
@@ -125,28 +228,51 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   // kernel arguments would be fetched from memory
   const uint16_t* s_lane = sq == 0 ? p.s[0] : (sq == 1 ? p.s[1] : p.s[2]);
 
-  auto issue_stage = [&](uint32_t g, int buf) {
-    uint4* st = smem + buf * L::kSize;
-    const uint16_t* xsrc = xblk + (size_t)g * kGroup;
-#pragma unroll
-    for (int i = 0; i < XPER; ++i)
-      __builtin_amdgcn_global_load_lds(KAIO_GLOBAL(xsrc + xoff[i]),
-                                       KAIO_LDS(st + L::kX + (i * WAVES + wave) * 64), 16, 0, 0);
-    uint32_t* wst = reinterpret_cast<uint32_t*>(st + L::kW);
+  auto xslot = [&](uint32_t g) { return smem + (g % L::kXSlots) * X_CHUNKS; };
+  auto wslot = [&](uint32_t g) { return smem + L::kWBase + (g & 1) * L::kWSize; };
+  auto wave_words = [&](uint32_t g) { return reinterpret_cast<const uint32_t*>(wslot(g) + L::kW) + wave * 256; };
+
+  // Weights and scales of group g (clamped to the last group: a repeat lands
+  // in a slot nobody reads) into weight slot g & 1.
+  auto issue_w = [&](uint32_t g) {
+    uint4* st = wslot(g);
+    const uint32_t gc = g < G ? g : G - 1;
+    uint32_t* wst = reinterpret_cast<uint32_t*>(st + L::kW) + wave * 256;
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
-      const uint32_t* wg = p.w[q] + (size_t)g * 16 * N;
+      const char* wg = uniform(reinterpret_cast<const char*>(p.w[q] + (size_t)gc * 16 * N));
+      if (kAligned) {
+        __builtin_amdgcn_global_load_lds(KAIO_GLOBAL(wg + lane_offset(woff)), KAIO_LDS(wst + q * WAVES * 256), 16, 0,
+                                         0);
+      } else {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        __builtin_amdgcn_global_load_lds(KAIO_GLOBAL(wg + ks * 4 * N + woff),
-                                         KAIO_LDS(wst + ((q * 4 + ks) * WAVES + wave) * 64), 4, 0, 0);
+        for (int ks = 0; ks < 4; ++ks)
+          __builtin_amdgcn_global_load_lds(KAIO_GLOBAL(uniform(wg + (size_t)ks * 16 * N) + lane_offset(woff)),
+                                           KAIO_LDS(wst + q * WAVES * 256 + ks * 64), 4, 0, 0);
+      }
     }
     if (kAligned) {
       uint32_t* sst = reinterpret_cast<uint32_t*>(st + L::kS);
       if (lane < 24)
-        __builtin_amdgcn_global_load_lds(KAIO_GLOBAL(s_lane + (size_t)g * N + scolc),
+        __builtin_amdgcn_global_load_lds(KAIO_GLOBAL(s_lane + (size_t)gc * N + scolc),
                                          KAIO_LDS(sst + wave * 24), 4, 0, 0);
     }
+  };
+  // x of group g (clamped likewise) into x slot g % (XDIST+1).
+  auto issue_x = [&](uint32_t g) {
+    uint4* xst = xslot(g);
+    const char* xsrc = uniform(xblk + (size_t)(g < G ? g : G - 1) * kGroup * 2);
+#pragma unroll
+    for (int i = 0; i < XPER; ++i)
+      __builtin_amdgcn_global_load_lds(KAIO_GLOBAL(xsrc + lane_offset(xoff[i])),
+                                       KAIO_LDS(xst + (i * WAVES + wave) * 64), 16, 0, 0);
+  };
+  // where group g's scales for this lane's column are read from
+  auto scale_src = [&](uint32_t g, const uint16_t* (&ns)[3]) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+      ns[q] = kAligned ? reinterpret_cast<const uint16_t*>(wslot(g) + L::kS) + wave * 48 + q * 16 + l16
+                       : p.s[q] + (size_t)(g < G ? g : G - 1) * N + colc;
   };
 
   floatx4 acc[RT][3];
@@ -155,74 +281,44 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
 #pragma unroll
     for (int q = 0; q < 3; ++q) acc[r][q] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // prologue: stages 0 .. NSTAGE-2 (clamped past the end so every stage issues
-  // the same number of loads and the waits below stay exact)
+  // Prologue: x of groups 0 .. XDIST-1 in flight, group 0 in place and unpacked.
+  half8_t bq[3][4];
+  float sf[3];
+  issue_w(0);
 #pragma unroll
-  for (int st = 0; st < NSTAGE - 1; ++st) issue_stage((uint32_t)st < G ? st : G - 1, st);
-
-  for (uint32_t g = 0; g < G; ++g) {
-    // stage g has landed for this wave; after the barrier, for every wave
-    wait_vm_barrier<(NSTAGE - 2) * VM_PER_STAGE>();
-    // A clamped stage past the end lands in the slot of group g-1, which
-    // nobody reads again.
-    issue_stage(g + NSTAGE - 1 < G ? g + NSTAGE - 1 : G - 1, (g + NSTAGE - 1) % NSTAGE);
-
-    const uint4* st = smem + (g % NSTAGE) * L::kSize;
-    const uint4* xs = st + L::kX;
-    const uint32_t* wst = reinterpret_cast<const uint32_t*>(st + L::kW);
-    float sf[3];
-    if (kAligned) {
-      const uint16_t* sst = reinterpret_cast<const uint16_t*>(st + L::kS);
-#pragma unroll
-      for (int q = 0; q < 3; ++q) sf[q] = h2f(sst[wave * 48 + q * 16 + l16]);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 3; ++q) sf[q] = h2f(p.s[q][(size_t)g * N + colc]);
-    }
-
-    // Software-pipelined tile-major order.  Unpack the group's 12 weight
-    // words once; then per row tile r: fetch the A fragments of tile r+1,
-    // run tile r's three 4-deep MFMA chains, and fold tile r-1's finished
-    // partials into acc while those MFMAs execute.  Scheduling barriers keep
-    // the compiler from hoisting every tile's LDS reads (register blow-up).
-    half8_t bq[3][4];
+  for (int d = 0; d < XDIST; ++d) issue_x(d);
+  wait_vm_barrier<0>();
+  {
+    const uint32_t* w0 = wave_words(0);
 #pragma unroll
     for (int q = 0; q < 3; ++q)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) bq[q][ks] = unpack_int4x8(wst[((q * 4 + ks) * WAVES + wave) * 64 + lane]);
-    auto load_a = [&](int r, half8_t (&a)[4]) {
-      const uint32_t row = r * 16 + l16;
+      for (int ks = 0; ks < 4; ++ks) bq[q][ks] = unpack_int4x8(w0[q * WAVES * 256 + ks * 64 + lane]);
+    const uint16_t* ns[3];
+    scale_src(0, ns);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        a[ks] = __builtin_bit_cast(half8_t, xs[row * KC + ((ks * 4 + kb) ^ (row & 15))]);
-    };
-    half8_t abuf[2][4];
-    floatx4 pbuf[2][3];
-    load_a(0, abuf[0]);
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      if (r + 1 < RT) load_a(r + 1, abuf[(r + 1) & 1]);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int q = 0; q < 3; ++q)
-          pbuf[r & 1][q] = mfma16x16x32(abuf[r & 1][ks], bq[q][ks],
-                                        ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : pbuf[r & 1][q]);
-      if (r > 0) {
-#pragma unroll
-        for (int q = 0; q < 3; ++q)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[r - 1][q][i] = __builtin_fmaf(pbuf[(r - 1) & 1][q][i], sf[q], acc[r - 1][q][i]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int q = 0; q < 3; ++q)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[RT - 1][q][i] = __builtin_fmaf(pbuf[(RT - 1) & 1][q][i], sf[q], acc[RT - 1][q][i]);
+    for (int q = 0; q < 3; ++q) sf[q] = h2f(*ns[q]);
   }
+
+  // Per group g, after one barrier: weights of g+1 and x of g+XDIST are
+  // issued (weights first), then the tiles of g run, during whose tail the
+  // wave unpacks group g+1 (its own loads: it waits with vmcnt(XPER), which
+  // leaves only the newest x in flight).  At the barrier x of g is in place
+  // everywhere (the per-wave waits since have covered it) and every wave is
+  // done with x slot of g-1 and weight slot of g-1, the slots overwritten
+  // next.  Every group issues the same loads (clamped past the end), so the
+  // counts in the waits are exact; past the last group the tail unpacks a
+  // repeat that nothing uses.  (Barrier and loads sit at the top of the
+  // body so that no branch follows the MFMA block.)
+  for (uint32_t g = 0; g < G; ++g) {
+    wait_vm_barrier<(XDIST - 1) * XPER>();
+    issue_w(g + 1);
+    issue_x(g + XDIST);
+    const uint16_t* ns[3];
+    scale_src(g + 1, ns);
+    group_mma<WAVES, XPER>(acc, bq, sf, xslot(g), wave_words(g + 1), ns, l16, kb, lane);
+  }
+  wait_vm_barrier<0>();   // no load is still writing the ring the epilogue reuses
 
   // ---- epilogue: one output at a time through LDS -----------------------------
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
@@ -259,14 +355,14 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   }
 }
 
-template <int WAVES, int NSTAGE, bool kAligned>
+template <int WAVES, int XDIST, bool kAligned>
 hipError_t launch_variant(const QkvProblem& p, hipStream_t stream) {
   constexpr int BN = 16 * WAVES;
   const uint32_t mtiles = (p.m + BM - 1) / BM;
   const uint32_t ntiles = (p.n + BN - 1) / BN;
-  const size_t lds = (size_t)NSTAGE * StageLayout<WAVES>::kSize * 16;
+  const size_t lds = (size_t)RingLayout<WAVES, XDIST>::kSize * 16;
   const dim3 grid(mtiles * ntiles), block(WAVES * 64);
-  auto* kern = &qkv_prefill_kernel<WAVES, NSTAGE, kAligned>;
+  auto* kern = &qkv_prefill_kernel<WAVES, XDIST, kAligned>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
@@ -278,8 +374,8 @@ hipError_t launch_variant(const QkvProblem& p, hipStream_t stream) {
 
 hipError_t launch_qkv_prefill(const QkvProblem& p, hipStream_t stream) {
   // 16-byte output rows and f16-pair scale loads need n % 8 == 0
-  if (p.n % 8 == 0) return launch_variant<kPrefillWaves, kPrefillStages, true>(p, stream);
-  return launch_variant<kPrefillWaves, kPrefillStages, false>(p, stream);
+  if (p.n % 8 == 0) return launch_variant<kPrefillWaves, KAIO_PREFILL_XDIST, true>(p, stream);
+  return launch_variant<kPrefillWaves, KAIO_PREFILL_XDIST, false>(p, stream);
 }
 
 }  // namespace kaio
