@@ -165,6 +165,52 @@ def summarize(dirs):
                       ", ".join(f"{c}={avg[c]:.6g}" for c in keys))
 
 
+def write_traffic(key: str, src: str, fetch_dir: str, write_dir: str, command: str):
+    """Record HBM bytes per launch of one kernel from two rocprofv3 --pmc runs.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one counter per run) are each
+    scaled by what the same counter reads for the 256 MiB calibration copy of
+    `--copy-calibration` in the same run; the entry is stamped with the kernel
+    source hash so that bench.py stops using it once the kernel changes."""
+    import csv
+    import collections
+    import glob
+
+    def per_dispatch(d, counter):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not f:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        vals, names = collections.defaultdict(float), {}
+        for r in csv.DictReader(open(f[0])):
+            if r["Counter_Name"] == counter:
+                vals[r["Dispatch_Id"]] += float(r["Counter_Value"])
+                names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        kern = [v for dsp, v in vals.items() if key + "_kernel" in names[dsp]]
+        copy = [v for dsp, v in vals.items() if "copy" in names[dsp].lower()]
+        if not kern or not copy:
+            raise SystemExit(f"{counter}: no {key} dispatch or no calibration copy under {d}")
+        return sum(kern) / len(kern), max(copy), len(kern)
+
+    calib_kib = (256 << 20) / 1024
+    fk, fc, nf = per_dispatch(fetch_dir, "FETCH_SIZE")
+    wk, wc, nw = per_dispatch(write_dir, "WRITE_SIZE")
+    fs, ws = calib_kib / fc, calib_kib / wc
+    entry = {"source_hash": kernel_source_hash(src), "fetch_kib_raw": round(fk, 1), "write_kib_raw": round(wk, 1),
+             "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+             "bytes_per_launch": int(fk * fs * 1024 + wk * ws * 1024),
+             "read_bytes_per_launch": int(fk * fs * 1024), "write_bytes_per_launch": int(wk * ws * 1024),
+             "dispatches": [nf, nw], "command": command}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    data[key] = entry
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(data, f, indent=1)
+    print(json.dumps({key: entry}, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,9 +223,18 @@ def main():
                     help="also run one plain 256 MiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
                     help="summarize rocprofv3 CSV output directories instead of benchmarking")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("KERNEL", "SOURCE", "FETCH_DIR", "WRITE_DIR"),
+                    help="record HBM bytes per launch of qkv_prefill|qkv_decode (source file name under csrc/) "
+                         "from FETCH_SIZE and WRITE_SIZE counter runs into profiles/traffic.json")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize)
+        return
+    if args.write_traffic:
+        key, src, fdir, wdir = args.write_traffic
+        write_traffic(key, src, fdir, wdir,
+                      f"rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -d <dir> -o run -- python3 bench.py "
+                      f"--only {key.split('_')[1]} --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration")
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library has no "

@@ -45,7 +45,7 @@ constexpr int KC = kGroup / 8;          // 16-byte chunks per row per group
 constexpr int X_CHUNKS = BM * KC;       // 16-byte chunks of x per stage (32 KiB)
 
 #ifndef KAIO_PREFILL_XDIST
-#define KAIO_PREFILL_XDIST 2
+#define KAIO_PREFILL_XDIST 1
 #endif
 #ifndef KAIO_PREFILL_SM
 #define KAIO_PREFILL_SM 4
@@ -69,19 +69,20 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// LDS rings, in 16-byte units.  x of a group is fetched XDIST groups ahead
-// (ring of XDIST+1 slots); the weights and scales one group ahead (2 slots):
-//   x  [XDIST+1][X_CHUNKS]           swizzled rows of x
-//   w  [2] x { [3][WAVES][16][16] u32   packed rows x columns of output q, wave w
-//              [3][WAVES][8] u32 }      pairs of f16 scales of the wave's 16 columns
+// LDS, in 16-byte units.  x of a group is fetched XDIST groups ahead (ring
+// of XDIST+1 slots), the packed weights one group ahead (2 slots), and the
+// scales SCHUNK groups at a time:
+//   x  [XDIST+1][X_CHUNKS]            swizzled rows of x
+//   w  [2][3][WAVES][16][16] u32      packed rows x columns of output q, wave w
+//   s  [3][WAVES][SCHUNK][16] f16     scales of the wave's 16 columns (n % 8 == 0)
+constexpr int SCHUNK = 32;
 template <int WAVES, int XDIST>
 struct RingLayout {
   static constexpr int kXSlots = XDIST + 1;
   static constexpr int kWBase = kXSlots * X_CHUNKS;
-  static constexpr int kW = 0;                                   // within a weight slot
-  static constexpr int kS = 3 * WAVES * 256 / 4;
-  static constexpr int kWSize = kS + (3 * WAVES * 8 + 3) / 4;
-  static constexpr int kSize = kWBase + 2 * kWSize;              // uint4
+  static constexpr int kWSize = 3 * WAVES * 256 / 4;
+  static constexpr int kSBase = kWBase + 2 * kWSize;
+  static constexpr int kSize = kSBase + 3 * WAVES * SCHUNK * 16 * 2 / 16;   // uint4
 };
 
 // A wave-uniform pointer the compiler must treat as opaque (kept in SGPRs):
@@ -220,24 +221,23 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   // 4-byte path: lane (kb, c) fetches packed row 4 ks + kb, column c.
   const uint32_t c4 = n0 + wave * 16 + 4 * (lane & 3);
   const uint32_t woff = kAligned ? ((lane >> 2) * N + (c4 < N ? c4 : N - 4)) * 4 : (kb * N + colc) * 4;
-  // scale pairs: lanes 0..23 fetch the f16 pair (2j, 2j+1) of output q = lane / 8
-  const uint32_t sq = lane >> 3, sj = lane & 7;
-  const uint32_t scol = n0 + wave * 16 + 2 * sj;
-  const uint32_t scolc = (scol < N) ? scol : (N >= 2 ? N - 2 : 0);   // N even on this path
-  // select (not index) the scale tensor: a lane-dependent index into the
-  // kernel arguments would be fetched from memory
-  const uint16_t* s_lane = sq == 0 ? p.s[0] : (sq == 1 ? p.s[1] : p.s[2]);
+  // Scales (n % 8 == 0): lane l fetches the 8 columns 8(l % 2) .. +7 of the
+  // wave's 16 for group l / 2 of a chunk -- one 16-byte load per output per
+  // SCHUNK groups.
+  const uint32_t s8 = n0 + wave * 16 + 8 * (lane & 1);
+  const uint32_t s8c = s8 < N ? s8 : N - 8;
+  const uint32_t sgi = lane >> 1;     // group within the chunk
 
   auto xslot = [&](uint32_t g) { return smem + (g % L::kXSlots) * X_CHUNKS; };
   auto wslot = [&](uint32_t g) { return smem + L::kWBase + (g & 1) * L::kWSize; };
-  auto wave_words = [&](uint32_t g) { return reinterpret_cast<const uint32_t*>(wslot(g) + L::kW) + wave * 256; };
+  auto wave_words = [&](uint32_t g) { return reinterpret_cast<const uint32_t*>(wslot(g)) + wave * 256; };
+  uint16_t* const sbuf = reinterpret_cast<uint16_t*>(smem + L::kSBase);
 
-  // Weights and scales of group g (clamped to the last group: a repeat lands
-  // in a slot nobody reads) into weight slot g & 1.
+  // Weights of group g (clamped to the last group: a repeat lands in a slot
+  // nobody reads) into weight slot g & 1.
   auto issue_w = [&](uint32_t g) {
-    uint4* st = wslot(g);
     const uint32_t gc = g < G ? g : G - 1;
-    uint32_t* wst = reinterpret_cast<uint32_t*>(st + L::kW) + wave * 256;
+    uint32_t* wst = reinterpret_cast<uint32_t*>(wslot(g)) + wave * 256;
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
       const char* wg = uniform(reinterpret_cast<const char*>(p.w[q] + (size_t)gc * 16 * N));
@@ -251,12 +251,17 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
                                            KAIO_LDS(wst + q * WAVES * 256 + ks * 64), 4, 0, 0);
       }
     }
-    if (kAligned) {
-      uint32_t* sst = reinterpret_cast<uint32_t*>(st + L::kS);
-      if (lane < 24)
-        __builtin_amdgcn_global_load_lds(KAIO_GLOBAL(s_lane + (size_t)gc * N + scolc),
-                                         KAIO_LDS(sst + wave * 24), 4, 0, 0);
-    }
+  };
+  // Scales of groups c0 .. c0+SCHUNK-1 (clamped to the last group) for the
+  // wave's columns into the scale buffer (n % 8 == 0 only).
+  auto issue_s = [&](uint32_t c0) {
+    const uint32_t gi = c0 + sgi < G ? sgi : G - 1 - c0;
+    const uint32_t off = (gi * N + s8c) * 2;
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+      __builtin_amdgcn_global_load_lds(KAIO_GLOBAL(uniform(reinterpret_cast<const char*>(p.s[q] + (size_t)c0 * N)) +
+                                                   lane_offset(off)),
+                                       KAIO_LDS(sbuf + (q * WAVES + wave) * SCHUNK * 16), 16, 0, 0);
   };
   // x of group g (clamped likewise) into x slot g % (XDIST+1).
   auto issue_x = [&](uint32_t g) {
@@ -271,7 +276,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   auto scale_src = [&](uint32_t g, const uint16_t* (&ns)[3]) {
 #pragma unroll
     for (int q = 0; q < 3; ++q)
-      ns[q] = kAligned ? reinterpret_cast<const uint16_t*>(wslot(g) + L::kS) + wave * 48 + q * 16 + l16
+      ns[q] = kAligned ? sbuf + ((q * WAVES + wave) * SCHUNK + g % SCHUNK) * 16 + l16
                        : p.s[q] + (size_t)(g < G ? g : G - 1) * N + colc;
   };
 
@@ -284,6 +289,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   // Prologue: x of groups 0 .. XDIST-1 in flight, group 0 in place and unpacked.
   half8_t bq[3][4];
   float sf[3];
+  if (kAligned) issue_s(0);
   issue_w(0);
 #pragma unroll
   for (int d = 0; d < XDIST; ++d) issue_x(d);
@@ -313,6 +319,9 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   for (uint32_t g = 0; g < G; ++g) {
     wait_vm_barrier<(XDIST - 1) * XPER>();
     issue_w(g + 1);
+    // the next scale chunk replaces this one once the tail of g-1 has read
+    // the last scale it needed (the scale of g, before the barrier)
+    if (kAligned && (g + 1) % SCHUNK == 0 && g + 1 < G) issue_s(g + 1);
     issue_x(g + XDIST);
     const uint16_t* ns[3];
     scale_src(g + 1, ns);

@@ -62,6 +62,8 @@ def test_tiny_config_all_outputs():
     (1, 100, 128), (7, 100, 256), (8, 64, 128), (8, 65, 384), (9, 100, 128), (16, 8, 128),
     (17, 72, 384), (128, 64, 128), (129, 65, 128), (130, 200, 256), (1, 1, 128), (300, 24, 640),
     (64, 4, 128), (3, 4099, 256), (200, 1000, 1024),
+    # more than 32 groups: the tile kernel reloads its per-chunk scales
+    (33, 72, 4480), (129, 136, 8320), (20, 12, 4224),
 ])
 def test_ragged_shapes(M, N, K):
     inp = workloads.qkv_inputs(M, N, K, seed=M * 7919 + N * 31 + K)
