@@ -72,7 +72,8 @@ typedef enum kaio_dtype {
  *
  * Validation order: group_size != 128 -> UNSUPPORTED; k % 128 != 0 ->
  * INVALID_PROBLEM; m == 0 or n == 0 -> OK (nothing launched); sizes too
- * large for one launch -> INVALID_PROBLEM; null pointer (weights/scales/x
+ * large for one launch (n >= 2^26, k >= 2^24, any tensor of 2^62 bytes or
+ * more, or more than 2^24 - 1 workgroups) -> INVALID_PROBLEM; null pointer (weights/scales/x
  * only when k > 0) -> INVALID_ARGUMENT; misaligned pointer ->
  * INVALID_ARGUMENT; an output overlapping an input or another output ->
  * INVALID_ARGUMENT; device -> DEVICE; launch -> LAUNCH.  k == 0 writes

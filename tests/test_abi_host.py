@@ -76,6 +76,9 @@ def test_qkv_validation_order_and_messages():
     assert st == ARG and "overlaps x" in msg
     st, msg = qkv(m=2 ** 32 - 1, n=2 ** 32 - 1)
     assert st == PROB and "too large" in msg
+    # the documented per-dimension limits (32-bit per-lane byte offsets in the kernels)
+    assert qkv(m=16, n=2 ** 26, k=128)[0] == PROB
+    assert qkv(m=16, n=8, k=2 ** 24)[0] == PROB
 
 
 @no_gpu_only
