@@ -3,20 +3,22 @@
 // Operation: kaio-candle 0.2.0, src/matmul_tc_async.rs (module doc;
 // MatmulTcAsyncOp::cuda_fwd: A [m,k] and B [k,n] f16, a zeroed [m,n] f32
 // output that the kernel writes).  The pages stage tiles global -> shared
-// with cp.async on sm_80+; here the tiles go global -> registers -> LDS with
-// the next tile's loads in flight during the current tile's MFMAs.
+// with cp.async on sm_80+; here the main path moves them global -> LDS with
+// gfx950's direct loads, the fallback through registers.
 //
 // gfx950 design
 // -------------
-// * Workgroup = 4 waves, tile 256 x 256, k-step 64; each wave owns a
-//   128 x 128 sub-tile = 8 x 8 v_mfma_f32_16x16x32_f16 accumulators
-//   (256 f32 per lane), which keeps LDS traffic at 16 bytes/clock per SIMD.
-// * A [m,k] is K-contiguous, which is the MFMA A-operand order (8
-//   consecutive k per lane): stored as is, XOR-swizzled per 16-byte chunk.
-// * B [k,n] is N-contiguous; the B operand needs 8 consecutive k of one
-//   column.  Each thread loads an 8 (k) x 8 (n) block and transposes it in
-//   registers (16-bit shuffles within the thread), so LDS holds B^T [n][k]
-//   and the operand reads are plain 16-byte, conflict-free reads.
+// * Workgroup = 4 waves, tile 256 x 256; each wave owns a 128 x 128 sub-tile
+//   = 8 x 8 v_mfma_f32_16x16x32_f16 accumulators (256 f32 per lane, held in
+//   the accumulation registers), the largest tile the register file allows,
+//   which keeps LDS traffic per MFMA lowest.
+// * Main path (k % 64 == 0, n % 8 == 0): A [m,k] and B [k,n] tiles land in
+//   LDS in their natural layouts via 16-byte direct loads (two 64-k stages,
+//   one barrier per stage, the loads spread between MFMAs).  A is already in
+//   MFMA A-operand order (8 consecutive k per lane); the B operand (8
+//   consecutive k of one column) comes from the transposing LDS read.
+// * Fallback (any other shape): tiles go global -> registers -> LDS, B
+//   transposed in registers (8x8 blocks of 16-bit values) so LDS holds B^T.
 // * Epilogue: f32 stores straight from the accumulators.
 
 #include "common.hpp"
@@ -170,6 +172,190 @@ gemm_f16f32_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
     }
 }
 
+// ---------------------------------------------------------------------------
+// DMA path (k % 64 == 0, n % 8 == 0): both tiles go global -> LDS with
+// 16-byte direct loads in their natural layouts, two stages deep, no
+// registers and no VALU on the way.  A fragments are plain 16-byte LDS reads;
+// B fragments come from gfx950's transposing LDS read (ds_read_b64_tr_b16):
+// within each 16-lane group, lane i receives element i % 4 of the 8-byte
+// chunks that lanes 4j + i / 4 address, j = 0..3.  Lane a of a group
+// addresses row k0 + a / 4, columns 4(a % 4) .. +3 of the [k][n] tile, so
+// lane i gets B[k0 + j][i] for j = 0..3: four consecutive k of its column,
+// and two such reads make its eight-k MFMA B operand.
+//   A tile [256][64]: chunk kc of row r at slot r*8 + (kc ^ (r & 7)).
+//   B tile [64][256]: chunk c of k-row r at slot r*32 + (c ^ 2(r & 3)); the
+//   four k-rows a transposing read touches then sit in four different
+//   32-byte bank groups.
+// ---------------------------------------------------------------------------
+#define KAIO_GEMM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define KAIO_GEMM_GLOBAL(p) ((__attribute__((address_space(1))) const void*)(p))
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+constexpr int DBK = 64;
+constexpr int DSTAGE = BM * KCH + DBK * (BN / 8);   // uint4 per stage: A 2048 + B 2048
+
+__device__ __forceinline__ const char* sgpr_ptr(const char* p) {
+  asm volatile("" : "+s"(p));
+  return p;
+}
+__device__ __forceinline__ uint32_t vgpr_u32(uint32_t o) {
+  asm volatile("" : "+v"(o));
+  return o;
+}
+
+struct GemmFrags {
+  half8_t a[TT], b[TT];
+};
+
+// Fragments of one 32-k step from one LDS stage.  The stage pointers are
+// restrict-qualified: that tells the compiler these reads do not touch the
+// stage the global->LDS loads in flight are writing, so it does not make
+// them wait for those loads.
+__device__ __forceinline__ void load_gemm_frags(const uint4* __restrict__ as, const char* __restrict__ bs, int ks,
+                                                uint32_t arow0, uint32_t bk_lane, uint32_t bcol, uint32_t kb,
+                                                GemmFrags& f) {
+#pragma unroll
+  for (int c = 0; c < TT; ++c) {
+    const uint32_t col = bcol + c * 16;
+    short4_t h[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const uint32_t k = ks * 32 + bk_lane + 4 * hf;
+      const uint32_t off = (k * 32 + ((col >> 3) ^ (2 * (k & 3)))) * 16 + ((col >> 2) & 1) * 8;
+      h[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(bs + off));
+    }
+    f.b[c] = __builtin_bit_cast(half8_t, (short __attribute__((ext_vector_type(8)))){
+        h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]});
+  }
+#pragma unroll
+  for (int r = 0; r < TT; ++r) {
+    const uint32_t row = arow0 + r * 16;
+    f.a[r] = __builtin_bit_cast(half8_t, as[row * KCH + ((ks * 4 + kb) ^ (row & 7))]);
+  }
+}
+
+__global__ void __launch_bounds__(THREADS, 1)
+gemm_f16f32_dma_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, float* __restrict__ C,
+                       uint32_t M, uint32_t N, uint32_t K, uint32_t mtiles, uint32_t ntiles) {
+  extern __shared__ uint4 smem[];
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t kb = lane >> 4, l16 = lane & 15;
+  const uint32_t wm = wave >> 1, wn = wave & 1;
+
+  uint32_t tm, tn;
+  tile_of<4, 8>(blockIdx.x, gridDim.x, mtiles, ntiles, tm, tn);
+  const uint32_t m0 = tm * BM, n0 = tn * BN;
+
+  // per-lane byte offsets of the 16-byte chunks this lane moves (8 of A, 8
+  // of B per stage); rows past M and chunks past N repeat valid ones
+  uint32_t aoff[8], boff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t s = (i * 4 + wave) * 64 + lane;
+    const uint32_t r = s >> 3, kc = (s & 7) ^ (r & 7);
+    const uint32_t rc = (m0 + r < M) ? r : M - 1 - m0;
+    aoff[i] = (rc * K + kc * 8) * 2;
+    const uint32_t br = s >> 5, c = (s & 31) ^ (2 * (br & 3));
+    const uint32_t cc = (n0 + c * 8 < N) ? c * 8 : N - 8 - n0;
+    boff[i] = (br * N + cc) * 2;
+  }
+  const char* abase = reinterpret_cast<const char*>(A + (size_t)m0 * K);
+  const char* bbase = reinterpret_cast<const char*>(B + n0);
+
+  // load j (0..7: A chunks, 8..15: B chunks) of this lane's share of stage kt
+  auto issue_one = [&](uint32_t kt, uint32_t buf, int j) {
+    uint4* st = smem + buf * DSTAGE;
+    if (j < 8) {
+      const char* as = sgpr_ptr(abase + (size_t)kt * DBK * 2);
+      __builtin_amdgcn_global_load_lds(KAIO_GEMM_GLOBAL(as + vgpr_u32(aoff[j])),
+                                       KAIO_GEMM_LDS(st + (j * 4 + wave) * 64), 16, 0, 0);
+    } else {
+      const char* bs = sgpr_ptr(bbase + (size_t)kt * DBK * N * 2);
+      __builtin_amdgcn_global_load_lds(KAIO_GEMM_GLOBAL(bs + vgpr_u32(boff[j - 8])),
+                                       KAIO_GEMM_LDS(st + BM * KCH + ((j - 8) * 4 + wave) * 64), 16, 0, 0);
+    }
+  };
+  auto issue_stage = [&](uint32_t kt, uint32_t buf) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) issue_one(kt, buf, j);
+  };
+
+  floatx4 acc[TT][TT];
+#pragma unroll
+  for (int r = 0; r < TT; ++r)
+#pragma unroll
+    for (int c = 0; c < TT; ++c) acc[r][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // lane-invariant parts of the fragment addresses
+  const uint32_t arow0 = wm * WT + l16;                    // + 16 rt
+  const uint32_t bk_lane = kb * 8 + (l16 >> 2);            // k-row within the 32-k step (+ 4 for the 2nd read)
+  const uint32_t bcol = wn * WT + 4 * (l16 & 3);           // + 16 ct
+
+  auto load_frags = [&](uint32_t buf, int ks, GemmFrags& f) {
+    load_gemm_frags(smem + buf * DSTAGE, reinterpret_cast<const char*>(smem + buf * DSTAGE + BM * KCH), ks, arow0,
+                    bk_lane, bcol, kb, f);
+  };
+  auto mma = [&](const GemmFrags& f) {
+#pragma unroll
+    for (int r = 0; r < TT; ++r)
+#pragma unroll
+      for (int c = 0; c < TT; ++c) acc[r][c] = mfma16x16x32(f.a[r], f.b[c], acc[r][c]);
+  };
+  // the same, with stage kt's 16 loads spread two per 8 MFMAs, so that no
+  // wave stalls behind a burst of loads the address unit cannot take yet
+  auto mma_issue = [&](const GemmFrags& f, uint32_t kt, uint32_t buf) {
+#pragma unroll
+    for (int r = 0; r < TT; ++r) {
+#pragma unroll
+      for (int c = 0; c < TT; ++c) acc[r][c] = mfma16x16x32(f.a[r], f.b[c], acc[r][c]);
+      issue_one(kt, buf, 2 * r);
+      issue_one(kt, buf, 2 * r + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Two 32-k steps per stage.  Fragments are loaded one step ahead of the
+  // MFMAs that use them.  Barrier k sits between the two steps of stage k:
+  // stage k+1 has landed everywhere and every wave holds all of stage k in
+  // registers, so stage k+2 then goes into stage k's buffer, a full stage
+  // ahead of its use.
+  const uint32_t nk = K / DBK;
+  GemmFrags f0, f1;
+  issue_stage(0, 0);
+  if (nk > 1) {
+    issue_stage(1, 1);
+    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+  load_frags(0, 0, f0);
+  for (uint32_t kt = 0; kt < nk; ++kt) {
+    const uint32_t buf = kt & 1;
+    load_frags(buf, 1, f1);
+    mma(f0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (kt + 1 < nk) load_frags(buf ^ 1, 0, f0);
+    // stage kt+2, or a repeat of the last stage into this buffer, which
+    // nobody reads again (keeps the loop free of a branch around the MFMAs)
+    mma_issue(f1, kt + 2 < nk ? kt + 2 : nk - 1, buf);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+#pragma unroll
+  for (int r = 0; r < TT; ++r)
+#pragma unroll
+    for (int c = 0; c < TT; ++c) {
+      const uint32_t gc = n0 + wn * WT + c * 16 + l16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t gr = m0 + wm * WT + r * 16 + 4 * kb + i;
+        if (gr < M && gc < N) C[(size_t)gr * N + gc] = acc[r][c][i];
+      }
+    }
+}
+
 __global__ void fill_zero_kernel(uint4* __restrict__ dst, size_t n16, uint8_t* __restrict__ tail, uint32_t ntail) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
@@ -184,7 +370,14 @@ hipError_t launch_gemm_f16f32(const uint16_t* a, const uint16_t* b, float* c,
   const uint32_t mtiles = (m + BM - 1) / BM;
   const uint32_t ntiles = (n + BN - 1) / BN;
   const dim3 grid(mtiles * ntiles), block(THREADS);
-  if (k % 8 == 0 && n % 8 == 0)
+  // DMA path: 32-bit per-lane byte offsets need 256 * k * 2 and 64 * n * 2 below 2^31
+  if (k > 0 && k % DBK == 0 && n % 8 == 0 && k < (1u << 22) && n < (1u << 24)) {
+    const size_t lds = (size_t)2 * DSTAGE * 16;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_f16f32_dma_kernel),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(gemm_f16f32_dma_kernel, grid, block, lds, stream, a, b, c, m, n, k, mtiles, ntiles);
+  } else if (k % 8 == 0 && n % 8 == 0)
     hipLaunchKernelGGL(gemm_f16f32_kernel<true>, grid, block, 0, stream, a, b, c, m, n, k, mtiles);
   else
     hipLaunchKernelGGL(gemm_f16f32_kernel<false>, grid, block, 0, stream, a, b, c, m, n, k, mtiles);

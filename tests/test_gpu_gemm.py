@@ -31,14 +31,17 @@ def test_identity_and_exact_integers():
     rng = np.random.default_rng(1)
     a = rng.standard_normal((64, 96)).astype(np.float16)
     assert np.array_equal(run(a, np.eye(96, dtype=np.float16)), a.astype(np.float32))
-    ai = rng.integers(-8, 9, size=(300, 1024)).astype(np.float16)
-    bi = rng.integers(-8, 9, size=(1024, 260)).astype(np.float16)
-    c, _ = gemm(ai, bi)
-    assert np.array_equal(run(ai, bi), c.astype(np.float32))
+    for n in (260, 264):   # 264: the direct-to-LDS path
+        ai = rng.integers(-8, 9, size=(300, 1024)).astype(np.float16)
+        bi = rng.integers(-8, 9, size=(1024, n)).astype(np.float16)
+        c, _ = gemm(ai, bi)
+        assert np.array_equal(run(ai, bi), c.astype(np.float32))
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 7), (300, 200, 100), (257, 259, 72), (100, 100, 4096),
-                                   (513, 300, 520), (16, 1000, 33), (256, 256, 64)])
+                                   (513, 300, 520), (16, 1000, 33), (256, 256, 64),
+                                   # k % 64 == 0 and n % 8 == 0: the direct-to-LDS path, ragged m and n
+                                   (300, 264, 128), (513, 136, 192), (40, 520, 64), (257, 8, 256)])
 def test_ragged_shapes(M, N, K):
     a, b = workloads.gemm_inputs(M, N, K, seed=M + N + K)
     c, t = gemm(a, b)
