@@ -11,14 +11,15 @@
 // * f16: the product of two f16 values (<= 22 significant bits, magnitude
 //   >= 2^-48) is exact in f32; one f32 -> f16 conversion rounds it.
 // * bf16: the product of two bf16 values (<= 16 significant bits) is exact in
-//   f32 whenever it lies in the f32 normal range; it is then rounded to
-//   bf16 by integer round-to-nearest-even.  Below 2^-126 (where f32 itself
+//   f32 whenever it lies in the f32 normal range; gfx950's f32 -> bf16
+//   conversion then rounds it to nearest even.  Below 2^-126 (where f32 itself
 //   would round) the product is formed exactly in f64 and rounded to a
 //   multiple of 2^-133, the bf16 subnormal spacing.
 //
 // gfx950 design: HBM-bound streaming.  A workgroup (256 threads) covers
-// 4 x 256 consecutive 16-byte vectors of one row; all four loads of dy are
-// issued before any store.  With 16-byte alignment and g a multiple of the
+// UNROLL x 256 consecutive 16-byte vectors of one row (UNROLL = 1 measured
+// fastest: many small workgroups keep the most loads in flight).  With
+// 16-byte alignment and g a multiple of the
 // vector width every vector lies in one group and needs one scale; other
 // shapes take an element-wise path with the same arithmetic.
 
@@ -31,7 +32,10 @@ namespace kaio {
 namespace {
 
 constexpr int THREADS = 256;
-constexpr int UNROLL = 4;
+#ifndef KAIO_BWD_UNROLL
+#define KAIO_BWD_UNROLL 1
+#endif
+constexpr int UNROLL = KAIO_BWD_UNROLL;
 
 struct F32 {
   using T = float;
@@ -62,9 +66,15 @@ struct BF16 {
       const double k = rint(fabs(pd) * 0x1p133);        // <= 128; 128 is the smallest normal
       return (T)(((u >> 16) & 0x8000u) | (uint32_t)k);
     }
+#ifdef KAIO_BWD_SOFT_RNE
     if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0u)
       return (T)((u >> 16) | 0x0040u);                   // NaN stays NaN (quiet)
     return (T)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);   // RNE; overflow carries into inf
+#else
+    // the product is exact in f32 here: gfx950's f32 -> bf16 conversion
+    // rounds it once, to nearest even (overflow to inf, NaN stays NaN)
+    return __builtin_bit_cast(uint16_t, (__bf16)p);
+#endif
   }
 };
 
