@@ -44,6 +44,9 @@ constexpr int RT = BM / 16;             // row tiles per wave
 constexpr int KC = kGroup / 8;          // 16-byte chunks per row per group
 constexpr int X_CHUNKS = BM * KC;       // 16-byte chunks of x per stage (32 KiB)
 
+#ifndef KAIO_PREFILL_XSPREAD
+#define KAIO_PREFILL_XSPREAD 1
+#endif
 #ifndef KAIO_PREFILL_XDIST
 #define KAIO_PREFILL_XDIST 1
 #endif
@@ -127,11 +130,11 @@ __device__ __forceinline__ void fold(floatx4 (&acc)[3], const floatx4 (&pb)[3], 
 // stalling the start of the next group.  `next_w` points at this wave's
 // next-group words in LDS, `next_s[q]` at its scales; the wait before the
 // tail covers them (XPENDING = the x loads issued after them).
-template <int WAVES, int XPENDING>
+template <int WAVES, int XPENDING, typename IssueX>
 __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3][4], float (&sf)[3],
                                           const uint4* __restrict__ xs, const uint32_t* __restrict__ next_w,
                                           const uint16_t* const (&next_s)[3], uint32_t l16, uint32_t kb,
-                                          uint32_t lane) {
+                                          uint32_t lane, IssueX issue_x_part) {
   // A fragments two tiles ahead (three buffers); tiles RT-2 and RT-1 land
   // in buffers (RT-2) % 3 and (RT-1) % 3 during tiles RT-4 and RT-3.
   half8_t abuf[3][4];
@@ -141,6 +144,7 @@ __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3
 #pragma unroll
   for (int r = 0; r < RT - 2; ++r) {
     load_a(abuf[(r + 2) % 3], xs, r + 2, l16, kb);
+    if (r < XPENDING) issue_x_part(r);   // a later group's x, one load per tile
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -263,14 +267,16 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
                                                    lane_offset(off)),
                                        KAIO_LDS(sbuf + (q * WAVES + wave) * SCHUNK * 16), 16, 0, 0);
   };
-  // x of group g (clamped likewise) into x slot g % (XDIST+1).
-  auto issue_x = [&](uint32_t g) {
+  // Load i of x of group g (clamped likewise) into x slot g % (XDIST+1).
+  auto issue_x_one = [&](uint32_t g, int i) {
     uint4* xst = xslot(g);
     const char* xsrc = uniform(xblk + (size_t)(g < G ? g : G - 1) * kGroup * 2);
+    __builtin_amdgcn_global_load_lds(KAIO_GLOBAL(xsrc + lane_offset(xoff[i])),
+                                     KAIO_LDS(xst + (i * WAVES + wave) * 64), 16, 0, 0);
+  };
+  auto issue_x = [&](uint32_t g) {
 #pragma unroll
-    for (int i = 0; i < XPER; ++i)
-      __builtin_amdgcn_global_load_lds(KAIO_GLOBAL(xsrc + lane_offset(xoff[i])),
-                                       KAIO_LDS(xst + (i * WAVES + wave) * 64), 16, 0, 0);
+    for (int i = 0; i < XPER; ++i) issue_x_one(g, i);
   };
   // where group g's scales for this lane's column are read from
   auto scale_src = [&](uint32_t g, const uint16_t* (&ns)[3]) {
@@ -322,10 +328,18 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
     // the next scale chunk replaces this one once the tail of g-1 has read
     // the last scale it needed (the scale of g, before the barrier)
     if (kAligned && (g + 1) % SCHUNK == 0 && g + 1 < G) issue_s(g + 1);
+#if KAIO_PREFILL_XSPREAD
+    const uint16_t* ns[3];
+    scale_src(g + 1, ns);
+    // x of g + XDIST goes out one load per row tile, between MFMAs
+    group_mma<WAVES, XPER>(acc, bq, sf, xslot(g), wave_words(g + 1), ns, l16, kb, lane,
+                           [&](int i) { issue_x_one(g + XDIST, i); });
+#else
     issue_x(g + XDIST);
     const uint16_t* ns[3];
     scale_src(g + 1, ns);
-    group_mma<WAVES, XPER>(acc, bq, sf, xslot(g), wave_words(g + 1), ns, l16, kb, lane);
+    group_mma<WAVES, XPER>(acc, bq, sf, xslot(g), wave_words(g + 1), ns, l16, kb, lane, [](int) {});
+#endif
   }
   wait_vm_barrier<0>();   // no load is still writing the ring the epilogue reuses
 
