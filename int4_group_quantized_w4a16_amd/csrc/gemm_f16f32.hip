@@ -191,6 +191,12 @@ gemm_f16f32_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
 #define KAIO_GEMM_GLOBAL(p) ((__attribute__((address_space(1))) const void*)(p))
 typedef short short4_t __attribute__((ext_vector_type(4)));
 
+#ifndef KAIO_GEMM_SM
+#define KAIO_GEMM_SM 4
+#endif
+#ifndef KAIO_GEMM_SN
+#define KAIO_GEMM_SN 8
+#endif
 constexpr int DBK = 64;
 constexpr int DSTAGE = BM * KCH + DBK * (BN / 8);   // uint4 per stage: A 2048 + B 2048
 
@@ -245,7 +251,7 @@ gemm_f16f32_dma_kernel(const uint16_t* __restrict__ A, const uint16_t* __restric
   const uint32_t wm = wave >> 1, wn = wave & 1;
 
   uint32_t tm, tn;
-  tile_of<4, 8>(blockIdx.x, gridDim.x, mtiles, ntiles, tm, tn);
+  tile_of<KAIO_GEMM_SM, KAIO_GEMM_SN>(blockIdx.x, gridDim.x, mtiles, ntiles, tm, tn);
   const uint32_t m0 = tm * BM, n0 = tn * BN;
 
   // per-lane byte offsets of the 16-byte chunks this lane moves (8 of A, 8

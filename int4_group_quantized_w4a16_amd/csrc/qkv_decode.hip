@@ -146,14 +146,17 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   };
 
   if (g_begin < g_end) {
-    // two register buffers used ping-pong: chunk c+1 is in flight while chunk c computes
+    // two register buffers used ping-pong: chunk c+1 is in flight while
+    // chunk c computes.  No chunk past the wave's range is loaded: a load
+    // nobody uses would still hold up the wave's final wait.
     Chunk ca, cb;
     load_chunk(g_begin, ca);
     for (uint32_t g0 = g_begin; g0 < g_end; g0 += 2 * GCHUNK) {
-      load_chunk(g0 + GCHUNK, cb);
+      const bool more = g0 + GCHUNK < g_end;   // wave-uniform
+      if (more) load_chunk(g0 + GCHUNK, cb);
       compute_chunk(g0, ca);
-      if (g0 + GCHUNK >= g_end) break;
-      load_chunk(g0 + 2 * GCHUNK, ca);
+      if (!more) break;
+      if (g0 + 2 * GCHUNK < g_end) load_chunk(g0 + 2 * GCHUNK, ca);
       compute_chunk(g0 + GCHUNK, cb);
     }
   }
