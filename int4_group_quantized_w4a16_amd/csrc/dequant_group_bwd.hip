@@ -66,15 +66,9 @@ struct BF16 {
       const double k = rint(fabs(pd) * 0x1p133);        // <= 128; 128 is the smallest normal
       return (T)(((u >> 16) & 0x8000u) | (uint32_t)k);
     }
-#ifdef KAIO_BWD_SOFT_RNE
-    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0u)
-      return (T)((u >> 16) | 0x0040u);                   // NaN stays NaN (quiet)
-    return (T)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);   // RNE; overflow carries into inf
-#else
     // the product is exact in f32 here: gfx950's f32 -> bf16 conversion
     // rounds it once, to nearest even (overflow to inf, NaN stays NaN)
     return __builtin_bit_cast(uint16_t, (__bf16)p);
-#endif
   }
 };
 

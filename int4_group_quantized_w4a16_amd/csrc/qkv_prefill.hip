@@ -44,9 +44,6 @@ constexpr int RT = BM / 16;             // row tiles per wave
 constexpr int KC = kGroup / 8;          // 16-byte chunks per row per group
 constexpr int X_CHUNKS = BM * KC;       // 16-byte chunks of x per stage (32 KiB)
 
-#ifndef KAIO_PREFILL_XSPREAD
-#define KAIO_PREFILL_XSPREAD 1
-#endif
 #ifndef KAIO_PREFILL_XDIST
 #define KAIO_PREFILL_XDIST 1
 #endif
@@ -328,18 +325,11 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
     // the next scale chunk replaces this one once the tail of g-1 has read
     // the last scale it needed (the scale of g, before the barrier)
     if (kAligned && (g + 1) % SCHUNK == 0 && g + 1 < G) issue_s(g + 1);
-#if KAIO_PREFILL_XSPREAD
     const uint16_t* ns[3];
     scale_src(g + 1, ns);
     // x of g + XDIST goes out one load per row tile, between MFMAs
     group_mma<WAVES, XPER>(acc, bq, sf, xslot(g), wave_words(g + 1), ns, l16, kb, lane,
                            [&](int i) { issue_x_one(g + XDIST, i); });
-#else
-    issue_x(g + XDIST);
-    const uint16_t* ns[3];
-    scale_src(g + 1, ns);
-    group_mma<WAVES, XPER>(acc, bq, sf, xslot(g), wave_words(g + 1), ns, l16, kb, lane, [](int) {});
-#endif
   }
   wait_vm_barrier<0>();   // no load is still writing the ring the epilogue reuses
 
