@@ -326,7 +326,21 @@ def main():
                                     "us_per_call": round(gms * 1e3, 2), "value": round(gtf, 2),
                                     "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_F16_TFLOPS,
                                     "frac": round(gtf / PEAK_F16_TFLOPS, 4)}
-        del ad, bd, cd
+        # backward of the same product: grad f32[M,N] -> grad_a f16[M,K], grad_b f16[K,N]
+        gd = t(np.random.default_rng(c["seed"] + 1).standard_normal((M, N)).astype(np.float32))
+        gad = torch.empty((M, K), dtype=torch.float16, device=dev)
+        gbd = torch.empty((K, N), dtype=torch.float16, device=dev)
+        wsd = torch.empty((kaio.lib().kaio_gemm_f16f32_bwd_workspace_size(M, N),), dtype=torch.uint8, device=dev)
+        bms, _ = timed(lambda i: kaio.kaio_gemm_f16f32_bwd(ad, bd, gd, gad, gbd, wsd),
+                       max(10, args.steps // 2), 3, stream)
+        btf = 4.0 * M * N * K / (bms * 1e-3) / 1e12
+        log(f"[bench] gemm bwd 4096^3: {bms * 1e3:.1f} us/call, {btf:.1f} TFLOP/s")
+        secondary["gemm_f16f32_bwd"] = {
+            "workload": "grad f32[4096,4096] -> grad_a = f16(grad) . B^T, grad_b = A^T . f16(grad), f16 outputs "
+                        "(cast + two GEMM launches)",
+            "us_per_call": round(bms * 1e3, 2), "value": round(btf, 2), "unit": "TFLOP/s", "bound": "mfma",
+            "peak": PEAK_F16_TFLOPS, "frac": round(btf / PEAK_F16_TFLOPS, 4)}
+        del ad, bd, cd, gd, gad, gbd, wsd
 
     # ---- dequant backward --------------------------------------------------------------------
     if args.only in ("all", "bwd"):

@@ -5,6 +5,7 @@
  *
  *   kaio_qkv_w4a16          W4A16 group-quantized fused tri-output QKV projection
  *   kaio_gemm_f16f32        dense f16 x f16 -> f32 matmul
+ *   kaio_gemm_f16f32_bwd    its backward: f16 gradients of A and B
  *   kaio_dequant_group_bwd  straight-through per-group dequant backward
  *
  * Conventions shared by every entry point
@@ -103,6 +104,39 @@ kaio_status kaio_qkv_w4a16(const void* x,
  */
 kaio_status kaio_gemm_f16f32(const void* a, const void* b, float* c,
                              uint32_t m, uint32_t n, uint32_t k, void* stream);
+
+/*
+ * Backward of kaio_gemm_f16f32 for an f32 output gradient g [m, n]:
+ *   g16    = f16(g)                                (round to nearest even)
+ *   grad_a = f16( g16 . b^T )     f16[m, k]
+ *   grad_b = f16( a^T . g16 )     f16[k, n]
+ * each product accumulated in f32 and rounded once to f16 (nearest even).
+ * Defined by: kaio-candle 0.2.0, src/matmul_tc_async.rs --
+ * MatmulTcAsyncOp::bwd (the gradient cast to f16, dA = grad . B^T and
+ * dB = A^T . grad by the forward kernel, both results cast to f16).
+ *
+ *   a  f16[m, k]   b  f16[k, n]   grad  f32[m, n]
+ *   grad_a  f16[m, k]   grad_b  f16[k, n]
+ *   workspace  device scratch for g16: at least
+ *              kaio_gemm_f16f32_bwd_workspace_size(m, n) bytes, 16-byte
+ *              aligned, overlapping nothing else; its contents on return
+ *              are unspecified.  Calls on one workspace must not overlap.
+ *
+ * Validation order: sizes too large for one launch -> INVALID_PROBLEM;
+ * k == 0 -> OK (both gradients are empty, nothing launched); null output
+ * -> INVALID_ARGUMENT; m == 0 or n == 0 -> both gradients are the empty
+ * sum: zeros are written (a, b, grad and workspace are not read and may be
+ * null); null input or workspace, or workspace_bytes too small ->
+ * INVALID_ARGUMENT; misaligned -> INVALID_ARGUMENT; overlapping buffers ->
+ * INVALID_ARGUMENT; device -> DEVICE; launch -> LAUNCH.
+ */
+kaio_status kaio_gemm_f16f32_bwd(const void* a, const void* b, const float* grad,
+                                 void* grad_a, void* grad_b,
+                                 uint32_t m, uint32_t n, uint32_t k,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes kaio_gemm_f16f32_bwd needs for an [m, n] gradient: m * n * 2. */
+size_t kaio_gemm_f16f32_bwd_workspace_size(uint32_t m, uint32_t n);
 
 /*
  * Straight-through per-group dequant backward:

@@ -8,6 +8,7 @@ device is not gfx950 the call raises.
 
     kaio_qkv_w4a16(x, w_q, w_k, w_v, s_q, s_k, s_v) -> (q, k, v)
     kaio_gemm_f16f32(a, b) -> c
+    kaio_gemm_f16f32_bwd(a, b, grad) -> (grad_a, grad_b)
     kaio_dequant_group_bwd(dy, scale, group_size) -> dq
 """
 from __future__ import annotations
@@ -15,7 +16,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["DTYPE_CODES", "KaioError", "kaio_qkv_w4a16", "kaio_gemm_f16f32", "kaio_dequant_group_bwd",
+__all__ = ["DTYPE_CODES", "KaioError", "kaio_qkv_w4a16", "kaio_gemm_f16f32", "kaio_gemm_f16f32_bwd",
+           "kaio_dequant_group_bwd",
            "kaio_last_error", "kaio_version", "lib", "LIB_PATH", "GROUP_SIZE"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkaio.so")
@@ -48,6 +50,10 @@ def lib() -> ctypes.CDLL:
         L.kaio_qkv_w4a16.restype = ctypes.c_int
         L.kaio_gemm_f16f32.argtypes = [vp, vp, vp, u32, u32, u32, vp]
         L.kaio_gemm_f16f32.restype = ctypes.c_int
+        L.kaio_gemm_f16f32_bwd.argtypes = [vp] * 5 + [u32] * 3 + [vp, ctypes.c_size_t, vp]
+        L.kaio_gemm_f16f32_bwd.restype = ctypes.c_int
+        L.kaio_gemm_f16f32_bwd_workspace_size.argtypes = [u32, u32]
+        L.kaio_gemm_f16f32_bwd_workspace_size.restype = ctypes.c_size_t
         L.kaio_dequant_group_bwd.argtypes = [ctypes.c_int, i32, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.kaio_dequant_group_bwd.restype = ctypes.c_int
         L.kaio_last_error.argtypes = []
@@ -156,6 +162,38 @@ def kaio_gemm_f16f32(a, b, c=None, stream=None):
         raise ValueError(f"c must be [{M}, {N}]")
     _check(lib().kaio_gemm_f16f32(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, _stream(a.device, stream)))
     return c
+
+
+def kaio_gemm_f16f32_bwd(a, b, grad, grad_a=None, grad_b=None, workspace=None, stream=None):
+    """Backward of C = A . B: returns (grad_a f16[M,K], grad_b f16[K,N]) for grad f32[M,N].
+
+    grad is cast to f16 first; each gradient is accumulated in f32 and rounded to f16.
+    ``workspace`` (uint8, at least M*N*2 bytes) is allocated here when not given.
+    """
+    import torch
+    _tensor(a, "a", (torch.float16,))
+    _tensor(b, "b", (torch.float16,), a.device)
+    _tensor(grad, "grad", (torch.float32,), a.device)
+    M, K = a.shape
+    Kb, N = b.shape
+    if K != Kb or tuple(grad.shape) != (M, N):
+        raise ValueError(f"shape mismatch: a [{M}, {K}], b [{Kb}, {N}], grad {list(grad.shape)}")
+    if grad_a is None:
+        grad_a = torch.empty((M, K), dtype=torch.float16, device=a.device)
+    if grad_b is None:
+        grad_b = torch.empty((K, N), dtype=torch.float16, device=a.device)
+    _tensor(grad_a, "grad_a", (torch.float16,), a.device)
+    _tensor(grad_b, "grad_b", (torch.float16,), a.device)
+    if tuple(grad_a.shape) != (M, K) or tuple(grad_b.shape) != (K, N):
+        raise ValueError(f"grad_a must be [{M}, {K}] and grad_b [{K}, {N}]")
+    need = lib().kaio_gemm_f16f32_bwd_workspace_size(M, N)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=a.device)
+    _tensor(workspace, "workspace", (torch.uint8,), a.device, rank=1)
+    _check(lib().kaio_gemm_f16f32_bwd(a.data_ptr(), b.data_ptr(), grad.data_ptr(), grad_a.data_ptr(),
+                                      grad_b.data_ptr(), M, N, K, workspace.data_ptr(), workspace.numel(),
+                                      _stream(a.device, stream)))
+    return grad_a, grad_b
 
 
 def kaio_dequant_group_bwd(dy, scale, group_size, dq=None, stream=None):

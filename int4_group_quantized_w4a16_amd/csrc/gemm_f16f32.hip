@@ -209,40 +209,82 @@ __device__ __forceinline__ uint32_t vgpr_u32(uint32_t o) {
   return o;
 }
 
+// Operand staging modes of the direct-to-LDS path.  Each operand tile covers
+// 256 output indices (rows of the product for the A side, columns for the B
+// side) by 64 reduction indices.
+//   kTr = false: stored [index][reduction] (reduction contiguous, row stride
+//     ld): LDS tile [256][64], chunk kc of index row i at slot i*8 + (kc ^ (i & 7));
+//     an MFMA fragment is one plain 16-byte read.
+//   kTr = true: stored [reduction][index] (index contiguous, row stride ld):
+//     LDS tile [64][256], chunk c of reduction row r at slot r*32 + (c ^ 2(r & 3));
+//     a fragment is two transposing reads.
+template <bool kTr>
+struct DmaOperand {
+  // byte offset, within a stage's source window, of this lane's load i (0..7)
+  __device__ static uint32_t lane_offset(int i, uint32_t wave, uint32_t lane, uint32_t idx0, uint32_t nidx,
+                                         uint32_t ld) {
+    const uint32_t s = (i * 4 + wave) * 64 + lane;
+    if (!kTr) {
+      const uint32_t r = s >> 3, kc = (s & 7) ^ (r & 7);
+      const uint32_t rc = (idx0 + r < nidx) ? r : nidx - 1 - idx0;   // rows past the end repeat a valid one
+      return (rc * ld + kc * 8) * 2;
+    }
+    const uint32_t r = s >> 5, c = (s & 31) ^ (2 * (r & 3));
+    const uint32_t cc = (idx0 + c * 8 < nidx) ? c * 8 : nidx - 8 - idx0;   // likewise for 8-index chunks
+    return (r * ld + cc) * 2;
+  }
+  __device__ static const char* tile_base(const uint16_t* p, uint32_t idx0, uint32_t ld) {
+    return reinterpret_cast<const char*>(kTr ? p + idx0 : p + (size_t)idx0 * ld);
+  }
+  __device__ static size_t stage_stride(uint32_t ld) { return kTr ? (size_t)DBK * ld * 2 : (size_t)DBK * 2; }
+  // lane part of the fragment index for 16-wide tile t of a 128-wide wave block
+  __device__ static uint32_t lane_index(uint32_t wblock, uint32_t l16) {
+    return wblock * WT + (kTr ? 4 * (l16 & 3) : l16);
+  }
+  // The fragment of 32-k step ks for index `idx` (lane_index + 16 t).  The
+  // stage pointer is restrict-qualified: that tells the compiler the read
+  // does not touch the stage the loads in flight are writing, so it does not
+  // make the read wait for them.
+  __device__ static half8_t frag(const char* __restrict__ st, int ks, uint32_t idx, uint32_t kb, uint32_t l16) {
+    if (!kTr) {
+      const uint4* t = reinterpret_cast<const uint4*>(st);
+      return __builtin_bit_cast(half8_t, t[idx * KCH + ((ks * 4 + kb) ^ (idx & 7))]);
+    }
+    // transposing read: within each 16-lane group, lane i receives element
+    // i % 4 of the 8-byte chunks that lanes 4j + i / 4 address (j = 0..3).
+    // Lane a addresses reduction row k0 + a / 4 at indices 4(a % 4) .. +3 of
+    // its 16-wide tile, so lane i gets four consecutive reduction values of
+    // its own index; two reads (k0 and k0 + 4) make the eight of a fragment.
+    short4_t h[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const uint32_t k = ks * 32 + kb * 8 + (l16 >> 2) + 4 * hf;
+      const uint32_t off = (k * 32 + ((idx >> 3) ^ (2 * (k & 3)))) * 16 + ((idx >> 2) & 1) * 8;
+      h[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(st + off));
+    }
+    return __builtin_bit_cast(half8_t, (short __attribute__((ext_vector_type(8)))){
+        h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]});
+  }
+};
+
 struct GemmFrags {
   half8_t a[TT], b[TT];
 };
 
-// Fragments of one 32-k step from one LDS stage.  The stage pointers are
-// restrict-qualified: that tells the compiler these reads do not touch the
-// stage the global->LDS loads in flight are writing, so it does not make
-// them wait for those loads.
-__device__ __forceinline__ void load_gemm_frags(const uint4* __restrict__ as, const char* __restrict__ bs, int ks,
-                                                uint32_t arow0, uint32_t bk_lane, uint32_t bcol, uint32_t kb,
-                                                GemmFrags& f) {
-#pragma unroll
-  for (int c = 0; c < TT; ++c) {
-    const uint32_t col = bcol + c * 16;
-    short4_t h[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const uint32_t k = ks * 32 + bk_lane + 4 * hf;
-      const uint32_t off = (k * 32 + ((col >> 3) ^ (2 * (k & 3)))) * 16 + ((col >> 2) & 1) * 8;
-      h[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(bs + off));
-    }
-    f.b[c] = __builtin_bit_cast(half8_t, (short __attribute__((ext_vector_type(8)))){
-        h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]});
-  }
-#pragma unroll
-  for (int r = 0; r < TT; ++r) {
-    const uint32_t row = arow0 + r * 16;
-    f.a[r] = __builtin_bit_cast(half8_t, as[row * KCH + ((ks * 4 + kb) ^ (row & 7))]);
-  }
-}
+__device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_out(uint16_t* p, float v) { *p = __builtin_bit_cast(uint16_t, (_Float16)v); }
 
+// C[Mo, No] = sum over R of A-operand x B-operand, f32 accumulation; OutT is
+// float (f32 out) or uint16_t (f16 out, rounded to nearest even).  A is read
+// through DmaOperand<kATr> with row stride lda, B through DmaOperand<kBTr>
+// with row stride ldb.  Needs R % 64 == 0 and the strides and, for a
+// transposed operand, its index count multiples of 8.
+template <bool kATr, bool kBTr, typename OutT>
 __global__ void __launch_bounds__(THREADS, 1)
-gemm_f16f32_dma_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, float* __restrict__ C,
-                       uint32_t M, uint32_t N, uint32_t K, uint32_t mtiles, uint32_t ntiles) {
+gemm_dma_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __restrict__ B, uint32_t ldb,
+                OutT* __restrict__ C, uint32_t Mo, uint32_t No, uint32_t R, uint32_t mtiles, uint32_t ntiles) {
+  using OA = DmaOperand<kATr>;
+  using OB = DmaOperand<kBTr>;
   extern __shared__ uint4 smem[];
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
@@ -254,31 +296,25 @@ gemm_f16f32_dma_kernel(const uint16_t* __restrict__ A, const uint16_t* __restric
   tile_of<KAIO_GEMM_SM, KAIO_GEMM_SN>(blockIdx.x, gridDim.x, mtiles, ntiles, tm, tn);
   const uint32_t m0 = tm * BM, n0 = tn * BN;
 
-  // per-lane byte offsets of the 16-byte chunks this lane moves (8 of A, 8
-  // of B per stage); rows past M and chunks past N repeat valid ones
   uint32_t aoff[8], boff[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint32_t s = (i * 4 + wave) * 64 + lane;
-    const uint32_t r = s >> 3, kc = (s & 7) ^ (r & 7);
-    const uint32_t rc = (m0 + r < M) ? r : M - 1 - m0;
-    aoff[i] = (rc * K + kc * 8) * 2;
-    const uint32_t br = s >> 5, c = (s & 31) ^ (2 * (br & 3));
-    const uint32_t cc = (n0 + c * 8 < N) ? c * 8 : N - 8 - n0;
-    boff[i] = (br * N + cc) * 2;
+    aoff[i] = OA::lane_offset(i, wave, lane, m0, Mo, lda);
+    boff[i] = OB::lane_offset(i, wave, lane, n0, No, ldb);
   }
-  const char* abase = reinterpret_cast<const char*>(A + (size_t)m0 * K);
-  const char* bbase = reinterpret_cast<const char*>(B + n0);
+  const char* abase = OA::tile_base(A, m0, lda);
+  const char* bbase = OB::tile_base(B, n0, ldb);
+  const size_t astep = OA::stage_stride(lda), bstep = OB::stage_stride(ldb);
 
   // load j (0..7: A chunks, 8..15: B chunks) of this lane's share of stage kt
   auto issue_one = [&](uint32_t kt, uint32_t buf, int j) {
     uint4* st = smem + buf * DSTAGE;
     if (j < 8) {
-      const char* as = sgpr_ptr(abase + (size_t)kt * DBK * 2);
+      const char* as = sgpr_ptr(abase + kt * astep);
       __builtin_amdgcn_global_load_lds(KAIO_GEMM_GLOBAL(as + vgpr_u32(aoff[j])),
                                        KAIO_GEMM_LDS(st + (j * 4 + wave) * 64), 16, 0, 0);
     } else {
-      const char* bs = sgpr_ptr(bbase + (size_t)kt * DBK * N * 2);
+      const char* bs = sgpr_ptr(bbase + kt * bstep);
       __builtin_amdgcn_global_load_lds(KAIO_GEMM_GLOBAL(bs + vgpr_u32(boff[j - 8])),
                                        KAIO_GEMM_LDS(st + BM * KCH + ((j - 8) * 4 + wave) * 64), 16, 0, 0);
     }
@@ -294,14 +330,14 @@ gemm_f16f32_dma_kernel(const uint16_t* __restrict__ A, const uint16_t* __restric
 #pragma unroll
     for (int c = 0; c < TT; ++c) acc[r][c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // lane-invariant parts of the fragment addresses
-  const uint32_t arow0 = wm * WT + l16;                    // + 16 rt
-  const uint32_t bk_lane = kb * 8 + (l16 >> 2);            // k-row within the 32-k step (+ 4 for the 2nd read)
-  const uint32_t bcol = wn * WT + 4 * (l16 & 3);           // + 16 ct
-
+  const uint32_t ai0 = OA::lane_index(wm, l16), bi0 = OB::lane_index(wn, l16);
   auto load_frags = [&](uint32_t buf, int ks, GemmFrags& f) {
-    load_gemm_frags(smem + buf * DSTAGE, reinterpret_cast<const char*>(smem + buf * DSTAGE + BM * KCH), ks, arow0,
-                    bk_lane, bcol, kb, f);
+    const char* as = reinterpret_cast<const char*>(smem + buf * DSTAGE);
+    const char* bs = reinterpret_cast<const char*>(smem + buf * DSTAGE + BM * KCH);
+#pragma unroll
+    for (int c = 0; c < TT; ++c) f.b[c] = OB::frag(bs, ks, bi0 + c * 16, kb, l16);
+#pragma unroll
+    for (int r = 0; r < TT; ++r) f.a[r] = OA::frag(as, ks, ai0 + r * 16, kb, l16);
   };
   auto mma = [&](const GemmFrags& f) {
 #pragma unroll
@@ -327,7 +363,7 @@ gemm_f16f32_dma_kernel(const uint16_t* __restrict__ A, const uint16_t* __restric
   // stage k+1 has landed everywhere and every wave holds all of stage k in
   // registers, so stage k+2 then goes into stage k's buffer, a full stage
   // ahead of its use.
-  const uint32_t nk = K / DBK;
+  const uint32_t nk = R / DBK;
   GemmFrags f0, f1;
   issue_stage(0, 0);
   if (nk > 1) {
@@ -357,9 +393,43 @@ gemm_f16f32_dma_kernel(const uint16_t* __restrict__ A, const uint16_t* __restric
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t gr = m0 + wm * WT + r * 16 + 4 * kb + i;
-        if (gr < M && gc < N) C[(size_t)gr * N + gc] = acc[r][c][i];
+        if (gr < Mo && gc < No) store_out(C + (size_t)gr * No + gc, acc[r][c][i]);
       }
     }
+}
+
+// Any-shape fallback of the backward products: one output per thread,
+// element (i, j) = sum_r A[i*a_i + r*a_r] * B[r*b_r + j*b_j] in f32.
+template <typename OutT>
+__global__ void __launch_bounds__(256)
+gemm_strided_kernel(const uint16_t* __restrict__ A, size_t a_i, size_t a_r, const uint16_t* __restrict__ B,
+                    size_t b_r, size_t b_j, OutT* __restrict__ C, uint32_t Mo, uint32_t No, uint32_t R) {
+  const size_t total = (size_t)Mo * No;
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
+    const size_t i = e / No, j = e % No;
+    float acc = 0.f;
+    for (uint32_t r = 0; r < R; ++r)
+      acc = __builtin_fmaf(h2f(A[i * a_i + r * a_r]), h2f(B[r * b_r + j * b_j]), acc);
+    store_out(C + e, acc);
+  }
+}
+
+// f32 -> f16, round to nearest even (the cast of the output gradient)
+__global__ void __launch_bounds__(256)
+cast_f16_kernel(const float* __restrict__ src, uint16_t* __restrict__ dst, size_t n, bool vec) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  if (vec) {   // 8 values per step, 16-byte aligned, n % 8 == 0
+    for (size_t v = (size_t)blockIdx.x * 256 + threadIdx.x; v < n / 8; v += stride) {
+      const float4 lo = reinterpret_cast<const float4*>(src)[2 * v];
+      const float4 hi = reinterpret_cast<const float4*>(src)[2 * v + 1];
+      const half8_t h = {(_Float16)lo.x, (_Float16)lo.y, (_Float16)lo.z, (_Float16)lo.w,
+                         (_Float16)hi.x, (_Float16)hi.y, (_Float16)hi.z, (_Float16)hi.w};
+      reinterpret_cast<uint4*>(dst)[v] = __builtin_bit_cast(uint4, h);
+    }
+  } else {
+    for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += stride)
+      dst[e] = __builtin_bit_cast(uint16_t, (_Float16)src[e]);
+  }
 }
 
 __global__ void fill_zero_kernel(uint4* __restrict__ dst, size_t n16, uint8_t* __restrict__ tail, uint32_t ntail) {
@@ -379,15 +449,68 @@ hipError_t launch_gemm_f16f32(const uint16_t* a, const uint16_t* b, float* c,
   // DMA path: 32-bit per-lane byte offsets need 256 * k * 2 and 64 * n * 2 below 2^31
   if (k > 0 && k % DBK == 0 && n % 8 == 0 && k < (1u << 22) && n < (1u << 24)) {
     const size_t lds = (size_t)2 * DSTAGE * 16;
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_f16f32_dma_kernel),
+    auto* kern = &gemm_dma_kernel<false, true, float>;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(gemm_f16f32_dma_kernel, grid, block, lds, stream, a, b, c, m, n, k, mtiles, ntiles);
+    hipLaunchKernelGGL(kern, grid, block, lds, stream, a, k, b, n, c, m, n, k, mtiles, ntiles);
   } else if (k % 8 == 0 && n % 8 == 0)
     hipLaunchKernelGGL(gemm_f16f32_kernel<true>, grid, block, 0, stream, a, b, c, m, n, k, mtiles);
   else
     hipLaunchKernelGGL(gemm_f16f32_kernel<false>, grid, block, 0, stream, a, b, c, m, n, k, mtiles);
   return hipGetLastError();
+}
+
+namespace {
+template <bool kATr, bool kBTr>
+hipError_t launch_dma_f16out(const uint16_t* a, uint32_t lda, const uint16_t* b, uint32_t ldb, uint16_t* c,
+                             uint32_t mo, uint32_t no, uint32_t r, hipStream_t stream) {
+  const uint32_t mtiles = (mo + BM - 1) / BM, ntiles = (no + BN - 1) / BN;
+  const size_t lds = (size_t)2 * DSTAGE * 16;
+  auto* kern = &gemm_dma_kernel<kATr, kBTr, uint16_t>;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3(mtiles * ntiles), dim3(THREADS), lds, stream, a, lda, b, ldb, c, mo, no, r, mtiles,
+                     ntiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_strided_f16out(const uint16_t* a, size_t a_i, size_t a_r, const uint16_t* b, size_t b_r,
+                                 size_t b_j, uint16_t* c, uint32_t mo, uint32_t no, uint32_t r, hipStream_t stream) {
+  const size_t total = (size_t)mo * no;
+  size_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(gemm_strided_kernel<uint16_t>, dim3((uint32_t)blocks), dim3(256), 0, stream, a, a_i, a_r, b,
+                     b_r, b_j, c, mo, no, r);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemm_f16f32_bwd(const uint16_t* a, const uint16_t* b, const float* grad, uint16_t* grad_a,
+                                  uint16_t* grad_b, uint16_t* grad16, uint32_t m, uint32_t n, uint32_t k,
+                                  hipStream_t stream) {
+  // grad16 = f16(grad), [m, n]
+  const size_t mn = (size_t)m * n;
+  const bool vec = mn % 8 == 0 && (uintptr_t)grad % 16 == 0 && (uintptr_t)grad16 % 16 == 0;
+  size_t blocks = ((vec ? mn / 8 : mn) + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks == 0) blocks = 1;
+  hipLaunchKernelGGL(cast_f16_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, grad, grad16, mn, vec);
+  if (hipError_t e = hipGetLastError()) return e;
+  // grad_a[m, k] = grad16[m, n] . b[k, n]^T: both operands reduction (n) contiguous
+  hipError_t e;
+  if (n % DBK == 0 && n < (1u << 22))
+    e = launch_dma_f16out<false, false>(grad16, n, b, n, grad_a, m, k, n, stream);
+  else
+    e = launch_strided_f16out(grad16, n, 1, b, 1, n, grad_a, m, k, n, stream);
+  if (e != hipSuccess) return e;
+  // grad_b[k, n] = a[m, k]^T . grad16[m, n]: both operands index contiguous
+  if (m % DBK == 0 && k % 8 == 0 && n % 8 == 0 && k < (1u << 24) && n < (1u << 24))
+    e = launch_dma_f16out<true, true>(a, k, grad16, n, grad_b, k, n, m, stream);
+  else
+    e = launch_strided_f16out(a, 1, k, grad16, n, 1, grad_b, k, n, m, stream);
+  return e;
 }
 
 hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t stream) {

@@ -39,6 +39,10 @@ constexpr uint64_t kMaxWorkgroups = (1ull << 24) - 1;  // 1-D grid limit at 256 
 hipError_t launch_qkv_prefill(const QkvProblem& p, hipStream_t stream);
 hipError_t launch_qkv_decode(const QkvProblem& p, hipStream_t stream);
 hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t stream);
+// grad16 is caller-provided scratch for f16(grad), m * n halves.
+hipError_t launch_gemm_f16f32_bwd(const uint16_t* a, const uint16_t* b, const float* grad, uint16_t* grad_a,
+                                  uint16_t* grad_b, uint16_t* grad16, uint32_t m, uint32_t n, uint32_t k,
+                                  hipStream_t stream);
 hipError_t launch_gemm_f16f32(const uint16_t* a, const uint16_t* b, float* c,
                               uint32_t m, uint32_t n, uint32_t k, hipStream_t stream);
 hipError_t launch_dequant_group_bwd(kaio_dtype dtype, int64_t outer, int64_t axis,

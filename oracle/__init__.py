@@ -8,6 +8,8 @@ operations compute, written from the pages that define them:
                       the doc comment of ``qkv_project_int4``).
 * ``gemm``         -- the dense f16 x f16 -> f32 matmul
                       (kaio-candle 0.2.0, src/matmul_tc_async.rs, module doc).
+* ``gemm_bwd``     -- its backward: f16 gradients of A and B from an f32 output
+                      gradient (same file, ``MatmulTcAsyncOp::bwd``).
 * ``dequant_bwd``  -- the straight-through per-group dequant backward
                       (baracuda-kernels 0.0.1-alpha.68,
                       src/quantize/dequantize_per_group_backward.rs, module doc).
@@ -23,4 +25,4 @@ Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against hand-worked cases (``tests/golden/``), exact rational brute force,
 closed forms, or a library routine it does not itself call.
 """
-from . import int4, rounding, qkv, gemm, dequant_bwd, compare  # noqa: F401
+from . import int4, rounding, qkv, gemm, gemm_bwd, dequant_bwd, compare  # noqa: F401

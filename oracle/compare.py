@@ -2,6 +2,7 @@
 
 * f32 GEMM outputs:   |d| <= 1e-5 * T,                    T = sum_k |a_ik * b_kj|
 * f16 Q/K/V outputs:  |d| <= ulp16(Y*) + 1e-5 * T,        T = sum_k |x_ik * w_kj|
+  (the same bound for the f16 gradients of the GEMM backward, T = sum |products|)
 * dequant backward:   bit-exact (one rounded multiply per element).
 
 ``Y*`` is the unrounded float64 oracle value.  ``ulp16(v)`` is the spacing of
@@ -27,6 +28,11 @@ def ulp16(v: np.ndarray) -> np.ndarray:
 
 def qkv_tolerance(y_ref, t_ref):
     return ulp16(y_ref) + QKV_REL * np.asarray(t_ref, dtype=np.float64)
+
+
+def f16_tolerance(y_ref, t_ref):
+    """Any f16 output of an f32 accumulation: one f16 ulp plus the accumulation bound."""
+    return qkv_tolerance(y_ref, t_ref)
 
 
 def gemm_tolerance(t_ref):

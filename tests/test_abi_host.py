@@ -111,6 +111,45 @@ def test_gemm_without_gpu_reports_device():
     assert gemm(a=0, b=0, k=0)[0] == DEVICE   # k == 0: inputs unused, zeros still need the device
 
 
+def gbwd(a=A, b=A + STEP, g=A + 2 * STEP, ga=A + 3 * STEP, gb=A + 4 * STEP, m=64, n=64, k=64,
+         ws=A + 5 * STEP, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = kaio.lib().kaio_gemm_f16f32_bwd_workspace_size(m, n)
+    st = kaio.lib().kaio_gemm_f16f32_bwd(a, b, g, ga, gb, m, n, k, ws, ws_bytes, None)
+    return st, kaio.kaio_last_error()
+
+
+def test_gemm_bwd_validation():
+    L = kaio.lib()
+    assert L.kaio_gemm_f16f32_bwd_workspace_size(300, 72) == 300 * 72 * 2
+    assert gbwd(k=0, a=0, b=0, g=0, ga=0, gb=0, ws=0)[0] == OK        # both gradients empty
+    st, msg = gbwd(ga=0)
+    assert st == ARG and msg.startswith("kaio::gemm_f16f32_bwd:") and "grad_a is null" in msg
+    assert "grad_b is null" in gbwd(gb=0)[1]
+    for kw, text in ((dict(a=0), "input a"), (dict(b=0), "input b"), (dict(g=0), "input grad"),
+                     (dict(ws=0), "workspace is null")):
+        st, msg = gbwd(**kw)
+        assert st == ARG and text in msg, (kw, msg)
+    st, msg = gbwd(ws_bytes=64 * 64 * 2 - 1)
+    assert st == ARG and "workspace_bytes" in msg
+    assert gbwd(gb=A + 4 * STEP + 8)[0] == ARG
+    assert "not 16-byte aligned" in gbwd(ws=A + 5 * STEP + 4)[1]
+    assert "grad_a overlaps grad" in gbwd(ga=A + 2 * STEP + 64)[1]
+    assert "grad_a overlaps workspace" in gbwd(ws=A + 3 * STEP + 4096)[1]
+    assert "grad_b overlaps workspace" in gbwd(ws=A + 4 * STEP)[1]
+    assert "workspace overlaps a" in gbwd(ws=A + 16)[1]
+    assert gbwd(m=2 ** 32 - 1, n=2 ** 32 - 1)[0] == PROB
+    # m == 0 or n == 0: inputs and workspace are unused, only the written gradient is checked
+    assert gbwd(m=0, a=0, b=0, g=0, ws=0, ga=0)[0] in (OK, DEVICE)
+    assert gbwd(n=0, a=0, b=0, g=0, ws=0, gb=0)[0] in (OK, DEVICE)
+
+
+@no_gpu_only
+def test_gemm_bwd_without_gpu_reports_device():
+    assert gbwd()[0] == DEVICE
+    assert gbwd(m=0, a=0, b=0, g=0, ws=0, ga=0)[0] == DEVICE   # zeros for grad_b need the device
+
+
 def bwd(dt=0, outer=4, axis=256, g=128, dy=A, sc=A + STEP, dq=A + 2 * STEP):
     return kaio.lib().kaio_dequant_group_bwd(dt, outer, axis, g, dy, sc, dq, None, 0, None), kaio.kaio_last_error()
 

@@ -20,6 +20,7 @@ from int4_group_quantized_w4a16_amd import workloads
 from oracle import compare
 from oracle.dequant_bwd import dequant_bwd
 from oracle.gemm import gemm
+from oracle.gemm_bwd import gemm_bwd
 from oracle.qkv import qkv_project
 from tests.gpu_util import DEV, to_dev, to_host
 
@@ -169,3 +170,35 @@ def test_dequant_bwd_graph_replay_and_determinism(dt):
         dy.copy_(to_dev(new))
         dq.zero_()
     replay_and_compare(g, refill, lambda: [kaio.kaio_dequant_group_bwd(dy, sc, group)], [dq])
+
+
+def test_gemm_bwd_graph_replay_and_determinism():
+    M, N, K = 192, 256, 320            # both gradients on the direct-to-LDS path
+    a_np, b_np = workloads.gemm_inputs(M, N, K, seed=78)
+    rng = np.random.default_rng(6)
+    a, b = to_dev(a_np), to_dev(b_np)
+    grad = to_dev(rng.standard_normal((M, N)).astype(np.float32))
+    ins0 = [t.clone() for t in (a, b, grad)]
+    first = kaio.kaio_gemm_f16f32_bwd(a, b, grad)
+    torch.cuda.synchronize()
+    (da, ta), (db, tb) = gemm_bwd(a_np, b_np, to_host(grad))
+    for o, y, t in zip(first, (da, db), (ta, tb)):
+        bad, ratio = compare.excess(to_host(o), y, compare.f16_tolerance(y, t))
+        assert bad == 0, f"{bad} outside tolerance (max ratio {ratio:.3f})"
+    again = kaio.kaio_gemm_f16f32_bwd(a, b, grad)
+    torch.cuda.synchronize()
+    for x, y in zip(first, again):
+        assert np.array_equal(bits(x), bits(y))
+    assert all(torch.equal(x, y) for x, y in zip((a, b, grad), ins0))
+
+    ga = torch.empty((M, K), dtype=torch.float16, device=DEV)
+    gb = torch.empty((K, N), dtype=torch.float16, device=DEV)
+    ws = torch.empty((M * N * 2,), dtype=torch.uint8, device=DEV)
+    g = capture(lambda: kaio.kaio_gemm_f16f32_bwd(a, b, grad, ga, gb, ws))
+
+    def refill(i):
+        grad.copy_(torch.from_numpy(rng.standard_normal((M, N)).astype(np.float32)))
+        ws.fill_(0xff)
+        ga.fill_(float("nan"))
+        gb.fill_(float("nan"))
+    replay_and_compare(g, refill, lambda: list(kaio.kaio_gemm_f16f32_bwd(a, b, grad)), [ga, gb])
