@@ -24,6 +24,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <type_traits>
+
 namespace kaio {
 namespace {
 
@@ -198,6 +200,9 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 #define KAIO_GEMM_SN 8
 #endif
 constexpr int DBK = 64;
+// word 3 of a raw buffer descriptor on the gfx9 family: 32-bit data format,
+// no swizzle, no index stride
+constexpr int kBufferFlags = 0x00020000;
 constexpr int DSTAGE = BM * KCH + DBK * (BN / 8);   // uint4 per stage: A 2048 + B 2048
 
 __device__ __forceinline__ const char* sgpr_ptr(const char* p) {
@@ -271,6 +276,35 @@ struct GemmFrags {
   half8_t a[TT], b[TT];
 };
 
+// The accumulating MFMAs of the direct-to-LDS kernel are issued through asm
+// with the accumulator tied in place in the accumulation registers.  With the
+// builtin, the compiler picks the form whose result register differs from the
+// accumulator input, so every accumulator moves each step and is copied back
+// at the loop edge: 100-300 register copies per 128 MFMAs, which cost more
+// than the DMA and LDS work of the stage.
+__device__ __forceinline__ void mfma_inplace(floatx4& acc, const half8_t& a, const half8_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// The asm MFMAs are invisible to the compiler's hazard tracking, which covers
+// the other cases here: their A/B operands only ever come from LDS reads
+// (waited on through lgkmcnt, which the compiler does track for asm operands).
+// What remains are the VALU writes that zero the accumulators before the first
+// MFMA reads them, and the MFMA writes before the epilogue reads the results.
+// Each row of accumulators passes through an asm that takes it as an in/out
+// operand and waits 2 * (NOP + 1) cycles, so no access to a row can move
+// across its wait, and the wait exceeds what an 8-pass MFMA needs.
+template <int NOP>
+__device__ __forceinline__ void hazard_guard(floatx4 (&acc)[TT][TT]) {
+  static_assert(TT == 8, "one asm operand per accumulator of a row");
+#pragma unroll
+  for (int r = 0; r < TT; ++r)
+    asm volatile("s_nop %8\n\ts_nop %8"
+                 : "+a"(acc[r][0]), "+a"(acc[r][1]), "+a"(acc[r][2]), "+a"(acc[r][3]),
+                   "+a"(acc[r][4]), "+a"(acc[r][5]), "+a"(acc[r][6]), "+a"(acc[r][7])
+                 : "i"(NOP));
+}
+
 __device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(uint16_t* p, float v) { *p = __builtin_bit_cast(uint16_t, (_Float16)v); }
 
@@ -306,17 +340,25 @@ gemm_dma_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
   const char* bbase = OB::tile_base(B, n0, ldb);
   const size_t astep = OA::stage_stride(lda), bstep = OB::stage_stride(ldb);
 
-  // load j (0..7: A chunks, 8..15: B chunks) of this lane's share of stage kt
+  // load j (0..7: A chunks, 8..15: B chunks) of this lane's share of stage kt.
+  // The buffer form of the direct-to-LDS load is used, not the global one:
+  // while a global (FLAT-encoded) load is pending the compiler can no longer
+  // order the LDS counter and turns every wait for a fragment read into a full
+  // wait.  The descriptor is rebuilt per stage from the stage's 64-bit base,
+  // so the 32-bit lane offsets never overflow; its range is unlimited (every
+  // offset is in bounds by construction).
   auto issue_one = [&](uint32_t kt, uint32_t buf, int j) {
     uint4* st = smem + buf * DSTAGE;
     if (j < 8) {
-      const char* as = sgpr_ptr(abase + kt * astep);
-      __builtin_amdgcn_global_load_lds(KAIO_GEMM_GLOBAL(as + vgpr_u32(aoff[j])),
-                                       KAIO_GEMM_LDS(st + (j * 4 + wave) * 64), 16, 0, 0);
+      const __amdgpu_buffer_rsrc_t r =
+          __builtin_amdgcn_make_buffer_rsrc((void*)sgpr_ptr(abase + kt * astep), 0, -1, kBufferFlags);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, KAIO_GEMM_LDS(st + (j * 4 + wave) * 64), 16,
+                                               vgpr_u32(aoff[j]), 0, 0, 0);
     } else {
-      const char* bs = sgpr_ptr(bbase + kt * bstep);
-      __builtin_amdgcn_global_load_lds(KAIO_GEMM_GLOBAL(bs + vgpr_u32(boff[j - 8])),
-                                       KAIO_GEMM_LDS(st + BM * KCH + ((j - 8) * 4 + wave) * 64), 16, 0, 0);
+      const __amdgpu_buffer_rsrc_t r =
+          __builtin_amdgcn_make_buffer_rsrc((void*)sgpr_ptr(bbase + kt * bstep), 0, -1, kBufferFlags);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, KAIO_GEMM_LDS(st + BM * KCH + ((j - 8) * 4 + wave) * 64), 16,
+                                               vgpr_u32(boff[j - 8]), 0, 0, 0);
     }
   };
   auto issue_stage = [&](uint32_t kt, uint32_t buf) {
@@ -330,6 +372,7 @@ gemm_dma_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
 #pragma unroll
     for (int c = 0; c < TT; ++c) acc[r][c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  hazard_guard<4>(acc);
   const uint32_t ai0 = OA::lane_index(wm, l16), bi0 = OB::lane_index(wn, l16);
   auto load_frags = [&](uint32_t buf, int ks, GemmFrags& f) {
     const char* as = reinterpret_cast<const char*>(smem + buf * DSTAGE);
@@ -339,31 +382,42 @@ gemm_dma_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
 #pragma unroll
     for (int r = 0; r < TT; ++r) f.a[r] = OA::frag(as, ks, ai0 + r * 16, kb, l16);
   };
-  auto mma = [&](const GemmFrags& f) {
-#pragma unroll
-    for (int r = 0; r < TT; ++r)
-#pragma unroll
-      for (int c = 0; c < TT; ++c) acc[r][c] = mfma16x16x32(f.a[r], f.b[c], acc[r][c]);
-  };
-  // the same, with stage kt's 16 loads spread two per 8 MFMAs, so that no
-  // wave stalls behind a burst of loads the address unit cannot take yet
-  auto mma_issue = [&](const GemmFrags& f, uint32_t kt, uint32_t buf) {
+  // The MFMAs on fragments f, row by row, with the reads of the next
+  // fragments nf (32-k step nks of stage buffer nbuf) spread between the rows:
+  // all B fragments during rows 0-3, the A fragment of row r after row r.
+  // Every read then has at least a row of MFMAs (128 cycles) before its use,
+  // and no wait ever covers a read issued just before it.  With kIssue, stage
+  // kt's 16 direct loads into buffer buf go between the rows too (two per row).
+  auto mma_read = [&](const GemmFrags& f, uint32_t nbuf, int nks, GemmFrags& nf, auto kIssue, uint32_t kt,
+                      uint32_t buf) {
+    const char* as = reinterpret_cast<const char*>(smem + nbuf * DSTAGE);
+    const char* bs = reinterpret_cast<const char*>(smem + nbuf * DSTAGE + BM * KCH);
 #pragma unroll
     for (int r = 0; r < TT; ++r) {
 #pragma unroll
-      for (int c = 0; c < TT; ++c) acc[r][c] = mfma16x16x32(f.a[r], f.b[c], acc[r][c]);
-      issue_one(kt, buf, 2 * r);
-      issue_one(kt, buf, 2 * r + 1);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int c = 0; c < TT; ++c) mfma_inplace(acc[r][c], f.a[r], f.b[c]);
+      if constexpr (decltype(kIssue)::value) {
+        issue_one(kt, buf, 2 * r);
+        issue_one(kt, buf, 2 * r + 1);
+      }
+      if (r < TT / 2) {
+        nf.b[2 * r] = OB::frag(bs, nks, bi0 + 2 * r * 16, kb, l16);
+        nf.b[2 * r + 1] = OB::frag(bs, nks, bi0 + (2 * r + 1) * 16, kb, l16);
+      }
+      nf.a[r] = OA::frag(as, nks, ai0 + r * 16, kb, l16);
     }
   };
 
-  // Two 32-k steps per stage.  Fragments are loaded one step ahead of the
-  // MFMAs that use them.  Barrier k sits between the two steps of stage k:
-  // stage k+1 has landed everywhere and every wave holds all of stage k in
+  // Two 32-k steps per stage.  Barrier k sits between the two steps of stage
+  // k: stage k+1 has landed everywhere and every wave holds all of stage k in
   // registers, so stage k+2 then goes into stage k's buffer, a full stage
-  // ahead of its use.
+  // ahead of its use.  In the last iteration the reads of "the next stage"
+  // reread a buffer nobody writes any more (no branch around them), and the
+  // loads repeat the last stage into the current buffer, which nobody reads.
   const uint32_t nk = R / DBK;
+  // the epilogue's kernel arguments, loaded here rather than inside the loop,
+  // where a pending scalar load would again force full LDS waits
+  asm volatile("" ::"s"(C), "s"(Mo), "s"(No));
   GemmFrags f0, f1;
   issue_stage(0, 0);
   if (nk > 1) {
@@ -375,15 +429,13 @@ gemm_dma_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
   load_frags(0, 0, f0);
   for (uint32_t kt = 0; kt < nk; ++kt) {
     const uint32_t buf = kt & 1;
-    load_frags(buf, 1, f1);
-    mma(f0);
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (kt + 1 < nk) load_frags(buf ^ 1, 0, f0);
-    // stage kt+2, or a repeat of the last stage into this buffer, which
-    // nobody reads again (keeps the loop free of a branch around the MFMAs)
-    mma_issue(f1, kt + 2 < nk ? kt + 2 : nk - 1, buf);
+    mma_read(f0, buf, 1, f1, std::false_type{}, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) expcnt(7) lgkmcnt(0), visible to the compiler
+    __builtin_amdgcn_s_barrier();
+    mma_read(f1, buf ^ 1, 0, f0, std::true_type{}, kt + 2 < nk ? kt + 2 : nk - 1, buf);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  hazard_guard<7>(acc);
 
 #pragma unroll
   for (int r = 0; r < TT; ++r)
