@@ -99,6 +99,20 @@ __device__ __forceinline__ uint32_t lane_offset(uint32_t o) {
   return o;
 }
 
+// Direct global -> LDS load of `bytes` (4 or 16) per lane from base + off,
+// in the buffer form: while a global (FLAT-encoded) direct load is pending,
+// the compiler cannot order the LDS counter and makes every wait for an LDS
+// read a full wait, which would drain the fragment prefetch.  The descriptor
+// takes the wave-uniform base (SGPRs) with an unlimited range: every offset
+// is in bounds by construction.
+__device__ __forceinline__ void dma_to_lds(const char* base, uint32_t off, void* lds, int bytes_is_16) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, -1, 0x00020000);
+  if (bytes_is_16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, KAIO_LDS(lds), 16, off, 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, KAIO_LDS(lds), 4, off, 0, 0, 0);
+}
+
 __device__ __forceinline__ void load_a(half8_t (&a)[4], const uint4* __restrict__ xs, int r, uint32_t l16,
                                        uint32_t kb) {
   const uint32_t row = r * 16 + l16;
@@ -156,6 +170,16 @@ __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3
   // this wave's own weights and scales of the next group have landed (only
   // its XPER x loads, issued after them, may still be in flight)
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(XPENDING) : "memory");
+  // all of the next group's words and scales are read at once, so that their
+  // LDS latency passes under the MFMAs instead of in front of each unpack
+  uint32_t nw[3][4];
+  uint16_t ns16[3];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int q = 0; q < 3; ++q) nw[q][ks] = next_w[q * WAVES * 256 + ks * 64 + lane];
+#pragma unroll
+  for (int q = 0; q < 3; ++q) ns16[q] = *next_s[q];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -165,13 +189,13 @@ __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3
         pbuf[t][q] = mfma16x16x32(abuf[t == 0 ? T0 : T1][ks], bq[q][ks],
                                   ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : pbuf[t][q]);
 #pragma unroll
-    for (int q = 0; q < 3; ++q) bq[q][ks] = unpack_int4x8(next_w[q * WAVES * 256 + ks * 64 + lane]);
+    for (int q = 0; q < 3; ++q) bq[q][ks] = unpack_int4x8(nw[q][ks]);
     __builtin_amdgcn_sched_barrier(0);
   }
   fold(acc[RT - 2], pbuf[0], sf);
   fold(acc[RT - 1], pbuf[1], sf);
 #pragma unroll
-  for (int q = 0; q < 3; ++q) sf[q] = h2f(*next_s[q]);
+  for (int q = 0; q < 3; ++q) sf[q] = h2f(ns16[q]);
 }
 
 template <int WAVES, int XDIST, bool kAligned>
@@ -243,13 +267,11 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
     for (int q = 0; q < 3; ++q) {
       const char* wg = uniform(reinterpret_cast<const char*>(p.w[q] + (size_t)gc * 16 * N));
       if (kAligned) {
-        __builtin_amdgcn_global_load_lds(KAIO_GLOBAL(wg + lane_offset(woff)), KAIO_LDS(wst + q * WAVES * 256), 16, 0,
-                                         0);
+        dma_to_lds(wg, lane_offset(woff), wst + q * WAVES * 256, 1);
       } else {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          __builtin_amdgcn_global_load_lds(KAIO_GLOBAL(uniform(wg + (size_t)ks * 16 * N) + lane_offset(woff)),
-                                           KAIO_LDS(wst + q * WAVES * 256 + ks * 64), 4, 0, 0);
+          dma_to_lds(uniform(wg + (size_t)ks * 16 * N), lane_offset(woff), wst + q * WAVES * 256 + ks * 64, 0);
       }
     }
   };
@@ -260,16 +282,14 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
     const uint32_t off = (gi * N + s8c) * 2;
 #pragma unroll
     for (int q = 0; q < 3; ++q)
-      __builtin_amdgcn_global_load_lds(KAIO_GLOBAL(uniform(reinterpret_cast<const char*>(p.s[q] + (size_t)c0 * N)) +
-                                                   lane_offset(off)),
-                                       KAIO_LDS(sbuf + (q * WAVES + wave) * SCHUNK * 16), 16, 0, 0);
+      dma_to_lds(uniform(reinterpret_cast<const char*>(p.s[q] + (size_t)c0 * N)), lane_offset(off),
+                 sbuf + (q * WAVES + wave) * SCHUNK * 16, 1);
   };
   // Load i of x of group g (clamped likewise) into x slot g % (XDIST+1).
   auto issue_x_one = [&](uint32_t g, int i) {
     uint4* xst = xslot(g);
     const char* xsrc = uniform(xblk + (size_t)(g < G ? g : G - 1) * kGroup * 2);
-    __builtin_amdgcn_global_load_lds(KAIO_GLOBAL(xsrc + lane_offset(xoff[i])),
-                                     KAIO_LDS(xst + (i * WAVES + wave) * 64), 16, 0, 0);
+    dma_to_lds(xsrc, lane_offset(xoff[i]), xst + (i * WAVES + wave) * 64, 1);
   };
   auto issue_x = [&](uint32_t g) {
 #pragma unroll
