@@ -310,6 +310,23 @@ def main():
             "bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
             "algorithmic_bytes": dbytes, "tflops": round(2.0 * M * N * K * 3 / (dms * 1e-3) / 1e12, 3),
             "traffic": measured_traffic("qkv_decode", "qkv_decode.hip", dbytes)}
+        # batched decode (split-K kernel up to m = 128) on the same rotated weights
+        batched = []
+        for bm in (16, 32, 64, 128):
+            xb = t(np.random.default_rng(c["seed"] + 100 + bm).standard_normal((bm, K)).astype(np.float16))
+            ob = [torch.empty((bm, N), dtype=torch.float16, device=dev) for _ in range(3)]
+            bstep = lambda i: kaio.kaio_qkv_w4a16(xb, *sets[i % R][0], *sets[i % R][1], *ob)
+            bms = timed_graph(bstep, 4 * R, max(5, args.steps // 10), stream)
+            bbytes = bm * K * 2 + sum(a.nbytes for a in dinp.w) + sum(a.nbytes for a in dinp.s) + 3 * bm * N * 2
+            bgbs = bbytes / (bms * 1e-3) / 1e9
+            btf = 2.0 * bm * N * K * 3 / (bms * 1e-3) / 1e12
+            log(f"[bench] batched decode m={bm}: {bms * 1e3:.2f} us/call, {bgbs:.0f} GB/s, {btf:.1f} TFLOP/s")
+            batched.append({"m": bm, "us_per_call": round(bms * 1e3, 3), "gbs": round(bgbs, 1),
+                            "tflops": round(btf, 2), "hbm_frac": round(bgbs / PEAK_HBM_GBS, 4)})
+            del xb, ob
+        secondary["qkv_batched_decode"] = {
+            "workload": "x f16[m,4096] for m = 16, 32, 64, 128; weights and rotation as qkv_decode",
+            "points": batched, "bound": "hbm"}
         del sets, x, outs
 
     # ---- dense GEMM ------------------------------------------------------------------------

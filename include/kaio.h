@@ -78,8 +78,8 @@ typedef enum kaio_dtype {
  * only when k > 0) -> INVALID_ARGUMENT; misaligned pointer ->
  * INVALID_ARGUMENT; an output overlapping an input or another output ->
  * INVALID_ARGUMENT; device -> DEVICE; launch -> LAUNCH.  k == 0 writes
- * zeros.  m <= 8 runs the memory-bound decode kernel, larger m the MFMA
- * tile kernel; both obey this contract.
+ * zeros.  m <= 128 runs the memory-bound split-K kernel (decode and batched
+ * decode), larger m the MFMA tile kernel; both obey this contract.
  */
 kaio_status kaio_qkv_w4a16(const void* x,
                            const uint32_t* w_q, const uint32_t* w_k, const uint32_t* w_v,

@@ -119,7 +119,7 @@ kaio_status kaio_qkv_w4a16(const void* x, const uint32_t* w_q, const uint32_t* w
 
   uint64_t out_bytes = 0, x_bytes = 0, w_bytes = 0, s_bytes = 0;
   const bool decode = m <= kaio::kDecodeMaxM;
-  const uint64_t wgs = decode ? 3ull * ((n + kaio::kDecodeBN - 1) / kaio::kDecodeBN)
+  const uint64_t wgs = decode ? 3ull * ((n + kaio::decode_bn(m) - 1) / kaio::decode_bn(m))
                               : (uint64_t)((m + kaio::kPrefillBM - 1) / kaio::kPrefillBM) *
                                     ((n + kaio::kPrefillBN - 1) / kaio::kPrefillBN);
   if (!bytes_of(m, n, 2, &out_bytes) || !bytes_of(m, k, 2, &x_bytes) || !bytes_of(k / 8, n, 4, &w_bytes) ||

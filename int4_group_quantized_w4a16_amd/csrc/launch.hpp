@@ -27,11 +27,30 @@ constexpr int kPrefillWaves = KAIO_PREFILL_WAVES;    // waves per workgroup; eac
 constexpr uint32_t kPrefillBN = 16 * kPrefillWaves;   // columns of each output per workgroup
 constexpr uint32_t kMaxN = 1u << 26;   // keeps 32-bit per-lane byte offsets in range (16 rows x N x 4 B)
 constexpr uint32_t kMaxK = 1u << 24;
-constexpr uint32_t kDecodeMaxM = 8;    // m <= this runs the decode kernel
-#ifndef KAIO_DECODE_VEC
-#define KAIO_DECODE_VEC 4
+#ifndef KAIO_SK_MAXM
+#define KAIO_SK_MAXM 128
 #endif
-constexpr uint32_t kDecodeBN = 16 * KAIO_DECODE_VEC;   // columns of one output per decode workgroup
+constexpr uint32_t kDecodeMaxM = KAIO_SK_MAXM;   // m <= this runs the split-K kernel
+// split-K configuration for 32 < m <= 64: row tiles per wave (the other
+// rows go to other waves), words per lane load, waves per workgroup
+#ifndef KAIO_SK4_RT
+#define KAIO_SK4_RT 2
+#endif
+#ifndef KAIO_SK4_VEC
+#define KAIO_SK4_VEC 4
+#endif
+#ifndef KAIO_SK4_WAVES
+#define KAIO_SK4_WAVES 8
+#endif
+// columns of one output per split-K workgroup, by row count
+constexpr uint32_t decode_bn(uint32_t m) { return m <= 32 ? 64u : m <= 64 ? 16u * KAIO_SK4_VEC : 64u; }
+// split-K configuration for 64 < m <= 128: row tiles per wave, waves per workgroup
+#ifndef KAIO_SK8_RT
+#define KAIO_SK8_RT 2
+#endif
+#ifndef KAIO_SK8_WAVES
+#define KAIO_SK8_WAVES 8
+#endif
 constexpr uint32_t kGemmBM = 256;
 constexpr uint32_t kGemmBN = 256;
 constexpr uint64_t kMaxWorkgroups = (1ull << 24) - 1;  // 1-D grid limit at 256 threads

@@ -64,6 +64,10 @@ def test_tiny_config_all_outputs():
     (64, 4, 128), (3, 4099, 256), (200, 1000, 1024),
     # more than 32 groups: the tile kernel reloads its per-chunk scales
     (33, 72, 4480), (129, 136, 8320), (20, 12, 4224),
+    # split-K row-tile boundaries (1, 2 and 4 row tiles), full and ragged strips, then the tile kernel
+    (16, 128, 512), (17, 64, 256), (24, 200, 384), (32, 130, 384), (33, 64, 512), (48, 96, 1152),
+    (63, 40, 256), (64, 200, 256), (65, 64, 256), (96, 136, 384), (127, 72, 256), (128, 64, 640),
+    (129, 64, 256),
 ])
 def test_ragged_shapes(M, N, K):
     inp = workloads.qkv_inputs(M, N, K, seed=M * 7919 + N * 31 + K)
@@ -178,3 +182,11 @@ def test_errors_on_device():
         kaio.kaio_qkv_w4a16(x, w[:16], w, w, s, s, s)
     with pytest.raises(ValueError, match="N mismatch"):
         kaio.kaio_qkv_w4a16(x, w, w, w[:, :8].contiguous(), s, s, s)
+
+
+@pytest.mark.parametrize("M", [16, 32, 64, 128])
+def test_batched_decode_full_size(M):
+    # the split-K kernel at the decode width (N = K = 4096), every output checked
+    N = K = 4096
+    inp = workloads.qkv_inputs(M, N, K, seed=4000 + M)
+    check(qkv_on_gpu(inp.x, inp.w, inp.s), inp)
