@@ -121,7 +121,7 @@ kaio_status kaio_qkv_w4a16(const void* x, const uint32_t* w_q, const uint32_t* w
   const bool decode = m <= kaio::kDecodeMaxM;
   const uint64_t wgs = decode ? 3ull * ((n + kaio::decode_bn(m) - 1) / kaio::decode_bn(m))
                               : (uint64_t)((m + kaio::kPrefillBM - 1) / kaio::kPrefillBM) *
-                                    ((n + kaio::kPrefillBN - 1) / kaio::kPrefillBN);
+                                    ((n + kaio::prefill_bn(m, n) - 1) / kaio::prefill_bn(m, n));
   if (!bytes_of(m, n, 2, &out_bytes) || !bytes_of(m, k, 2, &x_bytes) || !bytes_of(k / 8, n, 4, &w_bytes) ||
       !bytes_of(k / 128, n, 2, &s_bytes) || wgs > kaio::kMaxWorkgroups || n >= kaio::kMaxN ||
       k >= kaio::kMaxK)

@@ -20,11 +20,15 @@ struct QkvProblem {
 
 // Tile geometry, shared with the host-side grid-size checks.
 constexpr uint32_t kPrefillBM = 128;   // rows of x per workgroup
-#ifndef KAIO_PREFILL_WAVES
-#define KAIO_PREFILL_WAVES 8
-#endif
-constexpr int kPrefillWaves = KAIO_PREFILL_WAVES;    // waves per workgroup; each owns 16 columns of every output
-constexpr uint32_t kPrefillBN = 16 * kPrefillWaves;   // columns of each output per workgroup
+constexpr uint64_t kComputeUnits = 256;  // MI355X
+// Waves per tile-kernel workgroup (each owns 16 columns of every output):
+// 8, unless the grid of 4-wave workgroups (64 columns) still fits in one pass
+// over the compute units -- then the narrower tiles double the workgroups.
+constexpr int prefill_waves(uint32_t m, uint32_t n) {
+  return (uint64_t)((m + kPrefillBM - 1) / kPrefillBM) * ((n + 63) / 64) <= kComputeUnits ? 4 : 8;
+}
+// columns of each output per tile-kernel workgroup
+constexpr uint32_t prefill_bn(uint32_t m, uint32_t n) { return 16u * prefill_waves(m, n); }
 constexpr uint32_t kMaxN = 1u << 26;   // keeps 32-bit per-lane byte offsets in range (16 rows x N x 4 B)
 constexpr uint32_t kMaxK = 1u << 24;
 #ifndef KAIO_SK_MAXM

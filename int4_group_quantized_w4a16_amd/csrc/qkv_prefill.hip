@@ -155,7 +155,10 @@ __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3
 #pragma unroll
   for (int r = 0; r < RT - 2; ++r) {
     load_a(abuf[(r + 2) % 3], xs, r + 2, l16, kb);
-    if (r < XPENDING) issue_x_part(r);   // a later group's x, one load per tile
+    // a later group's x: load i goes out during tile i mod (RT - 2), so every
+    // one of the XPENDING loads is issued before the tail's wait counts them
+#pragma unroll
+    for (int i = r; i < XPENDING; i += RT - 2) issue_x_part(i);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -407,8 +410,12 @@ hipError_t launch_variant(const QkvProblem& p, hipStream_t stream) {
 
 hipError_t launch_qkv_prefill(const QkvProblem& p, hipStream_t stream) {
   // 16-byte output rows and f16-pair scale loads need n % 8 == 0
-  if (p.n % 8 == 0) return launch_variant<kPrefillWaves, KAIO_PREFILL_XDIST, true>(p, stream);
-  return launch_variant<kPrefillWaves, KAIO_PREFILL_XDIST, false>(p, stream);
+  const bool aligned = p.n % 8 == 0;
+  if (prefill_waves(p.m, p.n) == 4)
+    return aligned ? launch_variant<4, KAIO_PREFILL_XDIST, true>(p, stream)
+                   : launch_variant<4, KAIO_PREFILL_XDIST, false>(p, stream);
+  return aligned ? launch_variant<8, KAIO_PREFILL_XDIST, true>(p, stream)
+                 : launch_variant<8, KAIO_PREFILL_XDIST, false>(p, stream);
 }
 
 }  // namespace kaio

@@ -68,6 +68,8 @@ def test_tiny_config_all_outputs():
     (16, 128, 512), (17, 64, 256), (24, 200, 384), (32, 130, 384), (33, 64, 512), (48, 96, 1152),
     (63, 40, 256), (64, 200, 256), (65, 64, 256), (96, 136, 384), (127, 72, 256), (128, 64, 640),
     (129, 64, 256),
+    # tile kernel with 8 waves (the 4-wave grid would not fit in one pass), ragged and n % 8 != 0
+    (2100, 1000, 256), (2100, 1001, 128),
 ])
 def test_ragged_shapes(M, N, K):
     inp = workloads.qkv_inputs(M, N, K, seed=M * 7919 + N * 31 + K)
