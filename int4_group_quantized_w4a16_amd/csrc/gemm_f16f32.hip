@@ -203,7 +203,11 @@ constexpr int DBK = 64;
 // word 3 of a raw buffer descriptor on the gfx9 family: 32-bit data format,
 // no swizzle, no index stride
 constexpr int kBufferFlags = 0x00020000;
-constexpr int DSTAGE = BM * KCH + DBK * (BN / 8);   // uint4 per stage: A 2048 + B 2048
+constexpr int HSLOTS = 1024;   // 16-byte slots of one operand's 32-k half-stage tile (256 x 32 f16)
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8): at most 16 loads outstanding and no LDS read; nothing outstanding
+constexpr int kWait16 = 0x4070;
+constexpr int kWait0 = 0x0070;
 
 __device__ __forceinline__ const char* sgpr_ptr(const char* p) {
   asm volatile("" : "+s"(p));
@@ -214,23 +218,26 @@ __device__ __forceinline__ uint32_t vgpr_u32(uint32_t o) {
   return o;
 }
 
-// Operand staging modes of the direct-to-LDS path.  Each operand tile covers
-// 256 output indices (rows of the product for the A side, columns for the B
-// side) by 64 reduction indices.
+// Staging of one operand on the direct-to-LDS path.  The LDS holds four
+// half-stage buffers (stage s % 2, 32-k half h), each with an A part and a B
+// part of 1024 16-byte slots.  Each operand tile half covers 256 output
+// indices (rows of the product for the A side, columns for the B side) by 32
+// reduction indices.
 //   kTr = false: stored [index][reduction] (reduction contiguous, row stride
-//     ld): LDS tile [256][64], chunk kc of index row i at slot i*8 + (kc ^ (i & 7));
-//     an MFMA fragment is one plain 16-byte read.
+//     ld): LDS [256][4 chunks], chunk kc of index row i at slot
+//     i*4 + (kc ^ ((i >> 2) & 3)) -- the 16 rows of one 16-byte fragment read
+//     fill one 256-byte pass of the banks; a fragment is one 16-byte read.
 //   kTr = true: stored [reduction][index] (index contiguous, row stride ld):
-//     LDS tile [64][256], chunk c of reduction row r at slot r*32 + (c ^ 2(r & 3));
+//     LDS [32][32 chunks], chunk c of reduction row r at slot r*32 + (c ^ 2(r & 3));
 //     a fragment is two transposing reads.
 template <bool kTr>
 struct DmaOperand {
-  // byte offset, within a stage's source window, of this lane's load i (0..7)
+  // byte offset, within a half-stage's source window, of this lane's load i (0..3)
   __device__ static uint32_t lane_offset(int i, uint32_t wave, uint32_t lane, uint32_t idx0, uint32_t nidx,
                                          uint32_t ld) {
     const uint32_t s = (i * 4 + wave) * 64 + lane;
     if (!kTr) {
-      const uint32_t r = s >> 3, kc = (s & 7) ^ (r & 7);
+      const uint32_t r = s >> 2, kc = (s & 3) ^ ((r >> 2) & 3);
       const uint32_t rc = (idx0 + r < nidx) ? r : nidx - 1 - idx0;   // rows past the end repeat a valid one
       return (rc * ld + kc * 8) * 2;
     }
@@ -241,19 +248,20 @@ struct DmaOperand {
   __device__ static const char* tile_base(const uint16_t* p, uint32_t idx0, uint32_t ld) {
     return reinterpret_cast<const char*>(kTr ? p + idx0 : p + (size_t)idx0 * ld);
   }
-  __device__ static size_t stage_stride(uint32_t ld) { return kTr ? (size_t)DBK * ld * 2 : (size_t)DBK * 2; }
+  // bytes between the sources of consecutive 32-k halves
+  __device__ static size_t half_stride(uint32_t ld) { return kTr ? (size_t)32 * ld * 2 : (size_t)32 * 2; }
   // lane part of the fragment index for 16-wide tile t of a 128-wide wave block
   __device__ static uint32_t lane_index(uint32_t wblock, uint32_t l16) {
     return wblock * WT + (kTr ? 4 * (l16 & 3) : l16);
   }
-  // The fragment of 32-k step ks for index `idx` (lane_index + 16 t).  The
-  // stage pointer is restrict-qualified: that tells the compiler the read
-  // does not touch the stage the loads in flight are writing, so it does not
+  // The fragment for index `idx` (lane_index + 16 t) from a half-stage buffer.
+  // The buffer pointer is restrict-qualified: that tells the compiler the read
+  // does not touch the buffers the loads in flight are writing, so it does not
   // make the read wait for them.
-  __device__ static half8_t frag(const char* __restrict__ st, int ks, uint32_t idx, uint32_t kb, uint32_t l16) {
+  __device__ static half8_t frag(const char* __restrict__ st, uint32_t idx, uint32_t kb, uint32_t l16) {
     if (!kTr) {
       const uint4* t = reinterpret_cast<const uint4*>(st);
-      return __builtin_bit_cast(half8_t, t[idx * KCH + ((ks * 4 + kb) ^ (idx & 7))]);
+      return __builtin_bit_cast(half8_t, t[idx * 4 + (kb ^ ((idx >> 2) & 3))]);
     }
     // transposing read: within each 16-lane group, lane i receives element
     // i % 4 of the 8-byte chunks that lanes 4j + i / 4 address (j = 0..3).
@@ -263,7 +271,7 @@ struct DmaOperand {
     short4_t h[2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const uint32_t k = ks * 32 + kb * 8 + (l16 >> 2) + 4 * hf;
+      const uint32_t k = kb * 8 + (l16 >> 2) + 4 * hf;
       const uint32_t off = (k * 32 + ((idx >> 3) ^ (2 * (k & 3)))) * 16 + ((idx >> 2) & 1) * 8;
       h[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(st + off));
     }
@@ -330,40 +338,43 @@ gemm_dma_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
   tile_of<KAIO_GEMM_SM, KAIO_GEMM_SN>(blockIdx.x, gridDim.x, mtiles, ntiles, tm, tn);
   const uint32_t m0 = tm * BM, n0 = tn * BN;
 
-  uint32_t aoff[8], boff[8];
+  uint32_t aoff[4], boff[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     aoff[i] = OA::lane_offset(i, wave, lane, m0, Mo, lda);
     boff[i] = OB::lane_offset(i, wave, lane, n0, No, ldb);
   }
   const char* abase = OA::tile_base(A, m0, lda);
   const char* bbase = OB::tile_base(B, n0, ldb);
-  const size_t astep = OA::stage_stride(lda), bstep = OB::stage_stride(ldb);
+  const size_t ahalf = OA::half_stride(lda), bhalf = OB::half_stride(ldb);
 
-  // load j (0..7: A chunks, 8..15: B chunks) of this lane's share of stage kt.
-  // The buffer form of the direct-to-LDS load is used, not the global one:
-  // while a global (FLAT-encoded) load is pending the compiler can no longer
-  // order the LDS counter and turns every wait for a fragment read into a full
-  // wait.  The descriptor is rebuilt per stage from the stage's 64-bit base,
-  // so the 32-bit lane offsets never overflow; its range is unlimited (every
-  // offset is in bounds by construction).
-  auto issue_one = [&](uint32_t kt, uint32_t buf, int j) {
-    uint4* st = smem + buf * DSTAGE;
-    if (j < 8) {
+  // half-stage buffer of stage kt, half h (A part first, B part HSLOTS later)
+  auto hbuf = [&](uint32_t kt, uint32_t h) { return smem + ((kt & 1) * 2 + h) * (2 * HSLOTS); };
+  // load j (0..3: A chunks, 4..7: B chunks) of this lane's share of half h of
+  // stage kt.  The buffer form of the direct-to-LDS load is used, not the
+  // global one: while a global (FLAT-encoded) load is pending the compiler can
+  // no longer order the LDS counter and turns every wait for a fragment read
+  // into a full wait.  The descriptor is rebuilt per half-stage from its
+  // 64-bit base, so the 32-bit lane offsets never overflow; its range is
+  // unlimited (every offset is in bounds by construction).
+  auto issue_one = [&](uint32_t kt, uint32_t h, int j) {
+    uint4* st = hbuf(kt, h);
+    const uint32_t hk = 2 * kt + h;   // 32-k half index
+    if (j < 4) {
       const __amdgpu_buffer_rsrc_t r =
-          __builtin_amdgcn_make_buffer_rsrc((void*)sgpr_ptr(abase + kt * astep), 0, -1, kBufferFlags);
+          __builtin_amdgcn_make_buffer_rsrc((void*)sgpr_ptr(abase + hk * ahalf), 0, -1, kBufferFlags);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, KAIO_GEMM_LDS(st + (j * 4 + wave) * 64), 16,
                                                vgpr_u32(aoff[j]), 0, 0, 0);
     } else {
       const __amdgpu_buffer_rsrc_t r =
-          __builtin_amdgcn_make_buffer_rsrc((void*)sgpr_ptr(bbase + kt * bstep), 0, -1, kBufferFlags);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, KAIO_GEMM_LDS(st + BM * KCH + ((j - 8) * 4 + wave) * 64), 16,
-                                               vgpr_u32(boff[j - 8]), 0, 0, 0);
+          __builtin_amdgcn_make_buffer_rsrc((void*)sgpr_ptr(bbase + hk * bhalf), 0, -1, kBufferFlags);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, KAIO_GEMM_LDS(st + HSLOTS + ((j - 4) * 4 + wave) * 64), 16,
+                                               vgpr_u32(boff[j - 4]), 0, 0, 0);
     }
   };
-  auto issue_stage = [&](uint32_t kt, uint32_t buf) {
+  auto issue_half = [&](uint32_t kt, uint32_t h) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) issue_one(kt, buf, j);
+    for (int j = 0; j < 8; ++j) issue_one(kt, h, j);
   };
 
   floatx4 acc[TT][TT];
@@ -374,65 +385,79 @@ gemm_dma_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
 
   hazard_guard<4>(acc);
   const uint32_t ai0 = OA::lane_index(wm, l16), bi0 = OB::lane_index(wn, l16);
-  auto load_frags = [&](uint32_t buf, int ks, GemmFrags& f) {
-    const char* as = reinterpret_cast<const char*>(smem + buf * DSTAGE);
-    const char* bs = reinterpret_cast<const char*>(smem + buf * DSTAGE + BM * KCH);
+  auto load_frags = [&](const uint4* hb, GemmFrags& f) {
+    const char* as = reinterpret_cast<const char*>(hb);
+    const char* bs = reinterpret_cast<const char*>(hb + HSLOTS);
 #pragma unroll
-    for (int c = 0; c < TT; ++c) f.b[c] = OB::frag(bs, ks, bi0 + c * 16, kb, l16);
+    for (int c = 0; c < TT; ++c) f.b[c] = OB::frag(bs, bi0 + c * 16, kb, l16);
 #pragma unroll
-    for (int r = 0; r < TT; ++r) f.a[r] = OA::frag(as, ks, ai0 + r * 16, kb, l16);
+    for (int r = 0; r < TT; ++r) f.a[r] = OA::frag(as, ai0 + r * 16, kb, l16);
   };
   // The MFMAs on fragments f, row by row, with the reads of the next
-  // fragments nf (32-k step nks of stage buffer nbuf) spread between the rows:
-  // all B fragments during rows 0-3, the A fragment of row r after row r.
-  // Every read then has at least a row of MFMAs (128 cycles) before its use,
-  // and no wait ever covers a read issued just before it.  With kIssue, stage
-  // kt's 16 direct loads into buffer buf go between the rows too (two per row).
-  auto mma_read = [&](const GemmFrags& f, uint32_t nbuf, int nks, GemmFrags& nf, auto kIssue, uint32_t kt,
-                      uint32_t buf) {
-    const char* as = reinterpret_cast<const char*>(smem + nbuf * DSTAGE);
-    const char* bs = reinterpret_cast<const char*>(smem + nbuf * DSTAGE + BM * KCH);
+  // fragments nf (from half-stage buffer nb) spread between the rows: all B
+  // fragments during rows 0-3, the A fragment of row r after row r.  Every
+  // read then has at least a row of MFMAs (128 cycles) before its use, and no
+  // wait ever covers a read issued just before it.  The 8 direct loads of
+  // half h of stage kt go between the rows too, one per row.
+  auto mma_read = [&](const GemmFrags& f, const uint4* nb, GemmFrags& nf, uint32_t kt, uint32_t h) {
+    const char* as = reinterpret_cast<const char*>(nb);
+    const char* bs = reinterpret_cast<const char*>(nb + HSLOTS);
 #pragma unroll
     for (int r = 0; r < TT; ++r) {
 #pragma unroll
       for (int c = 0; c < TT; ++c) mfma_inplace(acc[r][c], f.a[r], f.b[c]);
-      if constexpr (decltype(kIssue)::value) {
-        issue_one(kt, buf, 2 * r);
-        issue_one(kt, buf, 2 * r + 1);
-      }
+      issue_one(kt, h, r);
       if (r < TT / 2) {
-        nf.b[2 * r] = OB::frag(bs, nks, bi0 + 2 * r * 16, kb, l16);
-        nf.b[2 * r + 1] = OB::frag(bs, nks, bi0 + (2 * r + 1) * 16, kb, l16);
+        nf.b[2 * r] = OB::frag(bs, bi0 + 2 * r * 16, kb, l16);
+        nf.b[2 * r + 1] = OB::frag(bs, bi0 + (2 * r + 1) * 16, kb, l16);
       }
-      nf.a[r] = OA::frag(as, nks, ai0 + r * 16, kb, l16);
+      nf.a[r] = OA::frag(as, ai0 + r * 16, kb, l16);
     }
   };
 
-  // Two 32-k steps per stage.  Barrier k sits between the two steps of stage
-  // k: stage k+1 has landed everywhere and every wave holds all of stage k in
-  // registers, so stage k+2 then goes into stage k's buffer, a full stage
-  // ahead of its use.  In the last iteration the reads of "the next stage"
-  // reread a buffer nobody writes any more (no branch around them), and the
-  // loads repeat the last stage into the current buffer, which nobody reads.
+  // Per 64-k stage kt, two halves, each ending at a barrier:
+  //   first half:  MFMAs on f0 (stage kt, k 0-31), reads of f1 (stage kt,
+  //                k 32-63), loads of stage kt+2's first half into the buffer
+  //                f0 came from (every wave read it before the last barrier);
+  //   second half: MFMAs on f1, reads of f0 (stage kt+1, k 0-31), loads of
+  //                stage kt+2's second half into the buffer f1 came from.
+  // Loads are issued in a fixed order, 8 per half per lane, so "at most 16
+  // outstanding" at a barrier means everything issued more than two halves
+  // ago has landed -- exactly the half the next half reads.  Past the last
+  // stage the loads reload consumed stages into their own buffers and the
+  // reads of "the next stage" read a buffer whose contents go unused (no
+  // branches around either).
   const uint32_t nk = R / DBK;
   // the epilogue's kernel arguments, loaded here rather than inside the loop,
   // where a pending scalar load would again force full LDS waits
   asm volatile("" ::"s"(C), "s"(Mo), "s"(No));
   GemmFrags f0, f1;
-  issue_stage(0, 0);
-  if (nk > 1) {
-    issue_stage(1, 1);
-    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  }
-  load_frags(0, 0, f0);
+  const uint32_t s1 = nk > 1 ? 1 : 0;
+  issue_half(0, 0);
+  issue_half(0, 1);
+  issue_half(s1, 0);
+  issue_half(s1, 1);
+  // stage 0 in place (with a single stage, all loads; the repeat would
+  // rewrite the buffers being read)
+  if (nk > 1)
+    __builtin_amdgcn_s_waitcnt(kWait16);
+  else
+    __builtin_amdgcn_s_waitcnt(kWait0);
+  __builtin_amdgcn_s_barrier();
+  load_frags(hbuf(0, 0), f0);
+  // every wave holds its f0 before the first half's loads overwrite that buffer
+  __builtin_amdgcn_s_waitcnt(kWait16);
+  __builtin_amdgcn_s_barrier();
   for (uint32_t kt = 0; kt < nk; ++kt) {
-    const uint32_t buf = kt & 1;
-    mma_read(f0, buf, 1, f1, std::false_type{}, 0, 0);
-    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) expcnt(7) lgkmcnt(0), visible to the compiler
+    // stage kt+2 goes into stage kt's buffers; past the end, stage kt itself
+    // is reloaded there (consumed, never read again)
+    const uint32_t kn = kt + 2 < nk ? kt + 2 : kt;
+    mma_read(f0, hbuf(kt, 1), f1, kn, 0);
+    __builtin_amdgcn_s_waitcnt(kWait16);
     __builtin_amdgcn_s_barrier();
-    mma_read(f1, buf ^ 1, 0, f0, std::true_type{}, kt + 2 < nk ? kt + 2 : nk - 1, buf);
+    mma_read(f1, hbuf(kt + 1, 0), f0, kn, 1);
+    __builtin_amdgcn_s_waitcnt(kWait16);
+    __builtin_amdgcn_s_barrier();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   hazard_guard<7>(acc);
@@ -500,7 +525,7 @@ hipError_t launch_gemm_f16f32(const uint16_t* a, const uint16_t* b, float* c,
   const dim3 grid(mtiles * ntiles), block(THREADS);
   // DMA path: 32-bit per-lane byte offsets need 256 * k * 2 and 64 * n * 2 below 2^31
   if (k > 0 && k % DBK == 0 && n % 8 == 0 && k < (1u << 22) && n < (1u << 24)) {
-    const size_t lds = (size_t)2 * DSTAGE * 16;
+    const size_t lds = (size_t)8 * HSLOTS * 16;
     auto* kern = &gemm_dma_kernel<false, true, float>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -518,7 +543,7 @@ template <bool kATr, bool kBTr>
 hipError_t launch_dma_f16out(const uint16_t* a, uint32_t lda, const uint16_t* b, uint32_t ldb, uint16_t* c,
                              uint32_t mo, uint32_t no, uint32_t r, hipStream_t stream) {
   const uint32_t mtiles = (mo + BM - 1) / BM, ntiles = (no + BN - 1) / BN;
-  const size_t lds = (size_t)2 * DSTAGE * 16;
+  const size_t lds = (size_t)8 * HSLOTS * 16;
   auto* kern = &gemm_dma_kernel<kATr, kBTr, uint16_t>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
