@@ -165,6 +165,10 @@ def summarize(dirs):
                       ", ".join(f"{c}={avg[c]:.6g}" for c in keys))
 
 
+# the kernel instantiation each workload runs (the bench's own calls also launch others)
+TRAFFIC_KERNELS = {"qkv_prefill": "qkv_prefill_kernel<8,", "qkv_decode": "qkv_decode_kernel<1, 1, 4, 16,"}
+
+
 def write_traffic(key: str, src: str, fetch_dir: str, write_dir: str, command: str):
     """Record HBM bytes per launch of one kernel from two rocprofv3 --pmc runs.
 
@@ -185,7 +189,7 @@ def write_traffic(key: str, src: str, fetch_dir: str, write_dir: str, command: s
             if r["Counter_Name"] == counter:
                 vals[r["Dispatch_Id"]] += float(r["Counter_Value"])
                 names[r["Dispatch_Id"]] = r["Kernel_Name"]
-        kern = [v for dsp, v in vals.items() if key + "_kernel" in names[dsp]]
+        kern = [v for dsp, v in vals.items() if TRAFFIC_KERNELS[key] in names[dsp]]
         copy = [v for dsp, v in vals.items() if "copy" in names[dsp].lower()]
         if not kern or not copy:
             raise SystemExit(f"{counter}: no {key} dispatch or no calibration copy under {d}")
@@ -218,7 +222,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "gemm", "bwd"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "batched", "gemm", "bwd"], default="all")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
@@ -285,7 +289,7 @@ def main():
     del x, w, s, outs
 
     # ---- decode, rotated weights ---------------------------------------------------------
-    if args.only in ("all", "decode"):
+    if args.only in ("all", "decode", "batched"):
         c = workloads.QKV_DECODE
         M, N, K, R = c["M"], c["N"], c["K"], c["rotate"]
         log(f"[bench] generating {R} decode weight sets {M}x{N}x{K}")
@@ -312,7 +316,7 @@ def main():
             "traffic": measured_traffic("qkv_decode", "qkv_decode.hip", dbytes)}
         # batched decode (split-K kernel up to m = 128) on the same rotated weights
         batched = []
-        for bm in (16, 32, 64, 128):
+        for bm in ((16, 32, 64, 128) if args.only != "decode" else ()):
             xb = t(np.random.default_rng(c["seed"] + 100 + bm).standard_normal((bm, K)).astype(np.float16))
             ob = [torch.empty((bm, N), dtype=torch.float16, device=dev) for _ in range(3)]
             bstep = lambda i: kaio.kaio_qkv_w4a16(xb, *sets[i % R][0], *sets[i % R][1], *ob)
@@ -324,9 +328,10 @@ def main():
             batched.append({"m": bm, "us_per_call": round(bms * 1e3, 3), "gbs": round(bgbs, 1),
                             "tflops": round(btf, 2), "hbm_frac": round(bgbs / PEAK_HBM_GBS, 4)})
             del xb, ob
-        secondary["qkv_batched_decode"] = {
-            "workload": "x f16[m,4096] for m = 16, 32, 64, 128; weights and rotation as qkv_decode",
-            "points": batched, "bound": "hbm"}
+        if batched:
+            secondary["qkv_batched_decode"] = {
+                "workload": "x f16[m,4096] for m = 16, 32, 64, 128; weights and rotation as qkv_decode",
+                "points": batched, "bound": "hbm"}
         del sets, x, outs
 
     # ---- dense GEMM ------------------------------------------------------------------------
