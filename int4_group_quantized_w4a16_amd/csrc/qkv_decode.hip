@@ -224,6 +224,7 @@ hipError_t launch_split_k(const QkvProblem& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_qkv_decode(const QkvProblem& p, hipStream_t stream) {
+  static_assert(kDecodeMaxM <= 128, "the widest configuration covers 128 rows");
   static_assert(decode_bn(16) == 64 && decode_bn(32) == 64 && decode_bn(64) == 16 * KAIO_SK4_VEC &&
                     decode_bn(128) == 64,
                 "strip widths must match the host-side grid computation");
