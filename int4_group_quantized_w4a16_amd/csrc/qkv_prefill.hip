@@ -170,6 +170,7 @@ __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3
   }
   constexpr int T0 = (RT - 2) % 3, T1 = (RT - 1) % 3;
   fold(acc[RT - 3], pbuf[(RT - 3) & 1], sf);
+  __builtin_amdgcn_s_setprio(0);
   // this wave's own weights and scales of the next group have landed (only
   // its XPER x loads, issued after them, may still be in flight)
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(XPENDING) : "memory");
@@ -344,6 +345,12 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   // body so that no branch follows the MFMA block.)
   for (uint32_t g = 0; g < G; ++g) {
     wait_vm_barrier<(XDIST - 1) * XPER>();
+    // Waves w and w+4 share a SIMD and leave each barrier together, so both
+    // would reach their VALU-heavy tails at once and leave the MFMA pipe idle.
+    // The second of each pair issues first through the pipelined tiles (its
+    // priority drops again before its tail), so its tail overlaps the other
+    // wave's MFMAs (~3% at 2048 x 4096 x 4096).
+    if (WAVES == 8 && wave >= 4) __builtin_amdgcn_s_setprio(1);
     issue_w(g + 1);
     // the next scale chunk replaces this one once the tail of g-1 has read
     // the last scale it needed (the scale of g, before the barrier)
