@@ -1,10 +1,12 @@
-// Dense f16 x f16 -> f32 matmul, C = A . B.
+// Dense f16 x f16 -> f32 matmul, C = A . B, and its backward.
 //
 // Operation: kaio-candle 0.2.0, src/matmul_tc_async.rs (module doc;
 // MatmulTcAsyncOp::cuda_fwd: A [m,k] and B [k,n] f16, a zeroed [m,n] f32
-// output that the kernel writes).  The pages stage tiles global -> shared
-// with cp.async on sm_80+; here the main path moves them global -> LDS with
-// gfx950's direct loads, the fallback through registers.
+// output that the kernel writes; MatmulTcAsyncOp::bwd: the f32 output
+// gradient cast to f16, grad_a = grad . B^T and grad_b = A^T . grad through
+// the forward kernel, each result cast to f16).  The pages stage tiles
+// global -> shared with cp.async on sm_80+; here the main path moves them
+// global -> LDS with gfx950's direct loads, the fallback through registers.
 //
 // gfx950 design
 // -------------
@@ -12,14 +14,19 @@
 //   = 8 x 8 v_mfma_f32_16x16x32_f16 accumulators (256 f32 per lane, held in
 //   the accumulation registers), the largest tile the register file allows,
 //   which keeps LDS traffic per MFMA lowest.
-// * Main path (k % 64 == 0, n % 8 == 0): A [m,k] and B [k,n] tiles land in
-//   LDS in their natural layouts via 16-byte direct loads (two 64-k stages,
-//   one barrier per stage, the loads spread between MFMAs).  A is already in
-//   MFMA A-operand order (8 consecutive k per lane); the B operand (8
-//   consecutive k of one column) comes from the transposing LDS read.
-// * Fallback (any other shape): tiles go global -> registers -> LDS, B
-//   transposed in registers (8x8 blocks of 16-bit values) so LDS holds B^T.
-// * Epilogue: f32 stores straight from the accumulators.
+// * Main path (reduction % 64 == 0, strides % 8 == 0): both operand tiles
+//   land in LDS via 16-byte direct loads into four 32-k half-stage buffers;
+//   each half-stage of MFMAs reads the next fragments and loads the half
+//   that will be needed two half-stages later, one barrier per half-stage.
+//   Each operand is staged in its own layout: reduction-contiguous (plain
+//   16-byte fragment reads) or index-contiguous (transposing LDS reads), so
+//   one kernel template serves the forward product and both backward
+//   products without transposed copies.
+// * Fallback (any other shape): forward tiles go global -> registers -> LDS,
+//   B transposed in registers (8x8 blocks of 16-bit values) so LDS holds B^T;
+//   the backward products use a strided one-output-per-thread kernel.
+// * Epilogue: f32 (forward) or f16 (backward, round to nearest even) stores
+//   straight from the accumulators.
 
 #include "common.hpp"
 #include "launch.hpp"
