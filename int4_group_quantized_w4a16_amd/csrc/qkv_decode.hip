@@ -1,4 +1,4 @@
-// W4A16 fused tri-output QKV projection -- split-K kernel for small m (m <= 64).
+// W4A16 fused tri-output QKV projection -- split-K kernel for small m (m <= 128).
 //
 // Operation: kaio-candle 0.2.0, src/qkv_project_int4.rs (module doc and the
 // doc comment of qkv_project_int4); same contract as the tile kernel.
@@ -17,9 +17,15 @@
 //   at packed row kb of a 32-k step: each word is the B operand of VEC x RT
 //   MFMAs (one per row tile), whose column c stands for output column
 //   VEC*c + t.  A wave-wide load covers 4 packed rows x 64*VEC contiguous bytes.
+// * Every workgroup reads the same small x.  Each wave loads its groups' x
+//   rows as 256-byte row segments (4 rows per load) into a wave-private LDS
+//   slice and reads its A fragments back from there; fragment-shaped loads
+//   (16 rows, 64 bytes each, per load) cost ~1.5 us more per call at
+//   m = 8, n = k = 4096.
 // * Split-K across the waves (wave w takes groups [wG/W, (w+1)G/W)); each
 //   wave streams its groups GCHUNK at a time through two register buffers,
-//   the next chunk's loads in flight while the current chunk computes.
+//   the next chunk's loads in flight while the current chunk computes.  No
+//   load sits under a branch (see the main loop).
 // * INT4 unpack in nibble-interleaved k order (9 VALU ops per word, once per
 //   word whatever RT is); the x fragments are permuted to the same k order in
 //   registers.
@@ -28,10 +34,11 @@
 //   the tile kernel).
 // * The wave partial sums meet in LDS and are added in a fixed order, so
 //   results are deterministic; then f32 -> f16 (RNE) and row stores.
-// Configurations (rows, columns per strip, waves) are chosen per m so that the
-// register file holds two chunks plus the accumulators and the reduction
-// buffer stays at 64 KiB: m <= 16: 1 row tile, 64 columns, 16 waves;
-// m <= 32: 2, 64, 8; m <= 64: 4, 32, 8.
+// Configurations (row tiles per wave x row blocks, columns per strip, waves)
+// are chosen per m so that the register file holds two chunks plus the
+// accumulators without spilling and the reduction buffer stays at 64 KiB
+// (plus 68 KiB of x slices): m <= 16: 1 x 1, 64, 16 (8 x rows kept when
+// m <= 8); m <= 32: 2 x 1, 64, 8; m <= 64: 2 x 2, 64, 8; m <= 128: 2 x 4, 64, 8.
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -56,7 +63,9 @@ template <> struct HalfVec<1> { typedef uint16_t T; };
 // weights (VEC words) and scales (VEC halves) stay inside their rows.
 // RSPLIT > 1 splits the rows across waves as well: wave w takes row block
 // w % RSPLIT (16*RT rows) and reduction part w / RSPLIT of WAVES / RSPLIT.
-template <int RT, int RSPLIT, int VEC, int WAVES, bool kFull>
+// XR = rows of x a wave keeps per group (a multiple of 4, at most 16*RT;
+// 8 when m <= 8, which leaves registers for two groups in flight).
+template <int RT, int RSPLIT, int VEC, int WAVES, bool kFull, int XR>
 __global__ void __launch_bounds__(WAVES * 64, 1)
 qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   constexpr int THREADS = WAVES * kWave;
@@ -67,7 +76,11 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   static_assert(KSPLIT * RSPLIT == WAVES, "row split must divide the waves");
   static_assert(KSPLIT * ROWS * BN * 4 <= 65536, "reduction buffer");
   using WV = typename WordVec<VEC>::T;
+  constexpr int XROWS = XR;                     // x rows of a wave's row block kept in LDS
+  static_assert(XR % 4 == 0 && XR <= 16 * RT, "x rows per wave");
+  constexpr int XLD = kGroup / 8 + 1;           // 16-byte chunks per padded LDS row of x
   __shared__ float red[KSPLIT][ROWS][BN];
+  __shared__ uint4 xl[WAVES][XROWS * XLD];
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
@@ -86,15 +99,35 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   const uint32_t* __restrict__ w = q == 0 ? p.w[0] : (q == 1 ? p.w[1] : p.w[2]);
   const uint16_t* __restrict__ s = q == 0 ? p.s[0] : (q == 1 ? p.s[1] : p.s[2]);
   const uint32_t colv = n0 + VEC * l16;     // first of the lane's VEC columns
-  // A-operand rows past M repeat row M-1: their outputs are never stored, and
-  // MFMA rows do not mix, so no load needs a predicate.
-  // (element offsets of the lane's rows: m <= 64 and k < 2^24 keep them below 2^30)
-  uint32_t xrow[RT];
+  // x of a group reaches the MFMAs through a wave-private LDS slice: load j
+  // brings rows 4j .. 4j+3 of the wave's row block, 256 contiguous bytes each
+  // (lane l: row 4j + l/16, 16-byte chunk l % 16), and each A fragment is read
+  // back from there.  Loading the fragments straight from memory would make
+  // every load touch 16 rows 2*K bytes apart with 64 bytes each, and the
+  // whole chip reads this same x: that costs ~1.5 us per call at m = 8,
+  // n = k = 4096.  Rows are padded to 17 chunks, so a fragment read (16 rows,
+  // one chunk each) is free of bank conflicts.
+  // Rows past M repeat row M-1 (their outputs are never stored, and MFMA rows
+  // do not mix).  Every load is issued, whatever M (repeated rows read the same
+  // addresses): a load under a branch would make the compiler wait for all
+  // loads in flight, the next group's included, before the first LDS write.
+  // (element offsets: m <= 128 and k < 2^24 keep them below 2^31)
+  const uint32_t xbase = 16 * RT * rblk;
+  const uint32_t xvalid = M > xbase ? (M - xbase < (uint32_t)XROWS ? M - xbase : XROWS) : 1;  // rows kept
+  // element offset of load j's chunk in group 0 (computed at each load: few
+  // registers are free in the widest configuration)
+  auto xoff = [&](int j) {
+    const uint32_t lr = 4 * j + kb;
+    const uint32_t row = xbase + (lr < xvalid ? lr : xvalid - 1);
+    return (row < M ? row : M - 1) * K + l16 * 8;
+  };
+  uint32_t xfrag[RT];       // LDS row of the lane's A fragment in row tile r
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
-    const uint32_t row = 16 * RT * rblk + 16 * r + l16;
-    xrow[r] = (row < M ? row : M - 1) * K + kb * 8;
+    const uint32_t lr = 16 * r + l16;
+    xfrag[r] = (lr < xvalid ? lr : xvalid - 1) * XLD + kb;
   }
+  uint4* const xw = xl[wave];
   const uint32_t* wlane = w + (size_t)kb * N + colv;   // + (16g + 4ks) * N
 
   floatx4 acc[VEC][RT];
@@ -105,7 +138,7 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
 
   struct Chunk {
     uint32_t wv[GCHUNK][4][VEC];
-    uint4 xa[GCHUNK][4][RT];
+    uint4 xs[GCHUNK][XROWS / 4];     // x rows 4j .. 4j+3 of the group, 16 bytes per lane
     uint32_t sc[GCHUNK][VEC];
   };
   // Loads of GCHUNK groups starting at g0.  Groups past the wave's range are
@@ -125,10 +158,10 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
 #pragma unroll
           for (int t = 0; t < VEC; ++t) c.wv[gi][ks][t] = (colv + t < N) ? wlane[roff + t] : 0u;
         }
-#pragma unroll
-        for (int r = 0; r < RT; ++r)
-          c.xa[gi][ks][r] = *reinterpret_cast<const uint4*>(p.x + xrow[r] + (size_t)g * kGroup + ks * 32);
       }
+#pragma unroll
+      for (int j = 0; j < XROWS / 4; ++j)
+        c.xs[gi][j] = *reinterpret_cast<const uint4*>(p.x + xoff(j) + (size_t)g * kGroup);
       if (kFull) {
         using HV = typename HalfVec<VEC>::T;
         const HV sv = *reinterpret_cast<const HV*>(s + (size_t)g * N + colv);
@@ -142,16 +175,23 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
       }
     }
   };
-  auto compute_chunk = [&](uint32_t g0, const Chunk& c) {
+  auto compute_chunk = [&](uint32_t g0, const Chunk& c, bool checked) {
 #pragma unroll
     for (int gi = 0; gi < GCHUNK; ++gi) {
-      if (g0 + gi < g_end) {   // wave-uniform
+      if (!checked || g0 + gi < g_end) {   // wave-uniform
+        // LDS accesses of one wave execute in order: these writes follow the
+        // previous group's fragment reads, and the reads below follow them;
+        // the empty asm statements keep the compiler from reordering them.
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < XROWS / 4; ++j) xw[(4 * j + kb) * XLD + l16] = c.xs[gi][j];
+        asm volatile("" ::: "memory");
         floatx4 part[VEC][RT];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           half8_t a[RT];
 #pragma unroll
-          for (int r = 0; r < RT; ++r) a[r] = permute_x_like_int4x8(c.xa[gi][ks][r]);
+          for (int r = 0; r < RT; ++r) a[r] = permute_x_like_int4x8(xw[xfrag[r] + 4 * ks]);
 #pragma unroll
           for (int t = 0; t < VEC; ++t) {
             const half8_t b = unpack_int4x8_interleaved(c.wv[gi][ks][t]);
@@ -174,17 +214,26 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
 
   if (g_begin < g_end) {
     // two register buffers used ping-pong: chunk c+1 is in flight while
-    // chunk c computes.  No chunk past the wave's range is loaded: a load
-    // nobody uses would still hold up the wave's final wait.
+    // chunk c computes.  Every load is issued unconditionally (past the
+    // wave's range they repeat its last group, which the cache holds): a load
+    // under a branch leaves the compiler's wait counts conservative where the
+    // paths meet, and it would wait for chunk c+1 before computing chunk c.
     Chunk ca, cb;
-    load_chunk(g_begin, ca);
-    for (uint32_t g0 = g_begin; g0 < g_end; g0 += 2 * GCHUNK) {
-      const bool more = g0 + GCHUNK < g_end;   // wave-uniform
-      if (more) load_chunk(g0 + GCHUNK, cb);
-      compute_chunk(g0, ca);
-      if (!more) break;
-      if (g0 + 2 * GCHUNK < g_end) load_chunk(g0 + 2 * GCHUNK, ca);
-      compute_chunk(g0 + GCHUNK, cb);
+    if (g_end - g_begin == 2 * GCHUNK) {
+      // exactly two chunks (every wave at m <= 16, k = 4096): straight-line
+      load_chunk(g_begin, ca);
+      load_chunk(g_begin + GCHUNK, cb);
+      compute_chunk(g_begin, ca, false);
+      compute_chunk(g_begin + GCHUNK, cb, false);
+    } else {
+      load_chunk(g_begin, ca);
+      load_chunk(g_begin + GCHUNK, cb);
+      for (uint32_t g0 = g_begin; g0 < g_end; g0 += 2 * GCHUNK) {
+        compute_chunk(g0, ca, true);
+        load_chunk(g0 + 2 * GCHUNK, ca);
+        compute_chunk(g0 + GCHUNK, cb, true);
+        load_chunk(g0 + 3 * GCHUNK, cb);
+      }
     }
   }
 
@@ -209,15 +258,15 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   }
 }
 
-template <int RT, int RSPLIT, int VEC, int WAVES>
+template <int RT, int RSPLIT, int VEC, int WAVES, int XR = 16 * RT>
 hipError_t launch_split_k(const QkvProblem& p, hipStream_t stream) {
   constexpr uint32_t BN = 16 * VEC;
   const uint32_t nstrips = (p.n + BN - 1) / BN;
   const dim3 grid(3 * nstrips), block(WAVES * kWave);
   if (p.n % BN == 0)
-    hipLaunchKernelGGL((qkv_decode_kernel<RT, RSPLIT, VEC, WAVES, true>), grid, block, 0, stream, p, nstrips);
+    hipLaunchKernelGGL((qkv_decode_kernel<RT, RSPLIT, VEC, WAVES, true, XR>), grid, block, 0, stream, p, nstrips);
   else
-    hipLaunchKernelGGL((qkv_decode_kernel<RT, RSPLIT, VEC, WAVES, false>), grid, block, 0, stream, p, nstrips);
+    hipLaunchKernelGGL((qkv_decode_kernel<RT, RSPLIT, VEC, WAVES, false, XR>), grid, block, 0, stream, p, nstrips);
   return hipGetLastError();
 }
 
@@ -228,6 +277,7 @@ hipError_t launch_qkv_decode(const QkvProblem& p, hipStream_t stream) {
   static_assert(decode_bn(16) == 64 && decode_bn(32) == 64 && decode_bn(64) == 16 * KAIO_SK4_VEC &&
                     decode_bn(128) == 64,
                 "strip widths must match the host-side grid computation");
+  if (p.m <= 8) return launch_split_k<1, 1, 4, 16, 8>(p, stream);
   if (p.m <= 16) return launch_split_k<1, 1, 4, 16>(p, stream);
   if (p.m <= 32) return launch_split_k<2, 1, 4, 8>(p, stream);
   if (p.m <= 64) return launch_split_k<KAIO_SK4_RT, 4 / KAIO_SK4_RT, KAIO_SK4_VEC, KAIO_SK4_WAVES>(p, stream);
