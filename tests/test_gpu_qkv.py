@@ -70,6 +70,9 @@ def test_tiny_config_all_outputs():
     (129, 64, 256),
     # tile kernel with 8 waves (the 4-wave grid would not fit in one pass), ragged and n % 8 != 0
     (2100, 1000, 256), (2100, 1001, 128),
+    # split-K: waves with exactly two groups on ragged strips (the straight-line path), and
+    # waves with three or more groups, odd counts included (the loop; 8 and 16 x rows kept)
+    (6, 65, 4096), (15, 100, 4096), (5, 72, 8320), (8, 64, 6272), (12, 64, 6272), (40, 72, 4480),
 ])
 def test_ragged_shapes(M, N, K):
     inp = workloads.qkv_inputs(M, N, K, seed=M * 7919 + N * 31 + K)
