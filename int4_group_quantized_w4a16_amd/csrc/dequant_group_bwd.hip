@@ -18,7 +18,11 @@
 //
 // gfx950 design: HBM-bound streaming.  A workgroup (256 threads) covers
 // UNROLL x 256 consecutive 16-byte vectors of one row (UNROLL = 1 measured
-// fastest: many small workgroups keep the most loads in flight).  With
+// fastest: many small workgroups keep the most loads in flight).  Every
+// element is touched once, so the vector stores are non-temporal, and so are
+// the vector loads of the 4- and 8-byte types (at [16384, 8192], g = 128:
+// f32 175.7 -> 169.9 us, bf16 91.2 -> 86.4 us; non-temporal bf16 loads
+// measured slower, 89.7 us).  With
 // 16-byte alignment and g a multiple of the
 // vector width every vector lies in one group and needs one scale; other
 // shapes take an element-wise path with the same arithmetic.
@@ -36,6 +40,7 @@ constexpr int THREADS = 256;
 #define KAIO_BWD_UNROLL 1
 #endif
 constexpr int UNROLL = KAIO_BWD_UNROLL;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct F32 {
   using T = float;
@@ -91,7 +96,10 @@ dequant_bwd_vec_kernel(const typename Op::T* __restrict__ dy, const typename Op:
     for (int u = 0; u < UNROLL; ++u) {
       const uint32_t jv = (chunk * UNROLL + u) * THREADS + threadIdx.x;
       if (jv < axis_v) {
-        in[u] = src[jv];
+        if (sizeof(T) >= 4)
+          in[u] = __builtin_bit_cast(Vec, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + jv));
+        else
+          in[u] = src[jv];
         const uint32_t j = jv * V;
         s[u] = srow[kPow2 ? (j >> gshift) : (j / group)];
       }
@@ -103,7 +111,7 @@ dequant_bwd_vec_kernel(const typename Op::T* __restrict__ dy, const typename Op:
         Vec o;
 #pragma unroll
         for (int e = 0; e < V; ++e) o.v[e] = Op::mul(in[u].v[e], s[u]);
-        dst[jv] = o;
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, o), reinterpret_cast<u32x4*>(dst) + jv);
       }
     }
   }
