@@ -52,6 +52,40 @@ __device__ __forceinline__ half8_t unpack_int4x8(uint32_t w) {
   return out;
 }
 
+// INT4 -> f16 times 2^-9, exact, in k order (10 VALU ops per word against
+// the 12 of unpack_int4x8).
+//
+// Two bit operations split the sign-flipped word (q -> q + 8 in [0, 15])
+// into its low nibbles and its high nibbles, each still in place within its
+// byte.  For byte j one byte permute then builds the dword whose halves are
+// 0x00:lo_j and 0x00:hi_j -- f16 subnormals worth (q_{2j} + 8) * 2^-24 and
+// 16 (q_{2j+1} + 8) * 2^-24 -- and one packed f16 FMA with (2^15, 2^11) and
+// (-2^-6, -2^-6) returns (q_{2j} * 2^-9, q_{2j+1} * 2^-9), exactly (f16
+// subnormal inputs are kept: the kernels run with f16 denormals enabled).
+// The results are normal f16 numbers; an MFMA over them gives 2^-9 times the
+// sum over exact integers, exactly, as no product or partial sum leaves the
+// f32 normal range, so multiplying by 512 * scale in the fold reproduces
+// partial * scale bit for bit.
+constexpr float kUnpackScaledInv = 512.0f;   // 1 / the 2^-9 factor of unpack_int4x8_scaled
+__device__ __forceinline__ half8_t unpack_int4x8_scaled(uint32_t w) {
+  const half2_t mul = {(_Float16)32768.0f, (_Float16)2048.0f};
+  const half2_t add = {(_Float16)-0.015625f, (_Float16)-0.015625f};
+  const uint32_t lo = (w ^ 0x88888888u) & 0x0F0F0F0Fu;   // low nibbles of the bytes, sign-flipped
+  const uint32_t hi = (w ^ 0x88888888u) & 0xF0F0F0F0u;   // high nibbles, sign-flipped
+  half8_t out;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // selector bytes: j picks byte j of lo, 4 + j byte j of hi, 0x0C a zero byte
+    const uint32_t sel = 0x0C000C00u | (uint32_t)(j | ((4 + j) << 16));
+    const uint32_t t = __builtin_amdgcn_perm(hi, lo, sel);
+    half2_t h = __builtin_bit_cast(half2_t, t);
+    h = __builtin_elementwise_fma(h, mul, add);
+    out[2 * j] = h[0];
+    out[2 * j + 1] = h[1];
+  }
+  return out;
+}
+
 // INT4 -> f16, exact, in nibble-interleaved order.
 //
 // Same exact integers as unpack_int4x8, but the eight results come out in the

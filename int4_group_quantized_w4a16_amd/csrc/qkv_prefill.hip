@@ -23,11 +23,13 @@
 //   feeds to one v_mfma_f32_16x16x32_f16 as its B operand.  Each wave fetches
 //   the 16 packed rows x 16 columns it multiplies (one 16-byte load per lane
 //   and output when n % 8 == 0), reads its words back and unpacks them to
-//   exact f16 integers in registers -- during the last two row tiles of the
-//   previous group, so that the unpack overlaps MFMAs.
+//   exact f16 values q * 2^-9 in registers (10 VALU ops per word) -- during
+//   the last two row tiles of the previous group, so that the unpack
+//   overlaps MFMAs; the scales carry the factor 2^9 back, exactly.
 // * Scales are applied per group in f32: the four MFMAs of a group
-//   accumulate a fresh partial sum of x*q (exact small integers times f16
-//   activations), then acc += partial * scale.  Rounding q*scale to f16
+//   accumulate a fresh partial sum of x*q*2^-9 (exact small integers, scaled
+//   by a power of two, times f16 activations), then
+//   acc += partial * (512 * scale).  Rounding q*scale to f16
 //   before the MFMA would cost up to 2^-12 relative per product, too much
 //   for the f16 output; the partial/scale split keeps every product exact.
 // * Epilogue: f32 -> f16 (RNE), transposed through LDS one output at a time,
@@ -193,13 +195,13 @@ __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3
         pbuf[t][q] = mfma16x16x32(abuf[t == 0 ? T0 : T1][ks], bq[q][ks],
                                   ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : pbuf[t][q]);
 #pragma unroll
-    for (int q = 0; q < 3; ++q) bq[q][ks] = unpack_int4x8(nw[q][ks]);
+    for (int q = 0; q < 3; ++q) bq[q][ks] = unpack_int4x8_scaled(nw[q][ks]);
     __builtin_amdgcn_sched_barrier(0);
   }
   fold(acc[RT - 2], pbuf[0], sf);
   fold(acc[RT - 1], pbuf[1], sf);
 #pragma unroll
-  for (int q = 0; q < 3; ++q) sf[q] = h2f(ns16[q]);
+  for (int q = 0; q < 3; ++q) sf[q] = h2f(ns16[q]) * kUnpackScaledInv;
 }
 
 template <int WAVES, int XDIST, bool kAligned>
@@ -326,11 +328,11 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
 #pragma unroll
     for (int q = 0; q < 3; ++q)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) bq[q][ks] = unpack_int4x8(w0[q * WAVES * 256 + ks * 64 + lane]);
+      for (int ks = 0; ks < 4; ++ks) bq[q][ks] = unpack_int4x8_scaled(w0[q * WAVES * 256 + ks * 64 + lane]);
     const uint16_t* ns[3];
     scale_src(0, ns);
 #pragma unroll
-    for (int q = 0; q < 3; ++q) sf[q] = h2f(*ns[q]);
+    for (int q = 0; q < 3; ++q) sf[q] = h2f(*ns[q]) * kUnpackScaledInv;
   }
 
   // Per group g, after one barrier: weights of g+1 and x of g+XDIST are
