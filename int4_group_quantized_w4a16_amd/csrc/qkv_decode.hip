@@ -26,9 +26,11 @@
 //   wave streams its groups GCHUNK at a time through two register buffers,
 //   the next chunk's loads in flight while the current chunk computes.  No
 //   load sits under a branch (see the main loop).
-// * INT4 unpack in nibble-interleaved k order (9 VALU ops per word, once per
-//   word whatever RT is); the x fragments are permuted to the same k order in
-//   registers.
+// * INT4 unpack once per word whatever RT is: with one row tile, in
+//   nibble-interleaved k order (9 VALU ops per word) with the x fragments
+//   permuted to the same order in registers; with two or more, in k order
+//   (10 ops per word, values q * 2^-9, the factor returned through the scale)
+//   with no permutation.
 // * Per group: 4 chained MFMAs per (column set, row tile) into a fresh
 //   partial, then acc += partial * scale in f32 (every product exact, as in
 //   the tile kernel).
@@ -77,6 +79,11 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   static_assert(KSPLIT * ROWS * BN * 4 <= 65536, "reduction buffer");
   using WV = typename WordVec<VEC>::T;
   constexpr int XROWS = XR;                     // x rows of a wave's row block kept in LDS
+  // Weights in k order (q * 2^-9, 10 VALU ops per word, x fragments used as
+  // read) when every word feeds two or more row tiles; otherwise in the
+  // nibble-interleaved order (9 ops per word) with each x fragment permuted
+  // to match (4 ops), which costs less when a word feeds one row tile.
+  constexpr bool kNatural = RT >= 2;
   static_assert(XR % 4 == 0 && XR <= 16 * RT, "x rows per wave");
   constexpr int XLD = kGroup / 8 + 1;           // 16-byte chunks per padded LDS row of x
   __shared__ float red[KSPLIT][ROWS][BN];
@@ -191,10 +198,13 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
         for (int ks = 0; ks < 4; ++ks) {
           half8_t a[RT];
 #pragma unroll
-          for (int r = 0; r < RT; ++r) a[r] = permute_x_like_int4x8(xw[xfrag[r] + 4 * ks]);
+          for (int r = 0; r < RT; ++r)
+            a[r] = kNatural ? __builtin_bit_cast(half8_t, xw[xfrag[r] + 4 * ks])
+                            : permute_x_like_int4x8(xw[xfrag[r] + 4 * ks]);
 #pragma unroll
           for (int t = 0; t < VEC; ++t) {
-            const half8_t b = unpack_int4x8_interleaved(c.wv[gi][ks][t]);
+            const half8_t b = kNatural ? unpack_int4x8_scaled(c.wv[gi][ks][t])
+                                       : unpack_int4x8_interleaved(c.wv[gi][ks][t]);
 #pragma unroll
             for (int r = 0; r < RT; ++r)
               part[t][r] = mfma16x16x32(a[r], b, ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : part[t][r]);
@@ -202,7 +212,7 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
         }
 #pragma unroll
         for (int t = 0; t < VEC; ++t) {
-          const float sf = h2f((uint16_t)c.sc[gi][t]);
+          const float sf = kNatural ? h2f((uint16_t)c.sc[gi][t]) * kUnpackScaledInv : h2f((uint16_t)c.sc[gi][t]);
 #pragma unroll
           for (int r = 0; r < RT; ++r)
 #pragma unroll
