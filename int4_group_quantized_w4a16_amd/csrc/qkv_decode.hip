@@ -155,6 +155,11 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
 #pragma unroll
     for (int gi = 0; gi < GCHUNK; ++gi) {
       const uint32_t g = (g0 + gi < g_end) ? g0 + gi : g_end - 1;
+      // x first: loads complete in issue order, so the LDS copy of x (needed
+      // before any MFMA) need not wait for the weights of later k-steps
+#pragma unroll
+      for (int j = 0; j < XROWS / 4; ++j)
+        c.xs[gi][j] = *reinterpret_cast<const uint4*>(p.x + xoff(j) + (size_t)g * kGroup);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const size_t roff = ((size_t)g * 16 + ks * 4) * N;
@@ -166,9 +171,6 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
           for (int t = 0; t < VEC; ++t) c.wv[gi][ks][t] = (colv + t < N) ? wlane[roff + t] : 0u;
         }
       }
-#pragma unroll
-      for (int j = 0; j < XROWS / 4; ++j)
-        c.xs[gi][j] = *reinterpret_cast<const uint4*>(p.x + xoff(j) + (size_t)g * kGroup);
       if (kFull) {
         using HV = typename HalfVec<VEC>::T;
         const HV sv = *reinterpret_cast<const HV*>(s + (size_t)g * N + colv);
