@@ -119,6 +119,32 @@ def test_one_hot_rows_read_back_every_weight():
         assert np.array_equal(o.view(np.uint16), y.astype(np.float16).view(np.uint16))
 
 
+@pytest.mark.parametrize("M", [8, 40, 200])
+def test_every_int4_value_and_extreme_scales_exact(M):
+    # one x entry per row, a signed power of two, so that each output is a single product
+    # x * q * s with at most 15 significant bits: exact in f32 on the GPU, and the one
+    # rounding to f16 (RNE, subnormals and overflow included) must match the oracle bit for bit.
+    # Every q in [-8, 7] meets scales at the f16 extremes (largest normal, smallest normal,
+    # smallest subnormal).  M = 8, 40 and 200 run the split-K kernel with one and with two row
+    # tiles per wave and the tile kernel.
+    K, N = 256, 64
+    kk, nn = np.meshgrid(np.arange(K), np.arange(N), indexing="ij")
+    q = ((kk + 3 * nn) % 16) - 8
+    w = pack_int4(q)
+    svals = np.array([65504.0, 2.0 ** -14, 2.0 ** -24, 1.0, 0.005, 3.0, 2.0 ** -20, 0.75])
+    gg, nn2 = np.meshgrid(np.arange(K // 128), np.arange(N), indexing="ij")
+    s = svals[(gg + nn2) % svals.size].astype(np.float16)
+    x = np.zeros((M, K), dtype=np.float16)
+    for i in range(M):
+        x[i, (37 * i) % K] = (-1.0) ** i * 2.0 ** ((i % 15) - 10)
+    outs = qkv_on_gpu(x, [w, w, w], [s, s, s])
+    ys, _ = qkv_project(x, [w, w, w], [s, s, s])
+    for o, y in zip(outs, ys):
+        with np.errstate(over="ignore"):   # products beyond 65504 round to +-inf, as on the GPU
+            want = y.astype(np.float16)
+        assert np.array_equal(o.view(np.uint16), want.view(np.uint16))
+
+
 @pytest.mark.parametrize("M", [8, 64])
 def test_symmetry_swap_and_linearity(M):
     inp = workloads.qkv_inputs(M, 192, 512, 99)
