@@ -43,7 +43,8 @@ def check_qkv(outs, inp):
         assert bad == 0, f"{bad} outside tolerance (max ratio {ratio:.3f})"
 
 
-@pytest.mark.parametrize("M", [5, 200])   # decode and tile kernels
+# split-K kernel with 8 and 16 x rows kept and with two row tiles per wave, then the tile kernel
+@pytest.mark.parametrize("M", [5, 12, 40, 200])
 def test_qkv_side_stream_matches_default_stream(M):
     inp, x, w, s = qkv_case(M, 264, 512, 31 + M)
     ref = kaio.kaio_qkv_w4a16(x, *w, *s)
@@ -89,9 +90,10 @@ def capture(fn):
     return g
 
 
-@pytest.mark.parametrize("M", [8, 300])
-def test_qkv_graph_replay_uses_current_inputs(M):
-    N, K = 136, 384
+# K = 4096 at M = 8 gives every split-K wave exactly two groups (its straight-line path)
+@pytest.mark.parametrize("M,K", [(8, 384), (8, 4096), (40, 1024), (300, 384)])
+def test_qkv_graph_replay_uses_current_inputs(M, K):
+    N = 136
     inp, x, w, s = qkv_case(M, N, K, 7)
     outs = [torch.empty((M, N), dtype=torch.float16, device=DEV) for _ in range(3)]
     g = capture(lambda: kaio.kaio_qkv_w4a16(x, *w, *s, *outs))
