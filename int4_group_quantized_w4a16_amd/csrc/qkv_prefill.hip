@@ -1,4 +1,4 @@
-// W4A16 fused tri-output QKV projection -- MFMA tile kernel (m > 8).
+// W4A16 fused tri-output QKV projection -- MFMA tile kernel (m > 128).
 //
 // Operation: kaio-candle 0.2.0, src/qkv_project_int4.rs (module doc and the
 // doc comment of qkv_project_int4): one launch computes Q, K and V f16[M,N]

@@ -44,7 +44,8 @@ def test_golden_handworked_bitwise():
                 rows = [np.array([int(h, 16) for h in g], dtype=np.uint32) for g in case["per_group_words"][p]]
                 w.append(np.concatenate([np.tile(r, (16, 1)) for r in rows]))
             s.append(np.array(case["scales"][p], dtype=np.float16))
-        for pad in (0, 20):   # also through the tile kernel (m > 8)
+        # pad 20 runs the split-K kernel with two row tiles per wave, pad 140 the tile kernel (m > 128)
+        for pad in (0, 20, 140):
             xx = np.concatenate([x, np.zeros((pad, K), np.float16)]) if pad else x
             outs = qkv_on_gpu(xx, w, s)
             for p, o in zip("qkv", outs):
@@ -86,15 +87,24 @@ def test_decode_config_all_outputs():
     print(f"decode 8x4096x4096: max |d|/tol = {worst:.3f}")
 
 
-def test_prefill_config_sampled_rows():
+def test_prefill_config_all_outputs():
+    # every one of the 3 x 2048 x 4096 outputs of the prefill workload (tile kernel, 8 waves,
+    # XCD super-block tile order: 16 row tiles x 32 column tiles)
     c = workloads.QKV_PREFILL
     inp = workloads.qkv_inputs(c["M"], c["N"], c["K"], c["seed"])
     outs = qkv_on_gpu(inp.x, inp.w, inp.s)
-    rng = np.random.default_rng(2024)
-    rows = np.unique(np.concatenate([np.arange(8), np.arange(c["M"] - 8, c["M"]),
-                                     rng.integers(0, c["M"], size=48)]))
-    worst = check(outs, inp, rows=rows)
-    print(f"prefill 2048x4096x4096 ({rows.size} rows): max |d|/tol = {worst:.3f}")
+    worst = check(outs, inp)
+    print(f"prefill 2048x4096x4096 (all outputs): max |d|/tol = {worst:.3f}")
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (512, 4096, 4096),    # 4-wave tile kernel: 4 x 64 tiles of 128 x 64, walked in 4 x 8 super-blocks
+    (1024, 4096, 1024),   # 8-wave tile kernel: 8 x 32 tiles of 128 x 128, walked in 4 x 8 super-blocks
+])
+def test_tile_kernel_super_block_grids_all_outputs(M, N, K):
+    inp = workloads.qkv_inputs(M, N, K, seed=M + N + K)
+    worst = check(qkv_on_gpu(inp.x, inp.w, inp.s), inp)
+    print(f"{M}x{N}x{K} (all outputs): max |d|/tol = {worst:.3f}")
 
 
 @pytest.mark.parametrize("M", [4, 40])

@@ -43,8 +43,9 @@ def check_qkv(outs, inp):
         assert bad == 0, f"{bad} outside tolerance (max ratio {ratio:.3f})"
 
 
-# split-K kernel with 8 and 16 x rows kept and with two row tiles per wave, then the tile kernel
-@pytest.mark.parametrize("M", [5, 12, 40, 200])
+# split-K kernel with 8 and 16 x rows kept, with two row tiles per wave (one, two and four row
+# blocks: m = 24, 40, 100), then the tile kernel
+@pytest.mark.parametrize("M", [5, 12, 24, 40, 100, 200])
 def test_qkv_side_stream_matches_default_stream(M):
     inp, x, w, s = qkv_case(M, 264, 512, 31 + M)
     ref = kaio.kaio_qkv_w4a16(x, *w, *s)
@@ -91,7 +92,7 @@ def capture(fn):
 
 
 # K = 4096 at M = 8 gives every split-K wave exactly two groups (its straight-line path)
-@pytest.mark.parametrize("M,K", [(8, 384), (8, 4096), (40, 1024), (300, 384)])
+@pytest.mark.parametrize("M,K", [(8, 384), (8, 4096), (24, 512), (40, 1024), (100, 640), (300, 384)])
 def test_qkv_graph_replay_uses_current_inputs(M, K):
     N = 136
     inp, x, w, s = qkv_case(M, N, K, 7)
