@@ -6,6 +6,7 @@
  *   kaio_qkv_w4a16          W4A16 group-quantized fused tri-output QKV projection
  *   kaio_gemm_f16f32        dense f16 x f16 -> f32 matmul
  *   kaio_gemm_f16f32_bwd    its backward: f16 gradients of A and B
+ *                           (kaio_gemm_f16f32_bwd_noalloc: the same without a workspace)
  *   kaio_dequant_group_bwd  straight-through per-group dequant backward
  *
  * Conventions shared by every entry point
@@ -137,6 +138,29 @@ kaio_status kaio_gemm_f16f32_bwd(const void* a, const void* b, const float* grad
 
 /* Workspace bytes kaio_gemm_f16f32_bwd needs for an [m, n] gradient: m * n * 2. */
 size_t kaio_gemm_f16f32_bwd_workspace_size(uint32_t m, uint32_t n);
+
+/*
+ * kaio_gemm_f16f32_bwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  f16(grad) is staged in a static device
+ * buffer of KAIO_GEMM_BWD_NOALLOC_MAX_BYTES bytes that the library's code
+ * object holds on every device it is loaded on, until the process ends; this
+ * call allocates and frees nothing.  Results are bit-identical to
+ * kaio_gemm_f16f32_bwd with a caller workspace (same kernels).
+ *
+ * Every call on a device shares that device's buffer: calls that overlap in
+ * time on one device (other streams, concurrently replayed graphs) race and
+ * must be serialized by the caller.  Nothing in the buffer needs to be
+ * cleared between calls (the cast overwrites what the products read).
+ *
+ * Validation order: as kaio_gemm_f16f32_bwd, without the workspace checks,
+ * plus m * n * 2 > KAIO_GEMM_BWD_NOALLOC_MAX_BYTES -> UNSUPPORTED (right
+ * after the size check; nothing launched).
+ */
+#define KAIO_GEMM_BWD_NOALLOC_MAX_BYTES (64ull << 20)
+kaio_status kaio_gemm_f16f32_bwd_noalloc(const void* a, const void* b, const float* grad,
+                                         void* grad_a, void* grad_b,
+                                         uint32_t m, uint32_t n, uint32_t k, void* stream);
 
 /*
  * Straight-through per-group dequant backward:

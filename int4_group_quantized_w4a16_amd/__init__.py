@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         L.kaio_gemm_f16f32.restype = ctypes.c_int
         L.kaio_gemm_f16f32_bwd.argtypes = [vp] * 5 + [u32] * 3 + [vp, ctypes.c_size_t, vp]
         L.kaio_gemm_f16f32_bwd.restype = ctypes.c_int
+        L.kaio_gemm_f16f32_bwd_noalloc.argtypes = [vp] * 5 + [u32] * 3 + [vp]
+        L.kaio_gemm_f16f32_bwd_noalloc.restype = ctypes.c_int
         L.kaio_gemm_f16f32_bwd_workspace_size.argtypes = [u32, u32]
         L.kaio_gemm_f16f32_bwd_workspace_size.restype = ctypes.c_size_t
         L.kaio_dequant_group_bwd.argtypes = [ctypes.c_int, i32, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]

@@ -31,6 +31,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <mutex>
 #include <type_traits>
 
 namespace kaio {
@@ -595,6 +596,49 @@ hipError_t launch_gemm_f16f32_bwd(const uint16_t* a, const uint16_t* b, const fl
   else
     e = launch_strided_f16out(a, 1, k, grad16, n, 1, grad_b, k, n, m, stream);
   return e;
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free backward: f16(grad) staged in a static device buffer.
+//
+// `scratch` is a file-scope device array: every device that loads this code
+// object holds its own copy, at its own address, until the process ends.  In
+// host code its name is only a host-side stand-in, so the kernels are given
+// the device address hipGetSymbolAddress returns, looked up once per device
+// (with that device current) and kept.  Calls that overlap in time on one
+// device share the array and race; nothing in it has to start at zero (the
+// cast overwrites the m*n halves the two products read).
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint16_t scratch[kGemmBwdScratchBytes / 2];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+uint16_t* g_scratch_ptr[kMaxScratchDevices] = {};
+
+hipError_t scratch_of_current_device(uint16_t** out) {
+  int dev = -1;
+  if (hipError_t e = hipGetDevice(&dev)) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = static_cast<uint16_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_gemm_f16f32_bwd_noalloc(const uint16_t* a, const uint16_t* b, const float* grad,
+                                          uint16_t* grad_a, uint16_t* grad_b, uint32_t m, uint32_t n,
+                                          uint32_t k, hipStream_t stream) {
+  if ((uint64_t)m * n * 2 > kGemmBwdScratchBytes) return hipErrorInvalidValue;   // checked by the caller
+  uint16_t* g16 = nullptr;
+  if (hipError_t e = scratch_of_current_device(&g16)) return e;
+  return launch_gemm_f16f32_bwd(a, b, grad, grad_a, grad_b, g16, m, n, k, stream);
 }
 
 hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t stream) {

@@ -12,6 +12,9 @@
 
 #include "launch.hpp"
 
+static_assert(kaio::kGemmBwdScratchBytes == KAIO_GEMM_BWD_NOALLOC_MAX_BYTES,
+              "the header's limit must match the static buffer");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -99,6 +102,75 @@ kaio_status check_device(const char* op) {
 kaio_status launched(const char* op, hipError_t e) {
   if (e != hipSuccess) return fail(KAIO_ERR_LAUNCH, op, "launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+// kaio_gemm_f16f32_bwd and its allocation-free variant (noalloc: f16(grad) goes
+// to the library's static per-device buffer instead of the caller's workspace).
+kaio_status gemm_bwd(const char* op, const void* a, const void* b, const float* grad, void* grad_a,
+                     void* grad_b, uint32_t m, uint32_t n, uint32_t k, bool noalloc, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  uint64_t a_bytes = 0, b_bytes = 0, g_bytes = 0, g16_bytes = 0;
+  const uint64_t wgs_a = (uint64_t)((m + kaio::kGemmBM - 1) / kaio::kGemmBM) *
+                         ((k + kaio::kGemmBN - 1) / kaio::kGemmBN);
+  const uint64_t wgs_b = (uint64_t)((k + kaio::kGemmBM - 1) / kaio::kGemmBM) *
+                         ((n + kaio::kGemmBN - 1) / kaio::kGemmBN);
+  if (!bytes_of(m, k, 2, &a_bytes) || !bytes_of(k, n, 2, &b_bytes) || !bytes_of(m, n, 4, &g_bytes) ||
+      !bytes_of(m, n, 2, &g16_bytes) || wgs_a > kaio::kMaxWorkgroups || wgs_b > kaio::kMaxWorkgroups)
+    return fail(KAIO_ERR_INVALID_PROBLEM, op, "problem too large for one launch (m=%u, n=%u, k=%u)", m, n, k);
+  if (noalloc && g16_bytes > kaio::kGemmBwdScratchBytes)
+    return fail(KAIO_ERR_UNSUPPORTED, op,
+                "f16(grad) needs m*n*2 = %llu bytes, more than the static buffer of %llu bytes "
+                "(use kaio_gemm_f16f32_bwd with a workspace)",
+                (unsigned long long)g16_bytes, (unsigned long long)kaio::kGemmBwdScratchBytes);
+  if (k == 0) return ok();
+  if (m > 0 && !grad_a) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "output grad_a is null");
+  if (n > 0 && !grad_b) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "output grad_b is null");
+  const bool empty = m == 0 || n == 0;   // both gradients are the empty sum
+  if (!empty) {
+    if (!a) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "input a is null");
+    if (!b) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "input b is null");
+    if (!grad) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "input grad is null");
+    if (!noalloc && !workspace) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "workspace is null");
+    if (!noalloc && workspace_bytes < g16_bytes)
+      return fail(KAIO_ERR_INVALID_ARGUMENT, op, "workspace_bytes (%zu) < %llu needed", workspace_bytes,
+                  (unsigned long long)g16_bytes);
+  }
+  if (m > 0 && !aligned16(grad_a)) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "output grad_a is not 16-byte aligned");
+  if (n > 0 && !aligned16(grad_b)) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "output grad_b is not 16-byte aligned");
+  if (!empty) {
+    if (!aligned16(a)) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "input a is not 16-byte aligned");
+    if (!aligned16(b)) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "input b is not 16-byte aligned");
+    if (!aligned16(grad)) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "input grad is not 16-byte aligned");
+    if (!noalloc && !aligned16(workspace)) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "workspace is not 16-byte aligned");
+  }
+  // written: grad_a, grad_b, and (when not empty) the workspace
+  const Range ro[3] = {range(grad_a, a_bytes, "grad_a"), range(grad_b, b_bytes, "grad_b"),
+                       range(empty || noalloc ? nullptr : workspace, empty || noalloc ? 0 : g16_bytes,
+                             "workspace")};
+  const Range ri[3] = {range(empty ? nullptr : a, empty ? 0 : a_bytes, "a"),
+                       range(empty ? nullptr : b, empty ? 0 : b_bytes, "b"),
+                       range(empty ? nullptr : grad, empty ? 0 : g_bytes, "grad")};
+  const Range* other = nullptr;
+  if (const Range* o = overlap(ro, 3, ri, 3, &other))
+    return fail(KAIO_ERR_INVALID_ARGUMENT, op, "%s overlaps %s", o->name, other->name);
+  if (kaio_status st = check_device(op)) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (empty) {
+    if (m > 0)
+      if (hipError_t e = kaio::launch_fill_zero(grad_a, a_bytes, s)) return launched(op, e);
+    if (n > 0)
+      if (hipError_t e = kaio::launch_fill_zero(grad_b, b_bytes, s)) return launched(op, e);
+    return launched(op, hipSuccess);
+  }
+  if (noalloc)
+    return launched(op, kaio::launch_gemm_f16f32_bwd_noalloc(
+                            static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), grad,
+                            static_cast<uint16_t*>(grad_a), static_cast<uint16_t*>(grad_b), m, n, k, s));
+  return launched(op, kaio::launch_gemm_f16f32_bwd(
+                          static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), grad,
+                          static_cast<uint16_t*>(grad_a), static_cast<uint16_t*>(grad_b),
+                          static_cast<uint16_t*>(workspace), m, n, k, s));
 }
 
 }  // namespace
@@ -209,59 +281,13 @@ size_t kaio_gemm_f16f32_bwd_workspace_size(uint32_t m, uint32_t n) { return (siz
 kaio_status kaio_gemm_f16f32_bwd(const void* a, const void* b, const float* grad, void* grad_a, void* grad_b,
                                  uint32_t m, uint32_t n, uint32_t k, void* workspace, size_t workspace_bytes,
                                  void* stream) {
-  static const char* op = "gemm_f16f32_bwd";
-  uint64_t a_bytes = 0, b_bytes = 0, g_bytes = 0, g16_bytes = 0;
-  const uint64_t wgs_a = (uint64_t)((m + kaio::kGemmBM - 1) / kaio::kGemmBM) *
-                         ((k + kaio::kGemmBN - 1) / kaio::kGemmBN);
-  const uint64_t wgs_b = (uint64_t)((k + kaio::kGemmBM - 1) / kaio::kGemmBM) *
-                         ((n + kaio::kGemmBN - 1) / kaio::kGemmBN);
-  if (!bytes_of(m, k, 2, &a_bytes) || !bytes_of(k, n, 2, &b_bytes) || !bytes_of(m, n, 4, &g_bytes) ||
-      !bytes_of(m, n, 2, &g16_bytes) || wgs_a > kaio::kMaxWorkgroups || wgs_b > kaio::kMaxWorkgroups)
-    return fail(KAIO_ERR_INVALID_PROBLEM, op, "problem too large for one launch (m=%u, n=%u, k=%u)", m, n, k);
-  if (k == 0) return ok();
-  if (m > 0 && !grad_a) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "output grad_a is null");
-  if (n > 0 && !grad_b) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "output grad_b is null");
-  const bool empty = m == 0 || n == 0;   // both gradients are the empty sum
-  if (!empty) {
-    if (!a) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "input a is null");
-    if (!b) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "input b is null");
-    if (!grad) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "input grad is null");
-    if (!workspace) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "workspace is null");
-    if (workspace_bytes < g16_bytes)
-      return fail(KAIO_ERR_INVALID_ARGUMENT, op, "workspace_bytes (%zu) < %llu needed", workspace_bytes,
-                  (unsigned long long)g16_bytes);
-  }
-  if (m > 0 && !aligned16(grad_a)) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "output grad_a is not 16-byte aligned");
-  if (n > 0 && !aligned16(grad_b)) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "output grad_b is not 16-byte aligned");
-  if (!empty) {
-    if (!aligned16(a)) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "input a is not 16-byte aligned");
-    if (!aligned16(b)) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "input b is not 16-byte aligned");
-    if (!aligned16(grad)) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "input grad is not 16-byte aligned");
-    if (!aligned16(workspace)) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "workspace is not 16-byte aligned");
-  }
-  // written: grad_a, grad_b, and (when not empty) the workspace
-  const Range ro[3] = {range(grad_a, a_bytes, "grad_a"), range(grad_b, b_bytes, "grad_b"),
-                       range(empty ? nullptr : workspace, empty ? 0 : g16_bytes, "workspace")};
-  const Range ri[3] = {range(empty ? nullptr : a, empty ? 0 : a_bytes, "a"),
-                       range(empty ? nullptr : b, empty ? 0 : b_bytes, "b"),
-                       range(empty ? nullptr : grad, empty ? 0 : g_bytes, "grad")};
-  const Range* other = nullptr;
-  if (const Range* o = overlap(ro, 3, ri, 3, &other))
-    return fail(KAIO_ERR_INVALID_ARGUMENT, op, "%s overlaps %s", o->name, other->name);
-  if (kaio_status st = check_device(op)) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
-  if (empty) {
-    if (m > 0)
-      if (hipError_t e = kaio::launch_fill_zero(grad_a, a_bytes, s)) return launched(op, e);
-    if (n > 0)
-      if (hipError_t e = kaio::launch_fill_zero(grad_b, b_bytes, s)) return launched(op, e);
-    return launched(op, hipSuccess);
-  }
-  return launched(op, kaio::launch_gemm_f16f32_bwd(
-                          static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), grad,
-                          static_cast<uint16_t*>(grad_a), static_cast<uint16_t*>(grad_b),
-                          static_cast<uint16_t*>(workspace), m, n, k, s));
+  return gemm_bwd("gemm_f16f32_bwd", a, b, grad, grad_a, grad_b, m, n, k, false, workspace, workspace_bytes,
+                  stream);
+}
+
+kaio_status kaio_gemm_f16f32_bwd_noalloc(const void* a, const void* b, const float* grad, void* grad_a,
+                                         void* grad_b, uint32_t m, uint32_t n, uint32_t k, void* stream) {
+  return gemm_bwd("gemm_f16f32_bwd_noalloc", a, b, grad, grad_a, grad_b, m, n, k, true, nullptr, 0, stream);
 }
 
 kaio_status kaio_dequant_group_bwd(kaio_dtype dtype, int32_t outer, int32_t axis, int32_t group_size,

@@ -66,6 +66,12 @@ hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t stream);
 hipError_t launch_gemm_f16f32_bwd(const uint16_t* a, const uint16_t* b, const float* grad, uint16_t* grad_a,
                                   uint16_t* grad_b, uint16_t* grad16, uint32_t m, uint32_t n, uint32_t k,
                                   hipStream_t stream);
+// The same with f16(grad) in the library's static per-device buffer of
+// kGemmBwdScratchBytes (m * n * 2 must fit); nothing is allocated.
+constexpr uint64_t kGemmBwdScratchBytes = 64ull << 20;
+hipError_t launch_gemm_f16f32_bwd_noalloc(const uint16_t* a, const uint16_t* b, const float* grad,
+                                          uint16_t* grad_a, uint16_t* grad_b, uint32_t m, uint32_t n,
+                                          uint32_t k, hipStream_t stream);
 hipError_t launch_gemm_f16f32(const uint16_t* a, const uint16_t* b, float* c,
                               uint32_t m, uint32_t n, uint32_t k, hipStream_t stream);
 hipError_t launch_dequant_group_bwd(kaio_dtype dtype, int64_t outer, int64_t axis,

@@ -150,6 +150,29 @@ def test_gemm_bwd_without_gpu_reports_device():
     assert gbwd(m=0, a=0, b=0, g=0, ws=0, ga=0)[0] == DEVICE   # zeros for grad_b need the device
 
 
+def gbwd_noalloc(a=A, b=A + STEP, g=A + 2 * STEP, ga=A + 3 * STEP, gb=A + 4 * STEP, m=64, n=64, k=64):
+    st = kaio.lib().kaio_gemm_f16f32_bwd_noalloc(a, b, g, ga, gb, m, n, k, None)
+    return st, kaio.kaio_last_error()
+
+
+def test_gemm_bwd_noalloc_validation():
+    # limit of the static f16(grad) buffer: 64 MiB = 2^25 halves
+    st, msg = gbwd_noalloc(m=8193, n=4096)
+    assert st == UNSUP and msg.startswith("kaio::gemm_f16f32_bwd_noalloc:") and "static buffer" in msg
+    assert gbwd_noalloc(m=2 ** 32 - 1, n=2 ** 32 - 1)[0] == PROB          # size check first
+    assert gbwd_noalloc(k=0, a=0, b=0, g=0, ga=0, gb=0)[0] == OK
+    assert "grad_a is null" in gbwd_noalloc(ga=0)[1]
+    assert "input grad is null" in gbwd_noalloc(g=0)[1]
+    assert "not 16-byte aligned" in gbwd_noalloc(gb=A + 4 * STEP + 8)[1]
+    assert "grad_a overlaps grad" in gbwd_noalloc(ga=A + 2 * STEP + 64)[1]
+
+
+@no_gpu_only
+def test_gemm_bwd_noalloc_without_gpu_reports_device():
+    assert gbwd_noalloc()[0] == DEVICE
+    assert gbwd_noalloc(m=8192, n=4096)[0] == DEVICE   # exactly the buffer size is accepted
+
+
 def bwd(dt=0, outer=4, axis=256, g=128, dy=A, sc=A + STEP, dq=A + 2 * STEP):
     return kaio.lib().kaio_dequant_group_bwd(dt, outer, axis, g, dy, sc, dq, None, 0, None), kaio.kaio_last_error()
 
