@@ -18,6 +18,11 @@ baracuda-kernels ``dequantize_per_group_backward``):
 
 * QKV:  x f16[M,K] ~ N(0,1); 3 x u32[K/8,N] uniform words; 3 x f16[K/128,N]
   ~ U[0.005, 0.02].  Draw order: x, w_q, w_k, w_v, s_q, s_k, s_v.
+* W8A16 QKV (the INT8 sibling): x f16[M,K] ~ N(0,1); 3 x u32[K/4,N] uniform
+  words (four independent INT8 values uniform in [-128, 127] each, by the same
+  argument as for INT4); 3 x f16[K/128,N] ~ U[0.0003125, 0.00125] -- the INT4
+  scale range divided by 16, so that the dequantized weights span the same
+  range as the INT4 workload's.  Draw order: x, w_q, w_k, w_v, s_q, s_k, s_v.
 * GEMM: A f16[M,K], B f16[K,N] ~ N(0,1).  Draw order: A, B.
 * Dequant backward: dy[outer,axis] ~ N(0,1), scale[outer,axis/g] ~ U[0.001, 0.1],
   drawn in f64, cast to the storage dtype.  Draw order: dy, scale.
@@ -36,6 +41,11 @@ GEMM_4096 = dict(M=4096, N=4096, K=4096, seed=1002, check_seed=1012)
 QKV_DECODE = dict(M=8, N=4096, K=4096, seed=1003, rotate=21)
 QKV_PREFILL = dict(M=2048, N=4096, K=4096, seed=1004)
 DEQUANT_BWD = dict(outer=16384, axis=8192, group=128, seed=1005)
+# W8A16 sibling at the INT4 workloads' shapes
+QKV8_TINY = dict(M=16, N=512, K=512, seed=1101)
+QKV8_DECODE = dict(M=8, N=4096, K=4096, seed=1103, rotate=11)
+QKV8_PREFILL = dict(M=2048, N=4096, K=4096, seed=1104)
+QKV8_SCALE_LO, QKV8_SCALE_HI = 0.005 / 16, 0.02 / 16
 
 
 @dataclass
@@ -60,6 +70,29 @@ def qkv_inputs(M: int, N: int, K: int, seed: int,
     g = K // GROUP
     s = tuple(rng.uniform(scale_lo, scale_hi, size=(g, N)).astype(np.float16) for _ in range(3))
     return QKVInputs(x=x, w=w, s=s)
+
+
+def qkv8_inputs(M: int, N: int, K: int, seed: int,
+                scale_lo: float = QKV8_SCALE_LO, scale_hi: float = QKV8_SCALE_HI) -> QKVInputs:
+    """W8A16 inputs: packed weights u32[K/4, N] (four INT8 values per word)."""
+    if K % 4:
+        raise ValueError("K must be a multiple of 4 to form packed rows")
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    w = tuple(rng.integers(0, 2 ** 32, size=(K // 4, N), dtype=np.uint32) for _ in range(3))
+    g = K // GROUP
+    s = tuple(rng.uniform(scale_lo, scale_hi, size=(g, N)).astype(np.float16) for _ in range(3))
+    return QKVInputs(x=x, w=w, s=s)
+
+
+def qkv8_weight_set(N: int, K: int, seed: int,
+                    scale_lo: float = QKV8_SCALE_LO, scale_hi: float = QKV8_SCALE_HI):
+    """A fresh W8A16 (w_q, w_k, w_v, s_q, s_k, s_v) set, used to rotate decode weights."""
+    rng = np.random.default_rng(seed)
+    w = tuple(rng.integers(0, 2 ** 32, size=(K // 4, N), dtype=np.uint32) for _ in range(3))
+    s = tuple(rng.uniform(scale_lo, scale_hi, size=(K // GROUP, N)).astype(np.float16)
+              for _ in range(3))
+    return w, s
 
 
 def qkv_weight_set(N: int, K: int, seed: int,
