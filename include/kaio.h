@@ -1,9 +1,10 @@
 /*
  * kaio.h -- C ABI of the MI355X (gfx950) W4A16 fused-QKV library.
  *
- * Three operations, each one asynchronous launch on the caller's HIP stream:
+ * Each operation is one asynchronous launch on the caller's HIP stream:
  *
  *   kaio_qkv_w4a16          W4A16 group-quantized fused tri-output QKV projection
+ *   kaio_qkv_w8a16          its W8A16 sibling (INT8 weights, same contract)
  *   kaio_gemm_f16f32        dense f16 x f16 -> f32 matmul
  *   kaio_gemm_f16f32_bwd    its backward: f16 gradients of A and B
  *                           (kaio_gemm_f16f32_bwd_noalloc: the same without a workspace)
@@ -83,6 +84,34 @@ typedef enum kaio_dtype {
  * decode), larger m the MFMA tile kernel; both obey this contract.
  */
 kaio_status kaio_qkv_w4a16(const void* x,
+                           const uint32_t* w_q, const uint32_t* w_k, const uint32_t* w_v,
+                           const void* s_q, const void* s_k, const void* s_v,
+                           void* q, void* k_out, void* v,
+                           uint32_t m, uint32_t n, uint32_t k, uint32_t group_size,
+                           void* stream);
+
+/*
+ * W8A16 fused tri-output QKV projection: the INT8 sibling of kaio_qkv_w4a16.
+ * Named by: kaio-candle 0.2.0, src/qkv_project_int4.rs -- module doc (the
+ * INT4 op follows the same direct-call pattern as qkv_project_int8, whose
+ * weight layout the pages do not print).  This library's reading of it is the
+ * 8-bit analogue of the INT4 packing:
+ *
+ *   For p in {q, k, v}:
+ *     Y_p[m, n] = sum_k x[m, k] * int8(W_p, k, n) * S_p[k / 128, n]
+ *
+ *   x        f16[m, k]       activations, shared by the three projections
+ *   w_q/k/v  u32[k/4, n]     packed INT8 weights: word (r, n) at offset r*n_cols + n;
+ *                            byte i (bits 8i..8i+7, low first) holds k = 4r + i as a
+ *                            signed two's-complement value in [-128, 127], no zero point
+ *   s_q/k/v  f16[k/128, n]   one scale per 128 consecutive k of each column
+ *   q, k_out, v  f16[m, n]   outputs, f32 accumulation rounded once to f16 (RNE)
+ *   group_size  must be 128
+ *
+ * Validation order, limits, dispatch (m <= 128 split-K kernel, else the tile
+ * kernel) and error behaviour: exactly as kaio_qkv_w4a16.
+ */
+kaio_status kaio_qkv_w8a16(const void* x,
                            const uint32_t* w_q, const uint32_t* w_k, const uint32_t* w_v,
                            const void* s_q, const void* s_k, const void* s_v,
                            void* q, void* k_out, void* v,

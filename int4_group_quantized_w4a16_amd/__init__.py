@@ -1,4 +1,4 @@
-"""MI355X (gfx950) W4A16 fused-QKV library: thin Python binding over libkaio.so.
+"""MI355X (gfx950) W4A16 fused-QKV library (and its W8A16 sibling): thin Python binding over libkaio.so.
 
 Every function here only marshals arguments (shape/dtype/device checks,
 output allocation through PyTorch, the current HIP stream) and calls the
@@ -7,6 +7,7 @@ kernels; there is no CPU fallback -- if ``libkaio.so`` is missing or the
 device is not gfx950 the call raises.
 
     kaio_qkv_w4a16(x, w_q, w_k, w_v, s_q, s_k, s_v) -> (q, k, v)
+    kaio_qkv_w8a16(x, w_q, w_k, w_v, s_q, s_k, s_v) -> (q, k, v)
     kaio_gemm_f16f32(a, b) -> c
     kaio_gemm_f16f32_bwd(a, b, grad) -> (grad_a, grad_b)
     kaio_dequant_group_bwd(dy, scale, group_size) -> dq
@@ -16,7 +17,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["DTYPE_CODES", "KaioError", "kaio_qkv_w4a16", "kaio_gemm_f16f32", "kaio_gemm_f16f32_bwd",
+__all__ = ["DTYPE_CODES", "KaioError", "kaio_qkv_w4a16", "kaio_qkv_w8a16", "kaio_gemm_f16f32", "kaio_gemm_f16f32_bwd",
            "kaio_dequant_group_bwd",
            "kaio_last_error", "kaio_version", "lib", "LIB_PATH", "GROUP_SIZE"]
 
@@ -48,6 +49,8 @@ def lib() -> ctypes.CDLL:
         vp, u32, i32 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int32
         L.kaio_qkv_w4a16.argtypes = [vp] * 10 + [u32] * 4 + [vp]
         L.kaio_qkv_w4a16.restype = ctypes.c_int
+        L.kaio_qkv_w8a16.argtypes = [vp] * 10 + [u32] * 4 + [vp]
+        L.kaio_qkv_w8a16.restype = ctypes.c_int
         L.kaio_gemm_f16f32.argtypes = [vp, vp, vp, u32, u32, u32, vp]
         L.kaio_gemm_f16f32.restype = ctypes.c_int
         L.kaio_gemm_f16f32_bwd.argtypes = [vp] * 5 + [u32] * 3 + [vp, ctypes.c_size_t, vp]
@@ -108,23 +111,20 @@ def _u32_dtypes():
     return (torch.int32, torch.uint32) if hasattr(torch, "uint32") else (torch.int32,)
 
 
-def kaio_qkv_w4a16(x, w_q, w_k, w_v, s_q, s_k, s_v, q=None, k=None, v=None, stream=None):
-    """Fused W4A16 QKV projection; returns (q, k, v), each f16[M, N].
-
-    x f16[M,K]; w_* packed INT4 as int32/uint32 [K/8, N]; s_* f16[K/128, N].
-    """
+def _qkv(fn, bits, x, w_q, w_k, w_v, s_q, s_k, s_v, q, k, v, stream):
     import torch
     f16 = (torch.float16,)
     _tensor(x, "x", f16)
     dev = x.device
     M, K = x.shape
+    per_word = 32 // bits
     ws = [_tensor(t, n, _u32_dtypes(), dev) for t, n in ((w_q, "w_q_packed"), (w_k, "w_k_packed"), (w_v, "w_v_packed"))]
     ss = [_tensor(t, n, f16, dev) for t, n in ((s_q, "scales_q"), (s_k, "scales_k"), (s_v, "scales_v"))]
     if K % GROUP_SIZE:
         raise ValueError(f"K ({K}) must be a multiple of group_size ({GROUP_SIZE})")
     for t, n in zip(ws, ("w_q_packed", "w_k_packed", "w_v_packed")):
-        if t.shape[0] != K // 8:
-            raise ValueError(f"{n} has {t.shape[0]} rows, expected K/8 = {K // 8} (K={K})")
+        if t.shape[0] != K // per_word:
+            raise ValueError(f"{n} has {t.shape[0]} rows, expected K/{per_word} = {K // per_word} (K={K})")
     for t, n in zip(ss, ("scales_q", "scales_k", "scales_v")):
         if t.shape[0] != K // GROUP_SIZE:
             raise ValueError(f"{n} has {t.shape[0]} rows, expected K/{GROUP_SIZE} = {K // GROUP_SIZE} (K={K})")
@@ -143,9 +143,26 @@ def kaio_qkv_w4a16(x, w_q, w_k, w_v, s_q, s_k, s_v, q=None, k=None, v=None, stre
     for dim in (M, N, K):
         if dim >= 2 ** 32:
             raise ValueError("dimension exceeds u32")
-    _check(lib().kaio_qkv_w4a16(x.data_ptr(), *[t.data_ptr() for t in ws], *[t.data_ptr() for t in ss],
-                                *[t.data_ptr() for t in outs], M, N, K, GROUP_SIZE, _stream(dev, stream)))
+    _check(fn(x.data_ptr(), *[t.data_ptr() for t in ws], *[t.data_ptr() for t in ss],
+              *[t.data_ptr() for t in outs], M, N, K, GROUP_SIZE, _stream(dev, stream)))
     return tuple(outs)
+
+
+def kaio_qkv_w4a16(x, w_q, w_k, w_v, s_q, s_k, s_v, q=None, k=None, v=None, stream=None):
+    """Fused W4A16 QKV projection; returns (q, k, v), each f16[M, N].
+
+    x f16[M,K]; w_* packed INT4 as int32/uint32 [K/8, N]; s_* f16[K/128, N].
+    """
+    return _qkv(lib().kaio_qkv_w4a16, 4, x, w_q, w_k, w_v, s_q, s_k, s_v, q, k, v, stream)
+
+
+def kaio_qkv_w8a16(x, w_q, w_k, w_v, s_q, s_k, s_v, q=None, k=None, v=None, stream=None):
+    """Fused W8A16 QKV projection; returns (q, k, v), each f16[M, N].
+
+    x f16[M,K]; w_* packed INT8 as int32/uint32 [K/4, N] (byte i of row r holds k = 4r+i);
+    s_* f16[K/128, N].
+    """
+    return _qkv(lib().kaio_qkv_w8a16, 8, x, w_q, w_k, w_v, s_q, s_k, s_v, q, k, v, stream)
 
 
 def kaio_gemm_f16f32(a, b, c=None, stream=None):

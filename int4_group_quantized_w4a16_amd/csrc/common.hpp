@@ -86,6 +86,41 @@ __device__ __forceinline__ half8_t unpack_int4x8_scaled(uint32_t w) {
   return out;
 }
 
+// INT8 -> f16 times 2^-9, exact, in k order (the W8A16 sibling; 5 VALU ops
+// per word of four values, the same cost per value as unpack_int4x8_scaled).
+//
+// Byte i of a word holds the signed value at k = 4r + i.  Flipping each
+// byte's top bit turns q into q + 128 in [0, 255]; one byte permute per pair
+// builds the dword [b_i, 0x00, b_{i+1}, 0x00], whose halves are the f16
+// subnormals (q_i + 128) * 2^-24 and (q_{i+1} + 128) * 2^-24, and one packed
+// f16 FMA with 2^15 and -2^-2 returns (q_i * 2^-9, q_{i+1} * 2^-9), exactly
+// (8 significant bits, normal for q != 0).  As with INT4, an MFMA over these
+// values is 2^-9 times the integer partial sum, exactly, and the fold's
+// 512 * scale restores it bit for bit.
+__device__ __forceinline__ half4_t unpack_int8x4_scaled(uint32_t w) {
+  const half2_t mul = {(_Float16)32768.0f, (_Float16)32768.0f};
+  const half2_t add = {(_Float16)-0.25f, (_Float16)-0.25f};
+  const uint32_t u = w ^ 0x80808080u;
+  // selector bytes: 0..3 pick bytes of the second operand (u), 0x0C a zero byte
+  const half2_t lo = __builtin_elementwise_fma(
+      __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, u, 0x0C010C00u)), mul, add);
+  const half2_t hi = __builtin_elementwise_fma(
+      __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, u, 0x0C030C02u)), mul, add);
+  return half4_t{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// One MFMA B operand (eight consecutive k of one column, times 2^-9) from
+// the packed words that hold them: one INT4 word, or two INT8 words (k order).
+template <int BITS>
+__device__ __forceinline__ half8_t unpack_b_scaled(const uint32_t* w) {
+  if constexpr (BITS == 4) {
+    return unpack_int4x8_scaled(w[0]);
+  } else {
+    const half4_t a = unpack_int8x4_scaled(w[0]), b = unpack_int8x4_scaled(w[1]);
+    return half8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+}
+
 // INT4 -> f16, exact, in nibble-interleaved order.
 //
 // Same exact integers as unpack_int4x8, but the eight results come out in the

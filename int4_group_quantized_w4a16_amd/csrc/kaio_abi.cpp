@@ -173,15 +173,12 @@ kaio_status gemm_bwd(const char* op, const void* a, const void* b, const float* 
                           static_cast<uint16_t*>(workspace), m, n, k, s));
 }
 
-}  // namespace
-
-extern "C" {
-
-kaio_status kaio_qkv_w4a16(const void* x, const uint32_t* w_q, const uint32_t* w_k, const uint32_t* w_v,
-                           const void* s_q, const void* s_k, const void* s_v, void* q, void* k_out,
-                           void* v, uint32_t m, uint32_t n, uint32_t k, uint32_t group_size,
-                           void* stream) {
-  static const char* op = "qkv_w4a16";
+// kaio_qkv_w4a16 (bits 4: u32[k/8, n] weights) and kaio_qkv_w8a16 (bits 8:
+// u32[k/4, n] weights): the same validation, the same kernels templated on
+// the weight width.
+kaio_status qkv(const char* op, uint32_t bits, const void* x, const uint32_t* w_q, const uint32_t* w_k,
+                const uint32_t* w_v, const void* s_q, const void* s_k, const void* s_v, void* q, void* k_out,
+                void* v, uint32_t m, uint32_t n, uint32_t k, uint32_t group_size, void* stream) {
   if (group_size != 128)
     return fail(KAIO_ERR_UNSUPPORTED, op, "group_size (%u) must be 128 (locked by the kernel contract)",
                 group_size);
@@ -194,7 +191,7 @@ kaio_status kaio_qkv_w4a16(const void* x, const uint32_t* w_q, const uint32_t* w
   const uint64_t wgs = decode ? 3ull * ((n + kaio::decode_bn(m) - 1) / kaio::decode_bn(m))
                               : (uint64_t)((m + kaio::kPrefillBM - 1) / kaio::kPrefillBM) *
                                     ((n + kaio::prefill_bn(m, n) - 1) / kaio::prefill_bn(m, n));
-  if (!bytes_of(m, n, 2, &out_bytes) || !bytes_of(m, k, 2, &x_bytes) || !bytes_of(k / 8, n, 4, &w_bytes) ||
+  if (!bytes_of(m, n, 2, &out_bytes) || !bytes_of(m, k, 2, &x_bytes) || !bytes_of(k / (32 / bits), n, 4, &w_bytes) ||
       !bytes_of(k / 128, n, 2, &s_bytes) || wgs > kaio::kMaxWorkgroups || n >= kaio::kMaxN ||
       k >= kaio::kMaxK)
     return fail(KAIO_ERR_INVALID_PROBLEM, op, "problem too large for one launch (m=%u, n=%u, k=%u)", m, n, k);
@@ -244,7 +241,26 @@ kaio_status kaio_qkv_w4a16(const void* x, const uint32_t* w_q, const uint32_t* w
   p.out[1] = static_cast<uint16_t*>(k_out);
   p.out[2] = static_cast<uint16_t*>(v);
   p.m = m; p.n = n; p.k = k;
+  p.bits = bits;
   return launched(op, decode ? kaio::launch_qkv_decode(p, s) : kaio::launch_qkv_prefill(p, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+kaio_status kaio_qkv_w4a16(const void* x, const uint32_t* w_q, const uint32_t* w_k, const uint32_t* w_v,
+                           const void* s_q, const void* s_k, const void* s_v, void* q, void* k_out,
+                           void* v, uint32_t m, uint32_t n, uint32_t k, uint32_t group_size,
+                           void* stream) {
+  return qkv("qkv_w4a16", 4, x, w_q, w_k, w_v, s_q, s_k, s_v, q, k_out, v, m, n, k, group_size, stream);
+}
+
+kaio_status kaio_qkv_w8a16(const void* x, const uint32_t* w_q, const uint32_t* w_k, const uint32_t* w_v,
+                           const void* s_q, const void* s_k, const void* s_v, void* q, void* k_out,
+                           void* v, uint32_t m, uint32_t n, uint32_t k, uint32_t group_size,
+                           void* stream) {
+  return qkv("qkv_w8a16", 8, x, w_q, w_k, w_v, s_q, s_k, s_v, q, k_out, v, m, n, k, group_size, stream);
 }
 
 kaio_status kaio_gemm_f16f32(const void* a, const void* b, float* c, uint32_t m, uint32_t n, uint32_t k,

@@ -12,10 +12,11 @@ namespace kaio {
 
 struct QkvProblem {
   const uint16_t* x;        // f16 [m, k]
-  const uint32_t* w[3];     // u32 [k/8, n]
+  const uint32_t* w[3];     // u32 [k*bits/32, n]: INT4 (bits 4) or INT8 (bits 8) values packed along k
   const uint16_t* s[3];     // f16 [k/128, n]
   uint16_t* out[3];         // f16 [m, n]
   uint32_t m, n, k;
+  uint32_t bits;            // 4 (W4A16) or 8 (W8A16)
 };
 
 // Tile geometry, shared with the host-side grid-size checks.

@@ -67,10 +67,13 @@ template <> struct HalfVec<1> { typedef uint16_t T; };
 // w % RSPLIT (16*RT rows) and reduction part w / RSPLIT of WAVES / RSPLIT.
 // XR = rows of x a wave keeps per group (a multiple of 4, at most 16*RT;
 // 8 when m <= 8, which leaves registers for two groups in flight).
-template <int RT, int RSPLIT, int VEC, int WAVES, bool kFull, int XR>
+// BITS = 4 (W4A16: one packed word per 8 k of a column) or 8 (W8A16: two).
+template <int BITS, int RT, int RSPLIT, int VEC, int WAVES, bool kFull, int XR>
 __global__ void __launch_bounds__(WAVES * 64, 1)
 qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   constexpr int THREADS = WAVES * kWave;
+  constexpr int WPK = BITS / 4;                 // packed words per 8 k of a column
+  constexpr int PR = 16 * WPK;                  // packed rows per group of 128 k
   constexpr int BN = 16 * VEC;                  // columns per strip
   constexpr int KSPLIT = WAVES / RSPLIT;        // waves per row block, splitting the reduction
   constexpr int ROWS = 16 * RT * RSPLIT;        // rows per workgroup
@@ -83,7 +86,7 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   // read) when every word feeds two or more row tiles; otherwise in the
   // nibble-interleaved order (9 ops per word) with each x fragment permuted
   // to match (4 ops), which costs less when a word feeds one row tile.
-  constexpr bool kNatural = RT >= 2;
+  constexpr bool kNatural = RT >= 2 || BITS == 8;
   static_assert(XR % 4 == 0 && XR <= 16 * RT, "x rows per wave");
   constexpr int XLD = kGroup / 8 + 1;           // 16-byte chunks per padded LDS row of x
   __shared__ float red[KSPLIT][ROWS][BN];
@@ -135,7 +138,9 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
     xfrag[r] = (lr < xvalid ? lr : xvalid - 1) * XLD + kb;
   }
   uint4* const xw = xl[wave];
-  const uint32_t* wlane = w + (size_t)kb * N + colv;   // + (16g + 4ks) * N
+  // lane (kb, c) of k-step ks holds packed rows WPK*(4ks + kb) + j, j < WPK:
+  // the 8 consecutive k of its B operand
+  const uint32_t* wlane = w + (size_t)(WPK * kb) * N + colv;   // + (PR*g + 4*WPK*ks + j) * N
 
   floatx4 acc[VEC][RT];
 #pragma unroll
@@ -144,7 +149,7 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
     for (int r = 0; r < RT; ++r) acc[t][r] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   struct Chunk {
-    uint32_t wv[GCHUNK][4][VEC];
+    uint32_t wv[GCHUNK][4][WPK][VEC];
     uint4 xs[GCHUNK][XROWS / 4];     // x rows 4j .. 4j+3 of the group, 16 bytes per lane
     uint32_t sc[GCHUNK][VEC];
   };
@@ -161,16 +166,18 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
       for (int j = 0; j < XROWS / 4; ++j)
         c.xs[gi][j] = *reinterpret_cast<const uint4*>(p.x + xoff(j) + (size_t)g * kGroup);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const size_t roff = ((size_t)g * 16 + ks * 4) * N;
-        if (kFull) {
-          const WV v = *reinterpret_cast<const WV*>(wlane + roff);
-          __builtin_memcpy(c.wv[gi][ks], &v, sizeof(v));
-        } else {
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-          for (int t = 0; t < VEC; ++t) c.wv[gi][ks][t] = (colv + t < N) ? wlane[roff + t] : 0u;
+        for (int j = 0; j < WPK; ++j) {
+          const size_t roff = ((size_t)g * PR + ks * 4 * WPK + j) * N;
+          if (kFull) {
+            const WV v = *reinterpret_cast<const WV*>(wlane + roff);
+            __builtin_memcpy(c.wv[gi][ks][j], &v, sizeof(v));
+          } else {
+#pragma unroll
+            for (int t = 0; t < VEC; ++t) c.wv[gi][ks][j][t] = (colv + t < N) ? wlane[roff + t] : 0u;
+          }
         }
-      }
       if (kFull) {
         using HV = typename HalfVec<VEC>::T;
         const HV sv = *reinterpret_cast<const HV*>(s + (size_t)g * N + colv);
@@ -205,8 +212,15 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
                             : permute_x_like_int4x8(xw[xfrag[r] + 4 * ks]);
 #pragma unroll
           for (int t = 0; t < VEC; ++t) {
-            const half8_t b = kNatural ? unpack_int4x8_scaled(c.wv[gi][ks][t])
-                                       : unpack_int4x8_interleaved(c.wv[gi][ks][t]);
+            half8_t b;
+            if constexpr (kNatural) {
+              uint32_t words[WPK];
+#pragma unroll
+              for (int j = 0; j < WPK; ++j) words[j] = c.wv[gi][ks][j][t];
+              b = unpack_b_scaled<BITS>(words);
+            } else {
+              b = unpack_int4x8_interleaved(c.wv[gi][ks][0][t]);
+            }
 #pragma unroll
             for (int r = 0; r < RT; ++r)
               part[t][r] = mfma16x16x32(a[r], b, ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : part[t][r]);
@@ -270,16 +284,31 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   }
 }
 
-template <int RT, int RSPLIT, int VEC, int WAVES, int XR = 16 * RT>
+template <int BITS, int RT, int RSPLIT, int VEC, int WAVES, int XR = 16 * RT>
 hipError_t launch_split_k(const QkvProblem& p, hipStream_t stream) {
   constexpr uint32_t BN = 16 * VEC;
   const uint32_t nstrips = (p.n + BN - 1) / BN;
   const dim3 grid(3 * nstrips), block(WAVES * kWave);
   if (p.n % BN == 0)
-    hipLaunchKernelGGL((qkv_decode_kernel<RT, RSPLIT, VEC, WAVES, true, XR>), grid, block, 0, stream, p, nstrips);
+    hipLaunchKernelGGL((qkv_decode_kernel<BITS, RT, RSPLIT, VEC, WAVES, true, XR>), grid, block, 0, stream, p,
+                       nstrips);
   else
-    hipLaunchKernelGGL((qkv_decode_kernel<RT, RSPLIT, VEC, WAVES, false, XR>), grid, block, 0, stream, p, nstrips);
+    hipLaunchKernelGGL((qkv_decode_kernel<BITS, RT, RSPLIT, VEC, WAVES, false, XR>), grid, block, 0, stream, p,
+                       nstrips);
   return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_decode_bits(const QkvProblem& p, hipStream_t stream) {
+  // INT8 words are twice the registers per group: at m <= 16 its waves keep
+  // the 8-wave register budget (each wave then streams four groups)
+  constexpr int kSmallWaves = BITS == 8 ? 8 : 16;
+  if (p.m <= 8) return launch_split_k<BITS, 1, 1, 4, kSmallWaves, 8>(p, stream);
+  if (p.m <= 16) return launch_split_k<BITS, 1, 1, 4, kSmallWaves>(p, stream);
+  if (p.m <= 32) return launch_split_k<BITS, 2, 1, 4, 8>(p, stream);
+  if (p.m <= 64)
+    return launch_split_k<BITS, KAIO_SK4_RT, 4 / KAIO_SK4_RT, KAIO_SK4_VEC, KAIO_SK4_WAVES>(p, stream);
+  return launch_split_k<BITS, KAIO_SK8_RT, 8 / KAIO_SK8_RT, 4, KAIO_SK8_WAVES>(p, stream);
 }
 
 }  // namespace
@@ -289,11 +318,7 @@ hipError_t launch_qkv_decode(const QkvProblem& p, hipStream_t stream) {
   static_assert(decode_bn(16) == 64 && decode_bn(32) == 64 && decode_bn(64) == 16 * KAIO_SK4_VEC &&
                     decode_bn(128) == 64,
                 "strip widths must match the host-side grid computation");
-  if (p.m <= 8) return launch_split_k<1, 1, 4, 16, 8>(p, stream);
-  if (p.m <= 16) return launch_split_k<1, 1, 4, 16>(p, stream);
-  if (p.m <= 32) return launch_split_k<2, 1, 4, 8>(p, stream);
-  if (p.m <= 64) return launch_split_k<KAIO_SK4_RT, 4 / KAIO_SK4_RT, KAIO_SK4_VEC, KAIO_SK4_WAVES>(p, stream);
-  return launch_split_k<KAIO_SK8_RT, 8 / KAIO_SK8_RT, 4, KAIO_SK8_WAVES>(p, stream);
+  return p.bits == 8 ? launch_decode_bits<8>(p, stream) : launch_decode_bits<4>(p, stream);
 }
 
 }  // namespace kaio

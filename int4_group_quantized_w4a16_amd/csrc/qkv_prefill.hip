@@ -75,17 +75,34 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // of XDIST+1 slots), the packed weights one group ahead (2 slots), and the
 // scales SCHUNK groups at a time:
 //   x  [XDIST+1][X_CHUNKS]            swizzled rows of x
-//   w  [2][3][WAVES][16][16] u32      packed rows x columns of output q, wave w
+//   w  [WSLOTS][3][WAVES][PR][16] u32 packed rows x columns of output q, wave w
 //   s  [3][WAVES][SCHUNK][16] f16     scales of the wave's 16 columns (n % 8 == 0)
+// PR = 16 packed rows per group for INT4, 32 for INT8.  A wave reads only the
+// words it loaded itself and has consumed (unpacked into registers) the words
+// of group g before the barrier that starts group g, after which it loads
+// group g+1: one weight slot is enough, and INT8 (twice the words) uses one so
+// that the ring fits in LDS.  INT4 keeps two.
 constexpr int SCHUNK = 32;
-template <int WAVES, int XDIST>
+template <int BITS, int WAVES, int XDIST>
 struct RingLayout {
   static constexpr int kXSlots = XDIST + 1;
+  static constexpr int kWSlots = BITS == 4 ? 2 : 1;
+  static constexpr int kWWords = 256 * (BITS / 4);       // words per output per wave per group
   static constexpr int kWBase = kXSlots * X_CHUNKS;
-  static constexpr int kWSize = 3 * WAVES * 256 / 4;
-  static constexpr int kSBase = kWBase + 2 * kWSize;
+  static constexpr int kWSize = 3 * WAVES * kWWords / 4;
+  static constexpr int kSBase = kWBase + kWSlots * kWSize;
   static constexpr int kSize = kSBase + 3 * WAVES * SCHUNK * 16 * 2 / 16;   // uint4
 };
+
+// LDS row position of packed row r within a wave's [PR][16] word block.  INT8
+// B operands take rows 8ks + 2kb + j (k-step ks, 8-k block kb, word j), which
+// land on the same banks for kb and kb + 2 unless rows with bit 2 set are
+// swapped pairwise (r ^ 1): then the four kb of one read hit four different
+// 16-bank windows.  INT4 rows 4ks + kb already do.
+template <int BITS>
+__device__ __forceinline__ uint32_t wrow_pos(uint32_t r) {
+  return BITS == 8 ? r ^ ((r >> 2) & 1u) : r;
+}
 
 // A wave-uniform pointer the compiler must treat as opaque (kept in SGPRs):
 // stops it from folding the per-lane offsets into 64-bit vector addresses
@@ -143,7 +160,7 @@ __device__ __forceinline__ void fold(floatx4 (&acc)[3], const floatx4 (&pb)[3], 
 // stalling the start of the next group.  `next_w` points at this wave's
 // next-group words in LDS, `next_s[q]` at its scales; the wait before the
 // tail covers them (XPENDING = the x loads issued after them).
-template <int WAVES, int XPENDING, typename IssueX>
+template <int BITS, int WAVES, int XPENDING, typename IssueX>
 __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3][4], float (&sf)[3],
                                           const uint4* __restrict__ xs, const uint32_t* __restrict__ next_w,
                                           const uint16_t* const (&next_s)[3], uint32_t l16, uint32_t kb,
@@ -178,12 +195,17 @@ __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(XPENDING) : "memory");
   // all of the next group's words and scales are read at once, so that their
   // LDS latency passes under the MFMAs instead of in front of each unpack
-  uint32_t nw[3][4];
+  constexpr int WPK = BITS / 4;
+  constexpr int WW = 256 * WPK;
+  uint32_t nw[3][4][WPK];
   uint16_t ns16[3];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int q = 0; q < 3; ++q) nw[q][ks] = next_w[q * WAVES * 256 + ks * 64 + lane];
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+      for (int j = 0; j < WPK; ++j)
+        nw[q][ks][j] = next_w[q * WAVES * WW + wrow_pos<BITS>(WPK * (4 * ks + kb) + j) * 16 + l16];
 #pragma unroll
   for (int q = 0; q < 3; ++q) ns16[q] = *next_s[q];
 #pragma unroll
@@ -195,7 +217,7 @@ __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3
         pbuf[t][q] = mfma16x16x32(abuf[t == 0 ? T0 : T1][ks], bq[q][ks],
                                   ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : pbuf[t][q]);
 #pragma unroll
-    for (int q = 0; q < 3; ++q) bq[q][ks] = unpack_int4x8_scaled(nw[q][ks]);
+    for (int q = 0; q < 3; ++q) bq[q][ks] = unpack_b_scaled<BITS>(nw[q][ks]);
     __builtin_amdgcn_sched_barrier(0);
   }
   fold(acc[RT - 2], pbuf[0], sf);
@@ -204,14 +226,18 @@ __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3
   for (int q = 0; q < 3; ++q) sf[q] = h2f(ns16[q]) * kUnpackScaledInv;
 }
 
-template <int WAVES, int XDIST, bool kAligned>
+// BITS = 4 (W4A16) or 8 (W8A16: two packed words per 8 k of a column).
+template <int BITS, int WAVES, int XDIST, bool kAligned>
 __global__ void __launch_bounds__(WAVES * 64, 1)
 qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   constexpr int THREADS = WAVES * 64;
+  constexpr int WPK = BITS / 4;                  // packed words per 8 k of a column
+  constexpr int PR = 16 * WPK;                   // packed rows per group
   constexpr int BN = 16 * WAVES;
   constexpr int XPER = X_CHUNKS / THREADS;       // x loads per thread per stage
   constexpr int OUT_LD = BN + 8;                 // padded f16 row of the epilogue tile
-  using L = RingLayout<WAVES, XDIST>;
+  using L = RingLayout<BITS, WAVES, XDIST>;
+  constexpr int WW = L::kWWords;
   static_assert(XPER * THREADS == X_CHUNKS, "x stage must split evenly");
   static_assert(BM * OUT_LD * 2 <= L::kSize * 16, "epilogue tile must fit in the ring");
   static_assert(XPER < 64, "vmcnt range");
@@ -246,12 +272,17 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   }
   const uint32_t col = n0 + wave * 16 + l16;
   const uint32_t colc = col < N ? col : N - 1;   // columns past N are computed, never stored
-  // Weights, 16-byte path (n % 8 == 0): lane l fetches packed row l / 4,
-  // columns 4(l % 4) .. +3 of the wave's 16 -- one load per output per group.
-  // A group of four columns lies wholly inside or wholly past N here.
-  // 4-byte path: lane (kb, c) fetches packed row 4 ks + kb, column c.
+  // Weights, 16-byte path (n % 8 == 0): load j of lane l fills LDS row
+  // position 16j + l/4, columns 4(l % 4) .. +3 of the wave's 16, from the
+  // packed row stored there (wrow_pos is its own inverse) -- WPK loads per
+  // output per group.  A group of four columns lies wholly inside or wholly
+  // past N here.  4-byte path: load i of lane (kb, c) fills row position
+  // 4i + kb, column c.
   const uint32_t c4 = n0 + wave * 16 + 4 * (lane & 3);
-  const uint32_t woff = kAligned ? ((lane >> 2) * N + (c4 < N ? c4 : N - 4)) * 4 : (kb * N + colc) * 4;
+  const uint32_t woff = kAligned ? (wrow_pos<BITS>(lane >> 2) * N + (c4 < N ? c4 : N - 4)) * 4
+                                 : (kb * N + colc) * 4;
+  // 4-byte path, INT8: odd loads (row positions with bit 2 set) take rows kb ^ 1
+  const uint32_t woff_odd = kAligned ? woff : ((BITS == 8 ? kb ^ 1u : kb) * N + colc) * 4;
   // Scales (n % 8 == 0): lane l fetches the 8 columns 8(l % 2) .. +7 of the
   // wave's 16 for group l / 2 of a chunk -- one 16-byte load per output per
   // SCHUNK groups.
@@ -260,24 +291,27 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   const uint32_t sgi = lane >> 1;     // group within the chunk
 
   auto xslot = [&](uint32_t g) { return smem + (g % L::kXSlots) * X_CHUNKS; };
-  auto wslot = [&](uint32_t g) { return smem + L::kWBase + (g & 1) * L::kWSize; };
-  auto wave_words = [&](uint32_t g) { return reinterpret_cast<const uint32_t*>(wslot(g)) + wave * 256; };
+  auto wslot = [&](uint32_t g) { return smem + L::kWBase + (g % L::kWSlots) * L::kWSize; };
+  auto wave_words = [&](uint32_t g) { return reinterpret_cast<const uint32_t*>(wslot(g)) + wave * WW; };
   uint16_t* const sbuf = reinterpret_cast<uint16_t*>(smem + L::kSBase);
 
   // Weights of group g (clamped to the last group: a repeat lands in a slot
-  // nobody reads) into weight slot g & 1.
+  // nobody reads) into weight slot g % kWSlots.
   auto issue_w = [&](uint32_t g) {
     const uint32_t gc = g < G ? g : G - 1;
-    uint32_t* wst = reinterpret_cast<uint32_t*>(wslot(g)) + wave * 256;
+    uint32_t* wst = reinterpret_cast<uint32_t*>(wslot(g)) + wave * WW;
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
-      const char* wg = uniform(reinterpret_cast<const char*>(p.w[q] + (size_t)gc * 16 * N));
+      const char* wg = uniform(reinterpret_cast<const char*>(p.w[q] + (size_t)gc * PR * N));
       if (kAligned) {
-        dma_to_lds(wg, lane_offset(woff), wst + q * WAVES * 256, 1);
+#pragma unroll
+        for (int j = 0; j < WPK; ++j)
+          dma_to_lds(uniform(wg + (size_t)j * 64 * N), lane_offset(woff), wst + q * WAVES * WW + j * 256, 1);
       } else {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          dma_to_lds(uniform(wg + (size_t)ks * 16 * N), lane_offset(woff), wst + q * WAVES * 256 + ks * 64, 0);
+        for (int i = 0; i < 4 * WPK; ++i)
+          dma_to_lds(uniform(wg + (size_t)i * 16 * N), lane_offset((i & 1) ? woff_odd : woff),
+                     wst + q * WAVES * WW + i * 64, 0);
       }
     }
   };
@@ -328,7 +362,12 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
 #pragma unroll
     for (int q = 0; q < 3; ++q)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) bq[q][ks] = unpack_int4x8_scaled(w0[q * WAVES * 256 + ks * 64 + lane]);
+      for (int ks = 0; ks < 4; ++ks) {
+        uint32_t words[WPK];
+#pragma unroll
+        for (int j = 0; j < WPK; ++j) words[j] = w0[q * WAVES * WW + wrow_pos<BITS>(WPK * (4 * ks + kb) + j) * 16 + l16];
+        bq[q][ks] = unpack_b_scaled<BITS>(words);
+      }
     const uint16_t* ns[3];
     scale_src(0, ns);
 #pragma unroll
@@ -360,7 +399,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
     const uint16_t* ns[3];
     scale_src(g + 1, ns);
     // x of g + XDIST goes out one load per row tile, between MFMAs
-    group_mma<WAVES, XPER>(acc, bq, sf, xslot(g), wave_words(g + 1), ns, l16, kb, lane,
+    group_mma<BITS, WAVES, XPER>(acc, bq, sf, xslot(g), wave_words(g + 1), ns, l16, kb, lane,
                            [&](int i) { issue_x_one(g + XDIST, i); });
   }
   wait_vm_barrier<0>();   // no load is still writing the ring the epilogue reuses
@@ -400,14 +439,14 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   }
 }
 
-template <int WAVES, int XDIST, bool kAligned>
+template <int BITS, int WAVES, int XDIST, bool kAligned>
 hipError_t launch_variant(const QkvProblem& p, hipStream_t stream) {
   constexpr int BN = 16 * WAVES;
   const uint32_t mtiles = (p.m + BM - 1) / BM;
   const uint32_t ntiles = (p.n + BN - 1) / BN;
-  const size_t lds = (size_t)RingLayout<WAVES, XDIST>::kSize * 16;
+  const size_t lds = (size_t)RingLayout<BITS, WAVES, XDIST>::kSize * 16;
   const dim3 grid(mtiles * ntiles), block(WAVES * 64);
-  auto* kern = &qkv_prefill_kernel<WAVES, XDIST, kAligned>;
+  auto* kern = &qkv_prefill_kernel<BITS, WAVES, XDIST, kAligned>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
@@ -415,16 +454,21 @@ hipError_t launch_variant(const QkvProblem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_qkv_prefill(const QkvProblem& p, hipStream_t stream) {
+template <int BITS>
+hipError_t launch_prefill_bits(const QkvProblem& p, hipStream_t stream) {
   // 16-byte output rows and f16-pair scale loads need n % 8 == 0
   const bool aligned = p.n % 8 == 0;
   if (prefill_waves(p.m, p.n) == 4)
-    return aligned ? launch_variant<4, KAIO_PREFILL_XDIST, true>(p, stream)
-                   : launch_variant<4, KAIO_PREFILL_XDIST, false>(p, stream);
-  return aligned ? launch_variant<8, KAIO_PREFILL_XDIST, true>(p, stream)
-                 : launch_variant<8, KAIO_PREFILL_XDIST, false>(p, stream);
+    return aligned ? launch_variant<BITS, 4, KAIO_PREFILL_XDIST, true>(p, stream)
+                   : launch_variant<BITS, 4, KAIO_PREFILL_XDIST, false>(p, stream);
+  return aligned ? launch_variant<BITS, 8, KAIO_PREFILL_XDIST, true>(p, stream)
+                 : launch_variant<BITS, 8, KAIO_PREFILL_XDIST, false>(p, stream);
+}
+
+}  // namespace
+
+hipError_t launch_qkv_prefill(const QkvProblem& p, hipStream_t stream) {
+  return p.bits == 8 ? launch_prefill_bits<8>(p, stream) : launch_prefill_bits<4>(p, stream);
 }
 
 }  // namespace kaio

@@ -20,8 +20,9 @@ def to_host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
-def qkv_on_gpu(x, w, s, **kw):
+def qkv_on_gpu(x, w, s, bits=4, **kw):
     import int4_group_quantized_w4a16_amd as kaio
-    outs = kaio.kaio_qkv_w4a16(to_dev(x), *[to_dev(a) for a in w], *[to_dev(a) for a in s], **kw)
+    fn = kaio.kaio_qkv_w8a16 if bits == 8 else kaio.kaio_qkv_w4a16
+    outs = fn(to_dev(x), *[to_dev(a) for a in w], *[to_dev(a) for a in s], **kw)
     torch.cuda.synchronize()
     return [to_host(o) for o in outs]

@@ -51,6 +51,23 @@ def qkv(x=A, w=(A + STEP, A + 2 * STEP, A + 3 * STEP), s=(A + 4 * STEP, A + 5 * 
     return st, kaio.kaio_last_error()
 
 
+def test_qkv_w8a16_validation():
+    L = kaio.lib()
+    w = (A + STEP, A + 2 * STEP, A + 3 * STEP)
+    s = (A + 4 * STEP, A + 5 * STEP, A + 6 * STEP)
+    o = (A + 7 * STEP, A + 8 * STEP, A + 9 * STEP)
+    call = lambda **kw: (L.kaio_qkv_w8a16(kw.get("x", A), *kw.get("w", w), *s, *kw.get("o", o), kw.get("m", 4),
+                                          64, kw.get("k", 256), kw.get("g", 128), None), kaio.kaio_last_error())
+    st, msg = call(g=64)
+    assert st == UNSUP and msg.startswith("kaio::qkv_w8a16:") and "group_size" in msg
+    assert call(k=200)[0] == PROB
+    assert call(m=0)[0] == OK
+    assert "output q is null" in call(o=(0, o[1], o[2]))[1]
+    # the packed weights are k/4 rows x 64 columns x 4 bytes = 16 KiB at k = 256: a weight
+    # tensor starting 8 KiB into another overlaps it for W8A16 (it would not for INT4's 8 KiB)
+    assert call(o=(A + STEP + 8192, o[1], o[2]))[1].endswith("overlaps w_q_packed")
+
+
 def test_qkv_validation_order_and_messages():
     st, msg = qkv(g=64)
     assert st == UNSUP and msg.startswith("kaio::qkv_w4a16:") and "group_size" in msg
