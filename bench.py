@@ -7,13 +7,19 @@ f16[32,4096] scales, group 128 -> Q, K, V f16[2048,4096]); ``value`` is its
 throughput in TFLOP/s (2*M*N*K*3 algorithmic flops per call).  The same JSON
 line carries:
 
-* ``roofline``     the prefill kernel against the dense f16 MFMA peak;
+* ``roofline``     the prefill kernel against the dense f16 MFMA peak, with the
+                   shader clock sampled while the kernel runs back to back and
+                   the fraction against the peak at that clock;
 * ``secondary``    decode (8 rows, weights rotated over 21 sets so every call
-                   streams from HBM), the dense 4096^3 GEMM and the dequant
-                   backward (f32 and bf16, [16384, 8192], g=128), each against
-                   its own roof;
-* ``cpu_baseline`` the float64 CPU oracle timed on this host's cores over a
-                   bounded sample of the prefill rows.
+                   streams from HBM) next to a plain streaming read of the same
+                   bytes, batched decode, the W8A16 sibling (decode and
+                   prefill), the dense 4096^3 GEMM and its backward, and the
+                   dequant backward (f32 and bf16, [16384, 8192], g=128) next to
+                   a plain copy of the same bytes -- each against its own roof,
+                   each with the CPU oracle timed on this host (``cpu_oracle``);
+* ``cpu_baseline`` the float64 CPU oracle timed on this host's cores over the
+                   prefill workload; the same leg compares the oracle's full
+                   results with the GPU's (``parity`` entries: all outputs).
 
 All inputs are seeded synthetic data already resident in device memory when
 a timed region starts.
@@ -49,9 +55,36 @@ def kernel_source_hash(name: str) -> str:
     return h.hexdigest()[:16]
 
 
-def timed(fn, steps, warmup, stream):
+CONDITION_MS = 100.0
+
+
+def condition(fn, ms=CONDITION_MS):
+    """Runs fn() back to back, untimed, for about `ms` of GPU time.
+
+    After an idle period (here: seconds of input generation on the host) the
+    GPU needs ~10 ms of load to leave its low-power state: the first ~50
+    prefill launches after idle take 210-280 us, the sustained rate is ~175 us
+    (per-launch event series).  Every leg is therefore conditioned with its own
+    work before its warm-up and timed steps, so that the timed steps measure
+    the sustained rate of the kernel, not the power ramp."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(3):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    per = max(e0.elapsed_time(e1) / 3, 1e-3)
+    for i in range(int(ms / per) + 1):
+        fn(i)
+    torch.cuda.synchronize()
+
+
+def timed(fn, steps, warmup, stream, conditioned=False):
     """Average duration (ms) of fn() over `steps` back-to-back launches, HIP events on `stream`."""
     import torch
+    if not conditioned:
+        condition(fn)
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -84,6 +117,7 @@ def timed_graph(fn, calls, replays, stream):
             fn(i)
     g.replay()
     torch.cuda.synchronize()
+    condition(lambda i: g.replay())
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -106,15 +140,42 @@ def measured_traffic(kernel: str, src: str, algorithmic_bytes: float):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(inp, budget_s: float):
-    """The float64 oracle on a bounded sample of prefill rows, scaled to TFLOP/s."""
-    import numpy as np
-    from oracle.qkv import qkv_project
+def host_cores():
+    """Cores this process may run on (the oracle's BLAS and numpy use them)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count()
+
+
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        cores = os.cpu_count()
+        return None
+
+
+def best_of(fn, runs):
+    """Shortest wall time of `runs` calls of fn() (seconds) and the last result."""
+    best, out = None, None
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        out = fn()
+        dt = time.perf_counter() - t0
+        best = dt if best is None else min(best, dt)
+    return best, out
+
+
+def oracle_entry(value, unit, seconds, sample):
+    return {"value": round(value, 6), "unit": unit, "cores": host_cores(), "blas_threads": blas_threads(),
+            "kind": "oracle", "seconds": round(seconds, 3), "sample": sample}
+
+
+def cpu_baseline(inp, budget_s: float):
+    """The float64 oracle on the prefill workload (all rows when they fit the budget), in TFLOP/s."""
+    import numpy as np
+    from oracle.qkv import qkv_project
     M, N, K = inp.shape
     probe = min(M, 128)
     t0 = time.perf_counter()
@@ -130,9 +191,112 @@ def cpu_baseline(inp, budget_s: float):
         spent += time.perf_counter() - t0
         runs += 1
     flops = 2.0 * rows * N * K * 3 * runs
-    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"float64 oracle (numpy dequantize + f64 matmul), rows 0..{rows - 1} of the {M}-row "
-                      f"prefill workload, {runs} run(s), {spent:.1f} s"}
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": host_cores(),
+            "blas_threads": blas_threads(), "kind": "oracle",
+            "sample": f"float64 oracle (numpy dequantize + f64 matmul, Y only), rows 0..{rows - 1} of the "
+                      f"{M}-row prefill workload, {runs} run(s), {spent:.1f} s"}
+
+
+def qkv_parity(outs, inp, bits=4):
+    """All outputs against the oracle: violations, max |d|/tol, and the share equal to RNE_f16(Y*)."""
+    import numpy as np
+    from oracle import compare
+    from oracle.qkv import qkv_project
+    ys, ts = qkv_project(inp.x, inp.w, inp.s, bits=bits)
+    bad, worst, equal, total = 0, 0.0, 0, 0
+    for o, y, t in zip(outs, ys, ts):
+        b, r = compare.excess(o, y, compare.qkv_tolerance(y, t))
+        bad += b
+        worst = max(worst, r)
+        equal += int(compare.bits_equal(o, y.astype(np.float16)).sum())
+        total += o.size
+    return {"checked": total, "violations": bad, "max_ratio_to_tol": round(worst, 4),
+            "bit_equal_to_rne_f16_of_oracle": round(equal / total, 6)}
+
+
+def shader_clock_under(work, stream, dev, probes=6, probe_us=1000):
+    """Shader clock while `work()` keeps the GPU busy: probe waves on a side stream (one
+    wave each, no LDS, so they run beside the kernel's workgroups) count shader cycles
+    against the real-time counter; returns their median in MHz, or None."""
+    import ctypes
+    import torch
+    L = roof_lib()
+    if L is None:
+        return None
+    khz = L.kaio_roof_wall_clock_khz()
+    if khz <= 0:
+        return None
+    out = torch.zeros((probes, 4), dtype=torch.int64, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    ticks = int(probe_us * khz / 1000)
+    side.wait_stream(stream)
+    work(0)                                   # queue the first part of the load
+    with torch.cuda.stream(side):
+        for i in range(probes):
+            st = L.kaio_roof_clock_probe(ctypes.c_void_p(out[i].data_ptr()), ctypes.c_ulonglong(ticks),
+                                         ctypes.c_void_p(side.cuda_stream))
+            if st != 0:
+                return None
+    work(1)                                   # and the rest behind the probes
+    torch.cuda.synchronize()
+    v = out.cpu().numpy()
+    mhz = sorted(float(c) / float(r) * khz / 1000.0 for c, r, _, _ in v if r > 0)
+    if not mhz:
+        return None
+    return {"median_mhz": round(mhz[len(mhz) // 2], 1), "min_mhz": round(mhz[0], 1), "max_mhz": round(mhz[-1], 1),
+            "probes": len(mhz), "probe_us": probe_us,
+            "source": "probe waves beside the back-to-back kernel: shader-clock counter (s_memtime) over the "
+                      "real-time counter (s_memrealtime)"}
+
+
+def roof_lib():
+    import ctypes
+    path = os.path.join(ROOT, "int4_group_quantized_w4a16_amd", "libkaio_roof.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    L.kaio_roof_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_void_p]
+    L.kaio_roof_stream_read.restype = ctypes.c_int
+    L.kaio_roof_sink_bytes.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.c_int]
+    L.kaio_roof_sink_bytes.restype = ctypes.c_size_t
+    L.kaio_roof_clock_probe.argtypes = [ctypes.c_void_p, ctypes.c_ulonglong, ctypes.c_void_p]
+    L.kaio_roof_clock_probe.restype = ctypes.c_int
+    L.kaio_roof_wall_clock_khz.argtypes = []
+    L.kaio_roof_wall_clock_khz.restype = ctypes.c_int
+    return L
+
+
+READ_SHAPES = ((1, 256), (2, 256), (4, 256), (8, 256), (16, 256), (4, 512), (8, 512), (8, 1024))
+
+
+def read_roof(nbytes, sets, replays, stream, dev):
+    """Best plain streaming read of `nbytes` (rotated over `sets` buffers, like the decode
+    weights) over a few launch shapes, timed exactly like decode: us per call and GB/s."""
+    import ctypes
+    import torch
+    L = roof_lib()
+    if L is None:
+        return None
+    nb = (nbytes + 15) // 16 * 16
+    bufs = [torch.randint(-2 ** 31, 2 ** 31 - 1, (nb // 4,), dtype=torch.int32, device=dev) for _ in range(sets)]
+    best = None
+    for u, th in READ_SHAPES:
+        sink = torch.empty((L.kaio_roof_sink_bytes(nb, u, th) // 4 + 1,), dtype=torch.int32, device=dev)
+
+        def call(i, u=u, th=th, sink=sink):
+            st = L.kaio_roof_stream_read(bufs[i % sets].data_ptr(), nb, sink.data_ptr(), u, th,
+                                         ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"kaio_roof_stream_read failed ({st})")
+        ms = timed_graph(call, 4 * sets, replays, stream)
+        if best is None or ms < best[0]:
+            best = (ms, u, th)
+    del bufs
+    ms, u, th = best
+    return {"us_per_call": round(ms * 1e3, 3), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "bytes": nbytes, "launch": f"{u} x 16-byte loads per thread, {th} threads per workgroup",
+            "shapes_tried": len(READ_SHAPES)}
 
 
 def summarize(dirs):
@@ -166,7 +330,7 @@ def summarize(dirs):
 
 
 # the kernel instantiation each workload runs (the bench's own calls also launch others)
-TRAFFIC_KERNELS = {"qkv_prefill": "qkv_prefill_kernel<8,", "qkv_decode": "qkv_decode_kernel<1, 1, 4, 16,"}
+TRAFFIC_KERNELS = {"qkv_prefill": "qkv_prefill_kernel<4, 8,", "qkv_decode": "qkv_decode_kernel<4, 1, 1, 4, 16,"}
 
 
 def write_traffic(key: str, src: str, fetch_dir: str, write_dir: str, command: str):
@@ -220,9 +384,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "batched", "gemm", "bwd"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "batched", "w8", "gemm", "bwd"], default="all")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
@@ -258,6 +422,8 @@ def main():
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int32) if a.dtype == np.uint32 else a)).to(dev)
     result = {}
     secondary = {}
+    host = {}          # GPU results kept for the CPU leg's full comparisons
+    replays = max(5, args.steps // 10)
 
     # ---- prefill: the step --------------------------------------------------------------
     c = workloads.QKV_PREFILL
@@ -268,11 +434,33 @@ def main():
     outs = [torch.empty((M, N), dtype=torch.float16, device=dev) for _ in range(3)]
     step = lambda i: kaio.kaio_qkv_w4a16(x, *w, *s, *outs)
     flops = 2.0 * M * N * K * 3
-    ms, wall = timed(step, args.steps, args.warmup, stream)
+    # conditioning (see condition()) doubles as the clock measurement: probe waves count
+    # shader cycles beside ~60 ms of back-to-back prefill launches
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+
+    def sustained(part):
+        for i in range(20 if part == 0 else 300):
+            step(i)
+    clock = shader_clock_under(sustained, stream, dev)
+    condition(step, 40.0)
+    ms, wall = timed(step, args.steps, args.warmup, stream, conditioned=True)
     tflops = flops / (ms * 1e-3) / 1e12
     algo_bytes = inp.x.nbytes + sum(a.nbytes for a in inp.w) + sum(a.nbytes for a in inp.s) + 3 * M * N * 2
     log(f"[bench] prefill: {ms * 1e3:.1f} us/call, {tflops:.1f} TFLOP/s ({tflops / PEAK_F16_TFLOPS:.1%} of peak)")
+    host["prefill"] = [o.cpu().numpy() for o in outs]
     traffic = measured_traffic("qkv_prefill", "qkv_prefill.hip", algo_bytes)
+    roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_F16_TFLOPS, 4),
+            "traffic": traffic, "algorithmic_flops": flops, "algorithmic_bytes": algo_bytes,
+            "kernel": "qkv_prefill_kernel", "launch_us": round(ms * 1e3, 2)}
+    if clock:
+        peak_clk = PEAK_F16_TFLOPS * clock["median_mhz"] / 2400.0
+        log(f"[bench] shader clock under sustained prefill: {clock['median_mhz']:.0f} MHz "
+            f"(peak there {peak_clk:.0f} TFLOP/s)")
+        roof.update({"sclk": clock, "peak_at_sclk": round(peak_clk, 1),
+                     "frac_at_sclk": round(tflops / peak_clk, 4)})
     result.update({
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -281,46 +469,49 @@ def main():
         "config": {"workload": "W4A16 fused QKV prefill: x f16[2048,4096], 3x packed int4 u32[512,4096], "
                                "3x f16 scales [32,4096], group 128 -> Q,K,V f16[2048,4096]",
                    "M": M, "N": N, "K": K, "group_size": 128},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_F16_TFLOPS, 4),
-                     "traffic": traffic, "algorithmic_flops": flops, "algorithmic_bytes": algo_bytes,
-                     "kernel": "qkv_prefill_kernel", "launch_us": round(ms * 1e3, 2)},
+        "roofline": roof,
     })
     del x, w, s, outs
 
-    # ---- decode, rotated weights ---------------------------------------------------------
+    # ---- decode, rotated weights, and the plain read of the same bytes ----------------
     if args.only in ("all", "decode", "batched"):
         c = workloads.QKV_DECODE
         M, N, K, R = c["M"], c["N"], c["K"], c["rotate"]
         log(f"[bench] generating {R} decode weight sets {M}x{N}x{K}")
         dinp = workloads.qkv_inputs(M, N, K, c["seed"])
         x = t(dinp.x)
-        sets = [(
-            [t(a) for a in dinp.w], [t(a) for a in dinp.s])]
+        sets = [([t(a) for a in dinp.w], [t(a) for a in dinp.s])]
         for j in range(1, R):
             wj, sj = workloads.qkv_weight_set(N, K, c["seed"] + j)
             sets.append(([t(a) for a in wj], [t(a) for a in sj]))
         outs = [torch.empty((M, N), dtype=torch.float16, device=dev) for _ in range(3)]
         dstep = lambda i: kaio.kaio_qkv_w4a16(x, *sets[i % R][0], *sets[i % R][1], *outs)
         # a ~10 us kernel: time it inside a HIP graph so host launch gaps are not counted
-        dms = timed_graph(dstep, 4 * R, max(5, args.steps // 10), stream)
+        dms = timed_graph(dstep, 4 * R, replays, stream)
         dbytes = dinp.x.nbytes + sum(a.nbytes for a in dinp.w) + sum(a.nbytes for a in dinp.s) + 3 * M * N * 2
         gbs = dbytes / (dms * 1e-3) / 1e9
         log(f"[bench] decode: {dms * 1e3:.2f} us/call, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of HBM)")
+        dstep(0)
+        torch.cuda.synchronize()
+        host["decode"] = [o.cpu().numpy() for o in outs]
+        rr = read_roof(dbytes, R, replays, stream, dev)
+        if rr:
+            log(f"[bench] plain read of the same {dbytes} bytes: {rr['us_per_call']:.2f} us/call, {rr['gbs']:.0f} GB/s")
         secondary["qkv_decode"] = {
             "workload": "x f16[8,4096], 3x u32[512,4096], 3x f16[32,4096]; 21 rotated weight sets, "
                         "84 calls per HIP graph replay",
             "us_per_call": round(dms * 1e3, 3), "value": round(gbs, 1), "unit": "GB/s",
             "bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
             "algorithmic_bytes": dbytes, "tflops": round(2.0 * M * N * K * 3 / (dms * 1e-3) / 1e12, 3),
-            "traffic": measured_traffic("qkv_decode", "qkv_decode.hip", dbytes)}
+            "traffic": measured_traffic("qkv_decode", "qkv_decode.hip", dbytes),
+            "read_roof": rr, "frac_of_read_roof": round(rr["us_per_call"] / (dms * 1e3), 4) if rr else None}
         # batched decode (split-K kernel up to m = 128) on the same rotated weights
         batched = []
         for bm in ((16, 32, 64, 128) if args.only != "decode" else ()):
             xb = t(np.random.default_rng(c["seed"] + 100 + bm).standard_normal((bm, K)).astype(np.float16))
             ob = [torch.empty((bm, N), dtype=torch.float16, device=dev) for _ in range(3)]
             bstep = lambda i: kaio.kaio_qkv_w4a16(xb, *sets[i % R][0], *sets[i % R][1], *ob)
-            bms = timed_graph(bstep, 4 * R, max(5, args.steps // 10), stream)
+            bms = timed_graph(bstep, 4 * R, replays, stream)
             bbytes = bm * K * 2 + sum(a.nbytes for a in dinp.w) + sum(a.nbytes for a in dinp.s) + 3 * bm * N * 2
             bgbs = bbytes / (bms * 1e-3) / 1e9
             btf = 2.0 * bm * N * K * 3 / (bms * 1e-3) / 1e12
@@ -334,6 +525,49 @@ def main():
                 "points": batched, "bound": "hbm"}
         del sets, x, outs
 
+    # ---- W8A16 sibling: decode (rotated) and prefill ----------------------------------
+    if args.only in ("all", "w8"):
+        c = workloads.QKV8_DECODE
+        M, N, K, R = c["M"], c["N"], c["K"], c["rotate"]
+        log(f"[bench] generating {R} W8A16 decode weight sets {M}x{N}x{K}")
+        d8 = workloads.qkv8_inputs(M, N, K, c["seed"])
+        x = t(d8.x)
+        sets = [([t(a) for a in d8.w], [t(a) for a in d8.s])]
+        for j in range(1, R):
+            wj, sj = workloads.qkv8_weight_set(N, K, c["seed"] + j)
+            sets.append(([t(a) for a in wj], [t(a) for a in sj]))
+        outs = [torch.empty((M, N), dtype=torch.float16, device=dev) for _ in range(3)]
+        dstep = lambda i: kaio.kaio_qkv_w8a16(x, *sets[i % R][0], *sets[i % R][1], *outs)
+        dms = timed_graph(dstep, 4 * R, replays, stream)
+        dbytes = d8.x.nbytes + sum(a.nbytes for a in d8.w) + sum(a.nbytes for a in d8.s) + 3 * M * N * 2
+        gbs = dbytes / (dms * 1e-3) / 1e9
+        log(f"[bench] W8A16 decode: {dms * 1e3:.2f} us/call, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of HBM)")
+        dstep(0)
+        torch.cuda.synchronize()
+        host["w8_decode"] = [o.cpu().numpy() for o in outs]
+        rr = read_roof(dbytes, R, replays, stream, dev)
+        secondary["qkv8_decode"] = {
+            "workload": "W8A16: x f16[8,4096], 3x u32[1024,4096] (INT8), 3x f16[32,4096]; 11 rotated weight "
+                        "sets, 44 calls per HIP graph replay",
+            "us_per_call": round(dms * 1e3, 3), "value": round(gbs, 1), "unit": "GB/s", "bound": "hbm",
+            "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": dbytes,
+            "read_roof": rr, "frac_of_read_roof": round(rr["us_per_call"] / (dms * 1e3), 4) if rr else None}
+        del sets, x, outs
+        c = workloads.QKV8_PREFILL
+        M, N, K = c["M"], c["N"], c["K"]
+        p8 = workloads.qkv8_inputs(M, N, K, c["seed"])
+        x, w, s = t(p8.x), [t(a) for a in p8.w], [t(a) for a in p8.s]
+        outs = [torch.empty((M, N), dtype=torch.float16, device=dev) for _ in range(3)]
+        pms, _ = timed(lambda i: kaio.kaio_qkv_w8a16(x, *w, *s, *outs), args.steps, args.warmup, stream)
+        ptf = 2.0 * M * N * K * 3 / (pms * 1e-3) / 1e12
+        log(f"[bench] W8A16 prefill: {pms * 1e3:.1f} us/call, {ptf:.1f} TFLOP/s")
+        host["w8_prefill"] = [o.cpu().numpy() for o in outs]
+        secondary["qkv8_prefill"] = {
+            "workload": "W8A16: x f16[2048,4096], 3x u32[1024,4096] (INT8), 3x f16[32,4096] -> Q,K,V f16[2048,4096]",
+            "us_per_call": round(pms * 1e3, 2), "value": round(ptf, 2), "unit": "TFLOP/s", "bound": "mfma",
+            "peak": PEAK_F16_TFLOPS, "frac": round(ptf / PEAK_F16_TFLOPS, 4)}
+        del x, w, s, outs
+
     # ---- dense GEMM ------------------------------------------------------------------------
     if args.only in ("all", "gemm"):
         c = workloads.GEMM_4096
@@ -344,12 +578,14 @@ def main():
         gms, _ = timed(lambda i: kaio.kaio_gemm_f16f32(ad, bd, cd), max(10, args.steps // 2), 3, stream)
         gtf = 2.0 * M * N * K / (gms * 1e-3) / 1e12
         log(f"[bench] gemm 4096^3: {gms * 1e3:.1f} us/call, {gtf:.1f} TFLOP/s")
+        host["gemm"] = cd.cpu().numpy()
         secondary["gemm_f16f32"] = {"workload": "A f16[4096,4096] x B f16[4096,4096] -> C f32",
                                     "us_per_call": round(gms * 1e3, 2), "value": round(gtf, 2),
                                     "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_F16_TFLOPS,
                                     "frac": round(gtf / PEAK_F16_TFLOPS, 4)}
         # backward of the same product: grad f32[M,N] -> grad_a f16[M,K], grad_b f16[K,N]
-        gd = t(np.random.default_rng(c["seed"] + 1).standard_normal((M, N)).astype(np.float32))
+        g = np.random.default_rng(c["seed"] + 1).standard_normal((M, N)).astype(np.float32)
+        gd = t(g)
         gad = torch.empty((M, K), dtype=torch.float16, device=dev)
         gbd = torch.empty((K, N), dtype=torch.float16, device=dev)
         wsd = torch.empty((kaio.lib().kaio_gemm_f16f32_bwd_workspace_size(M, N),), dtype=torch.uint8, device=dev)
@@ -357,6 +593,8 @@ def main():
                        max(10, args.steps // 2), 3, stream)
         btf = 4.0 * M * N * K / (bms * 1e-3) / 1e12
         log(f"[bench] gemm bwd 4096^3: {bms * 1e3:.1f} us/call, {btf:.1f} TFLOP/s")
+        host["gemm_bwd"] = (gad.cpu().numpy(), gbd.cpu().numpy(), g)
+        host["gemm_ab"] = (a, b)
         secondary["gemm_f16f32_bwd"] = {
             "workload": "grad f32[4096,4096] -> grad_a = f16(grad) . B^T, grad_b = A^T . f16(grad), f16 outputs "
                         "(cast + two GEMM launches)",
@@ -364,7 +602,7 @@ def main():
             "peak": PEAK_F16_TFLOPS, "frac": round(btf / PEAK_F16_TFLOPS, 4)}
         del ad, bd, cd, gd, gad, gbd, wsd
 
-    # ---- dequant backward --------------------------------------------------------------------
+    # ---- dequant backward, and a plain copy of the same bytes ---------------------------------
     if args.only in ("all", "bwd"):
         c = workloads.DEQUANT_BWD
         for dt, tdt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
@@ -380,10 +618,18 @@ def main():
             nbytes = 2 * dy.nbytes + sc.nbytes
             gbs = nbytes / (bms * 1e-3) / 1e9
             log(f"[bench] dequant bwd {dt}: {bms * 1e3:.1f} us/call, {gbs:.0f} GB/s")
+            host[f"bwd_{dt}"] = (dy, sc, dqd.view(torch.int16).cpu().numpy().view(np.uint16) if dt == "bf16"
+                                 else dqd.cpu().numpy())
+            cpy = torch.empty_like(dyd)
+            cms, _ = timed(lambda i: cpy.copy_(dyd), max(10, args.steps // 2), 3, stream)
+            cgbs = 2 * dy.nbytes / (cms * 1e-3) / 1e9
+            del cpy
             secondary[f"dequant_group_bwd_{dt}"] = {
                 "workload": f"dy, dq {dt}[16384,8192], scale [16384,64], g=128",
                 "us_per_call": round(bms * 1e3, 2), "value": round(gbs, 1), "unit": "GB/s", "bound": "hbm",
-                "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes}
+                "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes,
+                "copy_roof": {"us_per_call": round(cms * 1e3, 2), "gbs": round(cgbs, 1),
+                              "what": "torch copy_ of dy into a buffer like dq (same bytes read and written, scales aside)"}}
             del dyd, scd, dqd
 
     if args.copy_calibration:
@@ -398,9 +644,90 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+        cpu_leg(result, secondary, host, inp, workloads)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+
+
+def cpu_leg(result, secondary, host, inp, workloads):
+    """The oracle on every workload the GPU ran: its time on this host next to each GPU
+    figure, and a comparison of its full results with the GPU's."""
+    import numpy as np
+    from oracle import compare
+    from oracle.dequant_bwd import dequant_bwd
+    from oracle.gemm import gemm
+    from oracle.gemm_bwd import gemm_bwd
+    from oracle.qkv import qkv_project
+
+    if "prefill" in host:
+        result["roofline"]["parity"] = qkv_parity(host["prefill"], inp)
+        log(f"[bench] prefill parity (all outputs): {result['roofline']['parity']}")
+    # tiny QKV: the oracle only (the GPU side is latency, covered by the tests)
+    c = workloads.QKV_TINY
+    tin = workloads.qkv_inputs(c["M"], c["N"], c["K"], c["seed"])
+    sec, _ = best_of(lambda: qkv_project(tin.x, tin.w, tin.s, with_abs=False), 3)
+    secondary["qkv_tiny_cpu_oracle"] = oracle_entry(2.0 * c["M"] * c["N"] * c["K"] * 3 / sec / 1e9, "GFLOP/s", sec,
+                                                   "tiny QKV 16x512x512, full problem, best of 3")
+    if "decode" in host:
+        c = workloads.QKV_DECODE
+        dinp = workloads.qkv_inputs(c["M"], c["N"], c["K"], c["seed"])
+        sec, _ = best_of(lambda: qkv_project(dinp.x, dinp.w, dinp.s, with_abs=False), 3)
+        d = secondary["qkv_decode"]
+        d["cpu_oracle"] = oracle_entry(d["algorithmic_bytes"] / sec / 1e9, "GB/s", sec,
+                                       "decode 8x4096x4096 (weight set 0), full problem, best of 3")
+        d["parity"] = qkv_parity(host["decode"], dinp)
+    if "w8_decode" in host:
+        c = workloads.QKV8_DECODE
+        d8 = workloads.qkv8_inputs(c["M"], c["N"], c["K"], c["seed"])
+        sec, _ = best_of(lambda: qkv_project(d8.x, d8.w, d8.s, with_abs=False, bits=8), 3)
+        d = secondary["qkv8_decode"]
+        d["cpu_oracle"] = oracle_entry(d["algorithmic_bytes"] / sec / 1e9, "GB/s", sec,
+                                       "W8A16 decode 8x4096x4096 (weight set 0), full problem, best of 3")
+        d["parity"] = qkv_parity(host["w8_decode"], d8, bits=8)
+    if "w8_prefill" in host:
+        c = workloads.QKV8_PREFILL
+        p8 = workloads.qkv8_inputs(c["M"], c["N"], c["K"], c["seed"])
+        sec, _ = best_of(lambda: qkv_project(p8.x, p8.w, p8.s, with_abs=False, bits=8), 1)
+        d = secondary["qkv8_prefill"]
+        d["cpu_oracle"] = oracle_entry(2.0 * c["M"] * c["N"] * c["K"] * 3 / sec / 1e12, "TFLOP/s", sec,
+                                       "W8A16 prefill 2048x4096x4096, full problem (Y only), one run")
+        d["parity"] = qkv_parity(host["w8_prefill"], p8, bits=8)
+    if "gemm" in host:
+        a, b = host["gemm_ab"]
+        sec, (cref, tref) = best_of(lambda: gemm(a, b), 1)
+        d = secondary["gemm_f16f32"]
+        d["cpu_oracle"] = oracle_entry(2.0 * a.shape[0] * b.shape[1] * a.shape[1] / sec / 1e12, "TFLOP/s", sec,
+                                       "GEMM 4096^3, full problem (C and sum |a*b|), one run")
+        bad, worst = compare.excess(host["gemm"], cref, compare.gemm_tolerance(tref))
+        with np.errstate(divide="ignore", invalid="ignore"):
+            rel = np.where(tref > 0, np.abs(host["gemm"].astype(np.float64) - cref) / tref, 0.0)
+        d["parity"] = {"checked": int(cref.size), "violations": bad, "max_ratio_to_tol": round(worst, 5),
+                       "max_abs_diff_over_T": float(rel.max())}
+        del cref, tref, rel
+        ga, gb, g = host["gemm_bwd"]
+        sec, ((da, ta), (db, tb)) = best_of(lambda: gemm_bwd(a, b, g), 1)
+        d = secondary["gemm_f16f32_bwd"]
+        d["cpu_oracle"] = oracle_entry(4.0 * a.shape[0] * b.shape[1] * a.shape[1] / sec / 1e12, "TFLOP/s", sec,
+                                       "GEMM backward 4096^3, full problem (both gradients and their T), one run")
+        bads, worsts = 0, 0.0
+        for got, y, tt in ((ga, da, ta), (gb, db, tb)):
+            bb, ww = compare.excess(got, y, compare.f16_tolerance(y, tt))
+            bads, worsts = bads + bb, max(worsts, ww)
+        d["parity"] = {"checked": int(da.size + db.size), "violations": bads, "max_ratio_to_tol": round(worsts, 4)}
+    for dt in ("f32", "bf16"):
+        if f"bwd_{dt}" not in host:
+            continue
+        dy, sc, got = host[f"bwd_{dt}"]
+        rows = 2048                      # a bounded sample of rows: the f64 oracle takes ~1 s per 2048
+        sec, ref = best_of(lambda: dequant_bwd(dy[:rows], sc[:rows], 128, dt), 1)
+        d = secondary[f"dequant_group_bwd_{dt}"]
+        nbytes = 2 * dy[:rows].nbytes + sc[:rows].nbytes
+        d["cpu_oracle"] = oracle_entry(nbytes / sec / 1e9, "GB/s", sec,
+                                       f"rows 0..{rows - 1} of the 16384-row workload, one run")
+        eq = compare.bits_equal(got[:rows], ref)
+        d["parity"] = {"checked": int(eq.size), "bit_exact": bool(eq.all()),
+                       "note": "the tests compare all 134.2 M elements; the bench re-checks the timed sample"}
 
 
 if __name__ == "__main__":

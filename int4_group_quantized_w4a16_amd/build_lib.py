@@ -15,6 +15,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkaio.so")
 SOURCES = ["kaio_abi.cpp", "qkv_prefill.hip", "qkv_decode.hip", "gemm_f16f32.hip", "dequant_group_bwd.hip"]
+# measurement aid for the benchmark (a plain streaming read), a library of its own
+ROOF_LIB = os.path.join(PKG, "libkaio_roof.so")
+ROOF_SOURCES = ["roof.hip"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -40,19 +43,26 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra_flags=(), verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link libkaio.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(extra_flags=(), verbose: bool = False) -> str:
+    """Compile every source for gfx950, link libkaio.so (and the benchmark's
+    libkaio_roof.so); returns the path of libkaio.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + ROOF_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], ROOF_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {ROOF_LIB}")
     return LIB
 
 

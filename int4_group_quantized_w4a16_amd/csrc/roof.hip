@@ -1,0 +1,108 @@
+// Measurement aid, not an operation of the library: a plain streaming read of
+// device memory, the reference an HBM-bound kernel of the same bytes is
+// weighed against.
+//
+// Every thread issues all of its U 16-byte loads before it uses any of them
+// (so the whole grid's bytes are in flight at once, as in the decode kernel),
+// then XORs them.  The result is stored only if it equals a value the data is
+// never built to produce, which keeps the loads live without adding writes.
+// Chunk c of workgroup b, load u: index (b * U + u) * THREADS + tid -- each
+// wave-wide load covers 1 KiB contiguous.
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/kaio_roof.h"
+
+namespace {
+
+template <int U, int THREADS>
+__global__ void __launch_bounds__(THREADS) stream_read_kernel(const uint4* __restrict__ src, size_t n16,
+                                                              uint32_t* __restrict__ sink) {
+  const size_t base = (size_t)blockIdx.x * U * THREADS + threadIdx.x;
+  uint4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const size_t i = base + (size_t)u * THREADS;
+    v[u] = i < n16 ? src[i] : uint4{0u, 0u, 0u, 0u};
+  }
+  uint32_t acc = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  if (acc == 0x9E3779B9u) sink[(size_t)blockIdx.x * THREADS + threadIdx.x] = acc;
+}
+
+// One lane reads the shader-clock counter (s_memtime) and the constant-rate
+// real-time counter (s_memrealtime) at its start, sleeps in short steps until
+// the real-time counter has advanced by `ticks` (or a step limit is reached),
+// reads both again and stores the four values.  The ratio of the two deltas,
+// times the real-time counter's rate, is the average shader clock of its
+// compute unit over that window.  It needs one wave slot and no LDS, so it
+// can run beside another kernel's workgroups.
+__global__ void __launch_bounds__(64) clock_probe_kernel(unsigned long long* __restrict__ out,
+                                                         unsigned long long ticks) {
+  if (threadIdx.x != 0) return;
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  const unsigned long long c0 = __builtin_amdgcn_s_memtime();
+  unsigned long long r1 = r0, c1 = c0;
+  for (uint32_t step = 0; step < (1u << 24) && r1 - r0 < ticks; ++step) {
+    __builtin_amdgcn_s_sleep(8);
+    r1 = __builtin_amdgcn_s_memrealtime();
+    c1 = __builtin_amdgcn_s_memtime();
+  }
+  out[4 * blockIdx.x + 0] = c1 - c0;
+  out[4 * blockIdx.x + 1] = r1 - r0;
+  out[4 * blockIdx.x + 2] = r0;
+  out[4 * blockIdx.x + 3] = r1;
+}
+
+template <int U, int THREADS>
+int launch(const void* src, size_t bytes, void* sink, hipStream_t stream) {
+  const size_t n16 = bytes / 16;
+  const size_t per = (size_t)U * THREADS;
+  const size_t blocks = (n16 + per - 1) / per;
+  if (blocks == 0 || blocks > (1u << 24)) return 2;
+  hipLaunchKernelGGL((stream_read_kernel<U, THREADS>), dim3((uint32_t)blocks), dim3(THREADS), 0, stream,
+                     static_cast<const uint4*>(src), n16, static_cast<uint32_t*>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kaio_roof_sink_bytes(size_t bytes, int loads_per_thread, int threads) {
+  if (loads_per_thread <= 0 || threads <= 0) return 0;
+  const size_t per = (size_t)loads_per_thread * threads;
+  return ((bytes / 16 + per - 1) / per) * threads * 4;
+}
+
+int kaio_roof_stream_read(const void* src, size_t bytes, void* sink, int loads_per_thread, int threads,
+                          void* stream) {
+  if (!src || !sink || bytes % 16 || (reinterpret_cast<uintptr_t>(src) & 15)) return 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+#define KAIO_ROOF_CASE(U, T) \
+  if (loads_per_thread == U && threads == T) return launch<U, T>(src, bytes, sink, s);
+  KAIO_ROOF_CASE(1, 256) KAIO_ROOF_CASE(2, 256) KAIO_ROOF_CASE(4, 256) KAIO_ROOF_CASE(8, 256)
+  KAIO_ROOF_CASE(16, 256) KAIO_ROOF_CASE(4, 512) KAIO_ROOF_CASE(8, 512) KAIO_ROOF_CASE(16, 512)
+  KAIO_ROOF_CASE(4, 1024) KAIO_ROOF_CASE(8, 1024) KAIO_ROOF_CASE(16, 1024)
+#undef KAIO_ROOF_CASE
+  return 2;
+}
+
+int kaio_roof_clock_probe(void* out, unsigned long long ticks, void* stream) {
+  if (!out || (reinterpret_cast<uintptr_t>(out) & 7)) return 1;
+  hipLaunchKernelGGL(clock_probe_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                     static_cast<unsigned long long*>(out), ticks);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+int kaio_roof_wall_clock_khz(void) {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0;
+  return khz;
+}
+
+}  // extern "C"

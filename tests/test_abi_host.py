@@ -30,10 +30,28 @@ def gpu_visible():
 no_gpu_only = pytest.mark.skipif(gpu_visible(), reason="fake pointers would reach a real launch")
 
 
-def declared_functions():
-    src = open(HEADER).read()
+def declared_functions(header=HEADER):
+    src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(kaio_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_measurement_library_exports_its_header():
+    # libkaio_roof.so: the benchmark's plain-read and clock-probe kernels (not libkaio's ABI)
+    header = os.path.join(os.path.dirname(HEADER), "kaio_roof.h")
+    names = declared_functions(header)
+    assert set(names) == {"kaio_roof_stream_read", "kaio_roof_sink_bytes", "kaio_roof_clock_probe",
+                          "kaio_roof_wall_clock_khz"}
+    L = ctypes.CDLL(os.path.join(os.path.dirname(kaio.LIB_PATH), "libkaio_roof.so"))
+    for n in names:
+        assert hasattr(L, n), n
+    L.kaio_roof_sink_bytes.restype = ctypes.c_size_t
+    L.kaio_roof_sink_bytes.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.c_int]
+    assert L.kaio_roof_sink_bytes(16 * 256 * 4 * 3 + 16, 4, 256) == 4 * 256 * 4
+    L.kaio_roof_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_void_p]
+    assert L.kaio_roof_stream_read(A, 100, A + STEP, 4, 256, None) == 1      # not a multiple of 16
+    assert L.kaio_roof_stream_read(A, 1024, A + STEP, 3, 256, None) == 2     # unsupported shape
 
 
 def test_every_declared_symbol_is_exported():
