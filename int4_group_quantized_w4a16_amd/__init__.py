@@ -21,7 +21,9 @@ __all__ = ["DTYPE_CODES", "KaioError", "kaio_qkv_w4a16", "kaio_qkv_w8a16", "kaio
            "kaio_dequant_group_bwd",
            "kaio_last_error", "kaio_version", "lib", "LIB_PATH", "GROUP_SIZE"]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkaio.so")
+# KAIO_LIBRARY may name another in-tree build of the same library (the host-sanitizer
+# build used by the CPU boundary tests); by default the in-tree libkaio.so is loaded.
+LIB_PATH = os.environ.get("KAIO_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkaio.so")
 GROUP_SIZE = 128
 
 STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "INVALID_PROBLEM", 3: "UNSUPPORTED", 4: "DEVICE", 5: "LAUNCH"}

@@ -312,15 +312,22 @@ kaio_status kaio_dequant_group_bwd(kaio_dtype dtype, int32_t outer, int32_t axis
   static const char* op = "dequant_group_bwd";
   (void)workspace;
   (void)workspace_bytes;
+  // A C caller may pass any int here.  In C++ reading an enum object that holds a value
+  // outside the enumeration's range is undefined, so the code is taken from the
+  // parameter's bytes and only a validated code is turned back into a kaio_dtype.
+  static_assert(sizeof(kaio_dtype) == sizeof(int), "kaio_dtype is passed as an int");
+  int code = 0;
+  std::memcpy(&code, &dtype, sizeof code);
   size_t esz = 0;
-  switch (dtype) {
+  switch (code) {
     case KAIO_DTYPE_F32: esz = 4; break;
     case KAIO_DTYPE_BF16: esz = 2; break;
     case KAIO_DTYPE_F16: esz = 2; break;
     case KAIO_DTYPE_F64: esz = 8; break;
     default:
-      return fail(KAIO_ERR_UNSUPPORTED, op, "unsupported dtype %d (f32, bf16, f16, f64)", (int)dtype);
+      return fail(KAIO_ERR_UNSUPPORTED, op, "unsupported dtype %d (f32, bf16, f16, f64)", code);
   }
+  const kaio_dtype dt = static_cast<kaio_dtype>(code);
   if (outer < 0 || axis < 0)
     return fail(KAIO_ERR_INVALID_PROBLEM, op, "outer_size (%d) and axis_size (%d) must be non-negative",
                 outer, axis);
@@ -349,7 +356,7 @@ kaio_status kaio_dequant_group_bwd(kaio_dtype dtype, int32_t outer, int32_t axis
     return fail(KAIO_ERR_INVALID_ARGUMENT, op, "output %s overlaps %s", o->name, other->name);
   if (kaio_status st = check_device(op)) return st;
   (void)hipGetLastError();
-  return launched(op, kaio::launch_dequant_group_bwd(dtype, outer, axis, group_size, dy, scale, dq,
+  return launched(op, kaio::launch_dequant_group_bwd(dt, outer, axis, group_size, dy, scale, dq,
                                                      static_cast<hipStream_t>(stream)));
 }
 

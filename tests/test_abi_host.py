@@ -42,7 +42,7 @@ def test_measurement_library_exports_its_header():
     names = declared_functions(header)
     assert set(names) == {"kaio_roof_stream_read", "kaio_roof_sink_bytes", "kaio_roof_clock_probe",
                           "kaio_roof_wall_clock_khz"}
-    L = ctypes.CDLL(os.path.join(os.path.dirname(kaio.LIB_PATH), "libkaio_roof.so"))
+    L = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(kaio.__file__)), "libkaio_roof.so"))
     for n in names:
         assert hasattr(L, n), n
     L.kaio_roof_sink_bytes.restype = ctypes.c_size_t
