@@ -68,6 +68,8 @@ def condition(fn, ms=CONDITION_MS):
     work before its warm-up and timed steps, so that the timed steps measure
     the sustained rate of the kernel, not the power ramp."""
     import torch
+    fn(0)                       # a first call may load code; it is not part of the estimate
+    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(3):
@@ -386,6 +388,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-roof", action="store_true",
+                    help="skip the plain-read and copy ceilings (for profiler runs)")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "batched", "w8", "gemm", "bwd"], default="all")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy (reference for HBM byte counters)")
@@ -402,7 +406,7 @@ def main():
         key, src, fdir, wdir = args.write_traffic
         write_traffic(key, src, fdir, wdir,
                       f"rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -d <dir> -o run -- python3 bench.py "
-                      f"--only {key.split('_')[1]} --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration")
+                      f"--only {key.split('_')[1]} --steps 3 --warmup 1 --no-cpu-baseline --no-roof --copy-calibration")
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library has no "
@@ -494,7 +498,7 @@ def main():
         dstep(0)
         torch.cuda.synchronize()
         host["decode"] = [o.cpu().numpy() for o in outs]
-        rr = read_roof(dbytes, R, replays, stream, dev)
+        rr = None if args.no_roof else read_roof(dbytes, R, replays, stream, dev)
         if rr:
             log(f"[bench] plain read of the same {dbytes} bytes: {rr['us_per_call']:.2f} us/call, {rr['gbs']:.0f} GB/s")
         secondary["qkv_decode"] = {
@@ -545,7 +549,7 @@ def main():
         dstep(0)
         torch.cuda.synchronize()
         host["w8_decode"] = [o.cpu().numpy() for o in outs]
-        rr = read_roof(dbytes, R, replays, stream, dev)
+        rr = None if args.no_roof else read_roof(dbytes, R, replays, stream, dev)
         secondary["qkv8_decode"] = {
             "workload": "W8A16: x f16[8,4096], 3x u32[1024,4096] (INT8), 3x f16[32,4096]; 11 rotated weight "
                         "sets, 44 calls per HIP graph replay",
@@ -620,16 +624,18 @@ def main():
             log(f"[bench] dequant bwd {dt}: {bms * 1e3:.1f} us/call, {gbs:.0f} GB/s")
             host[f"bwd_{dt}"] = (dy, sc, dqd.view(torch.int16).cpu().numpy().view(np.uint16) if dt == "bf16"
                                  else dqd.cpu().numpy())
-            cpy = torch.empty_like(dyd)
-            cms, _ = timed(lambda i: cpy.copy_(dyd), max(10, args.steps // 2), 3, stream)
-            cgbs = 2 * dy.nbytes / (cms * 1e-3) / 1e9
-            del cpy
+            cms = None
+            if not args.no_roof:
+                cpy = torch.empty_like(dyd)
+                cms, _ = timed(lambda i: cpy.copy_(dyd), max(10, args.steps // 2), 3, stream)
+                del cpy
             secondary[f"dequant_group_bwd_{dt}"] = {
                 "workload": f"dy, dq {dt}[16384,8192], scale [16384,64], g=128",
                 "us_per_call": round(bms * 1e3, 2), "value": round(gbs, 1), "unit": "GB/s", "bound": "hbm",
                 "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes,
-                "copy_roof": {"us_per_call": round(cms * 1e3, 2), "gbs": round(cgbs, 1),
-                              "what": "torch copy_ of dy into a buffer like dq (same bytes read and written, scales aside)"}}
+                "copy_roof": None if cms is None else {
+                    "us_per_call": round(cms * 1e3, 2), "gbs": round(2 * dy.nbytes / (cms * 1e-3) / 1e9, 1),
+                    "what": "torch copy_ of dy into a buffer like dq (same bytes read and written, scales aside)"}}
             del dyd, scd, dqd
 
     if args.copy_calibration:
