@@ -56,8 +56,20 @@ constexpr int GCHUNK = KAIO_DECODE_GCHUNK;    // groups loaded per pass of a wav
 
 template <int V> struct WordVec;
 template <> struct WordVec<1> { using T = uint32_t; };
-template <> struct WordVec<2> { using T = uint2; };
-template <> struct WordVec<4> { using T = uint4; };
+template <> struct WordVec<2> { using T = u32x2; };
+template <> struct WordVec<4> { using T = u32x4; };
+
+// Packed weights that one wave alone reads (rows not split across waves) carry
+// the non-temporal hint: they stream past the caches instead of displacing the
+// small x that every workgroup re-reads (n = k = 4096: m = 8 7.94 -> 7.37 us,
+// m = 16 8.94 -> 8.25, m = 32 12.37 -> 11.76).  When RSPLIT waves read the
+// same words (m > 32) the hint would defeat that reuse (m = 128: +6%), and
+// the scales are faster without it.
+template <bool kOnce, typename T>
+__device__ __forceinline__ T load_w(const T* p) {
+  if constexpr (kOnce) return __builtin_nontemporal_load(p);
+  else return *p;
+}
 template <int V> struct HalfVec { typedef uint16_t T __attribute__((ext_vector_type(V))); };
 template <> struct HalfVec<1> { typedef uint16_t T; };
 
@@ -171,11 +183,11 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
         for (int j = 0; j < WPK; ++j) {
           const size_t roff = ((size_t)g * PR + ks * 4 * WPK + j) * N;
           if (kFull) {
-            const WV v = *reinterpret_cast<const WV*>(wlane + roff);
+            const WV v = load_w<RSPLIT == 1>(reinterpret_cast<const WV*>(wlane + roff));
             __builtin_memcpy(c.wv[gi][ks][j], &v, sizeof(v));
           } else {
 #pragma unroll
-            for (int t = 0; t < VEC; ++t) c.wv[gi][ks][j][t] = (colv + t < N) ? wlane[roff + t] : 0u;
+            for (int t = 0; t < VEC; ++t) c.wv[gi][ks][j][t] = (colv + t < N) ? load_w<RSPLIT == 1>(wlane + roff + t) : 0u;
           }
         }
       if (kFull) {
