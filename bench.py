@@ -269,7 +269,9 @@ def roof_lib():
     return L
 
 
-READ_SHAPES = ((1, 256), (2, 256), (4, 256), (8, 256), (16, 256), (4, 512), (8, 512), (8, 1024))
+# (loads per thread, threads); a negative count: the same shape with non-temporal loads
+READ_SHAPES = ((1, 256), (2, 256), (4, 256), (8, 256), (8, 1024), (-1, 256), (-2, 256), (-4, 256), (-8, 256),
+               (-8, 1024))
 
 
 def read_roof(nbytes, sets, replays, stream, dev):
@@ -297,7 +299,8 @@ def read_roof(nbytes, sets, replays, stream, dev):
     del bufs
     ms, u, th = best
     return {"us_per_call": round(ms * 1e3, 3), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
-            "bytes": nbytes, "launch": f"{u} x 16-byte loads per thread, {th} threads per workgroup",
+            "bytes": nbytes, "launch": f"{abs(u)} x 16-byte loads per thread{' (non-temporal)' if u < 0 else ''}, "
+                                       f"{th} threads per workgroup",
             "shapes_tried": len(READ_SHAPES)}
 
 

@@ -21,7 +21,8 @@ extern "C" {
  * loads before using any.  Nothing is written in practice; `sink` must be a
  * device buffer of kaio_roof_sink_bytes(bytes, loads_per_thread, threads)
  * bytes all the same (the kernel may store there).  Supported
- * (loads_per_thread, threads): (1|2|4|8|16, 256), (4|8|16, 512), (4|8|16, 1024).
+ * (loads_per_thread, threads): (1|2|4|8|16, 256), (4|8|16, 512), (4|8|16, 1024); a
+ * negative loads_per_thread selects the same shape with non-temporal loads.
  * Returns 0 on a queued launch, 1 for a bad pointer or size, 2 for an
  * unsupported shape, 3 if the launch failed.
  */

@@ -17,15 +17,21 @@
 
 namespace {
 
-template <int U, int THREADS>
-__global__ void __launch_bounds__(THREADS) stream_read_kernel(const uint4* __restrict__ src, size_t n16,
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// NT: the loads carry the non-temporal hint (stream past the caches).
+template <int U, int THREADS, bool NT>
+__global__ void __launch_bounds__(THREADS) stream_read_kernel(const u32x4_t* __restrict__ src, size_t n16,
                                                               uint32_t* __restrict__ sink) {
   const size_t base = (size_t)blockIdx.x * U * THREADS + threadIdx.x;
-  uint4 v[U];
+  u32x4_t v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const size_t i = base + (size_t)u * THREADS;
-    v[u] = i < n16 ? src[i] : uint4{0u, 0u, 0u, 0u};
+    if (i < n16)
+      v[u] = NT ? __builtin_nontemporal_load(src + i) : src[i];
+    else
+      v[u] = u32x4_t{0u, 0u, 0u, 0u};
   }
   uint32_t acc = 0;
 #pragma unroll
@@ -58,13 +64,17 @@ __global__ void __launch_bounds__(64) clock_probe_kernel(unsigned long long* __r
 }
 
 template <int U, int THREADS>
-int launch(const void* src, size_t bytes, void* sink, hipStream_t stream) {
+int launch(const void* src, size_t bytes, void* sink, bool nt, hipStream_t stream) {
   const size_t n16 = bytes / 16;
   const size_t per = (size_t)U * THREADS;
   const size_t blocks = (n16 + per - 1) / per;
   if (blocks == 0 || blocks > (1u << 24)) return 2;
-  hipLaunchKernelGGL((stream_read_kernel<U, THREADS>), dim3((uint32_t)blocks), dim3(THREADS), 0, stream,
-                     static_cast<const uint4*>(src), n16, static_cast<uint32_t*>(sink));
+  if (nt)
+    hipLaunchKernelGGL((stream_read_kernel<U, THREADS, true>), dim3((uint32_t)blocks), dim3(THREADS), 0, stream,
+                       static_cast<const u32x4_t*>(src), n16, static_cast<uint32_t*>(sink));
+  else
+    hipLaunchKernelGGL((stream_read_kernel<U, THREADS, false>), dim3((uint32_t)blocks), dim3(THREADS), 0, stream,
+                       static_cast<const u32x4_t*>(src), n16, static_cast<uint32_t*>(sink));
   return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 
@@ -73,7 +83,8 @@ int launch(const void* src, size_t bytes, void* sink, hipStream_t stream) {
 extern "C" {
 
 size_t kaio_roof_sink_bytes(size_t bytes, int loads_per_thread, int threads) {
-  if (loads_per_thread <= 0 || threads <= 0) return 0;
+  if (loads_per_thread < 0) loads_per_thread = -loads_per_thread;
+  if (loads_per_thread == 0 || threads <= 0) return 0;
   const size_t per = (size_t)loads_per_thread * threads;
   return ((bytes / 16 + per - 1) / per) * threads * 4;
 }
@@ -82,8 +93,11 @@ int kaio_roof_stream_read(const void* src, size_t bytes, void* sink, int loads_p
                           void* stream) {
   if (!src || !sink || bytes % 16 || (reinterpret_cast<uintptr_t>(src) & 15)) return 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // a negative count selects the same shape with non-temporal loads
+  const bool nt = loads_per_thread < 0;
+  if (nt) loads_per_thread = -loads_per_thread;
 #define KAIO_ROOF_CASE(U, T) \
-  if (loads_per_thread == U && threads == T) return launch<U, T>(src, bytes, sink, s);
+  if (loads_per_thread == U && threads == T) return launch<U, T>(src, bytes, sink, nt, s);
   KAIO_ROOF_CASE(1, 256) KAIO_ROOF_CASE(2, 256) KAIO_ROOF_CASE(4, 256) KAIO_ROOF_CASE(8, 256)
   KAIO_ROOF_CASE(16, 256) KAIO_ROOF_CASE(4, 512) KAIO_ROOF_CASE(8, 512) KAIO_ROOF_CASE(16, 512)
   KAIO_ROOF_CASE(4, 1024) KAIO_ROOF_CASE(8, 1024) KAIO_ROOF_CASE(16, 1024)
