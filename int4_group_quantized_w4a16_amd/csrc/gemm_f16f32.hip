@@ -193,9 +193,7 @@ gemm_f16f32_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
 // lane i gets B[k0 + j][i] for j = 0..3: four consecutive k of its column,
 // and two such reads make its eight-k MFMA B operand.
 //   A tile [256][64]: chunk kc of row r at slot r*8 + (kc ^ (r & 7)).
-//   B tile [64][256]: chunk c of k-row r at slot r*32 + (c ^ 2(r & 3)); the
-//   four k-rows a transposing read touches then sit in four different
-//   32-byte bank groups.
+//   B tile [64][256]: chunk c of k-row r at slot r*32 + (c ^ tr_swz(r)).
 // ---------------------------------------------------------------------------
 #define KAIO_GEMM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 #define KAIO_GEMM_GLOBAL(p) ((__attribute__((address_space(1))) const void*)(p))
@@ -236,8 +234,18 @@ __device__ __forceinline__ uint32_t vgpr_u32(uint32_t o) {
 //     i*4 + (kc ^ ((i >> 2) & 3)) -- the 16 rows of one 16-byte fragment read
 //     fill one 256-byte pass of the banks; a fragment is one 16-byte read.
 //   kTr = true: stored [reduction][index] (index contiguous, row stride ld):
-//     LDS [32][32 chunks], chunk c of reduction row r at slot r*32 + (c ^ 2(r & 3));
+//     LDS [32][32 chunks], chunk c of reduction row r at slot r*32 + (c ^ tr_swz(r));
 //     a fragment is two transposing reads.
+// Chunk swizzle of the index-contiguous layout.  One transposing read of a
+// wave touches k-rows kb*8 + {0..3} (+4 for the second read) for kb = 0..3,
+// 32 bytes (two chunks) of each; the hardware serves 32 lanes (two kb) per
+// pass.  2(r & 3) moves rows r and r+1..r+3 to different chunk pairs, and
+// 8((r >> 3) & 1) moves rows kb*8 + j and (kb+1)*8 + j apart, so the 16 chunk
+// slots of one pass fall in 16 distinct 16-byte bank groups.  (Without the
+// second term rows j and 8 + j shared their banks: two-way conflicts on
+// every transposing read.)
+__device__ __forceinline__ uint32_t tr_swz(uint32_t r) { return (2 * (r & 3)) ^ (8 * ((r >> 3) & 1)); }
+
 template <bool kTr>
 struct DmaOperand {
   // byte offset, within a half-stage's source window, of this lane's load i (0..3)
@@ -249,9 +257,18 @@ struct DmaOperand {
       const uint32_t rc = (idx0 + r < nidx) ? r : nidx - 1 - idx0;   // rows past the end repeat a valid one
       return (rc * ld + kc * 8) * 2;
     }
-    const uint32_t r = s >> 5, c = (s & 31) ^ (2 * (r & 3));
+    const uint32_t r = s >> 5, c = (s & 31) ^ tr_swz(r);
     const uint32_t cc = (idx0 + c * 8 < nidx) ? c * 8 : nidx - 8 - idx0;   // likewise for 8-index chunks
     return (r * ld + cc) * 2;
+  }
+  // reduction offset, within a 32-k half, of the first element of this lane's load i
+  __device__ static uint32_t lane_reduction(int i, uint32_t wave, uint32_t lane) {
+    const uint32_t s = (i * 4 + wave) * 64 + lane;
+    if (!kTr) {
+      const uint32_t r = s >> 2;
+      return ((s & 3) ^ ((r >> 2) & 3)) * 8;   // an 8-element chunk of one index row
+    }
+    return s >> 5;                            // one reduction row, 8 indices
   }
   __device__ static const char* tile_base(const uint16_t* p, uint32_t idx0, uint32_t ld) {
     return reinterpret_cast<const char*>(kTr ? p + idx0 : p + (size_t)idx0 * ld);
@@ -280,7 +297,7 @@ struct DmaOperand {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const uint32_t k = kb * 8 + (l16 >> 2) + 4 * hf;
-      const uint32_t off = (k * 32 + ((idx >> 3) ^ (2 * (k & 3)))) * 16 + ((idx >> 2) & 1) * 8;
+      const uint32_t off = (k * 32 + ((idx >> 3) ^ tr_swz(k))) * 16 + ((idx >> 2) & 1) * 8;
       h[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(st + off));
     }
     return __builtin_bit_cast(half8_t, (short __attribute__((ext_vector_type(8)))){
@@ -327,9 +344,15 @@ __device__ __forceinline__ void store_out(uint16_t* p, float v) { *p = __builtin
 // C[Mo, No] = sum over R of A-operand x B-operand, f32 accumulation; OutT is
 // float (f32 out) or uint16_t (f16 out, rounded to nearest even).  A is read
 // through DmaOperand<kATr> with row stride lda, B through DmaOperand<kBTr>
-// with row stride ldb.  Needs R % 64 == 0 and the strides and, for a
-// transposed operand, its index count multiples of 8.
-template <bool kATr, bool kBTr, typename OutT>
+// with row stride ldb.  Needs the strides and, for a transposed operand, its
+// index count multiples of 8, and R % 64 == 0 -- or, with kRagged, any R
+// (R % 8 == 0 for an operand stored reduction-contiguous): the last stage's
+// chunks past R are then zero.  A lane whose chunk starts at or past R
+// points its direct load past the end of the descriptor's range, and a
+// buffer load out of range returns zeros, which land in LDS like data.  No
+// load is skipped, so every wave still issues exactly 8 loads per half-stage
+// and the fixed vmcnt waits below stay exact.
+template <bool kATr, bool kBTr, typename OutT, bool kRagged>
 __global__ void __launch_bounds__(THREADS, 1)
 gemm_dma_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __restrict__ B, uint32_t ldb,
                 OutT* __restrict__ C, uint32_t Mo, uint32_t No, uint32_t R, uint32_t mtiles, uint32_t ntiles) {
@@ -346,12 +369,18 @@ gemm_dma_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
   tile_of<KAIO_GEMM_SM, KAIO_GEMM_SN>(blockIdx.x, gridDim.x, mtiles, ntiles, tm, tn);
   const uint32_t m0 = tm * BM, n0 = tn * BN;
 
-  uint32_t aoff[4], boff[4];
+  uint32_t aoff[4], boff[4], ared[4], bred[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     aoff[i] = OA::lane_offset(i, wave, lane, m0, Mo, lda);
     boff[i] = OB::lane_offset(i, wave, lane, n0, No, ldb);
+    ared[i] = OA::lane_reduction(i, wave, lane);
+    bred[i] = OB::lane_reduction(i, wave, lane);
   }
+  // kRagged: descriptors span 2 GiB (every in-bounds lane offset is below
+  // 2^31, by the host-side size limits); kOutOfRange lies past that
+  constexpr int kRange = kRagged ? 0x7FFFFFF0 : -1;
+  constexpr uint32_t kOutOfRange = 0x80000000u;
   const char* abase = OA::tile_base(A, m0, lda);
   const char* bbase = OB::tile_base(B, n0, ldb);
   const size_t ahalf = OA::half_stride(lda), bhalf = OB::half_stride(ldb);
@@ -369,15 +398,19 @@ gemm_dma_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
     uint4* st = hbuf(kt, h);
     const uint32_t hk = 2 * kt + h;   // 32-k half index
     if (j < 4) {
+      uint32_t off = aoff[j];
+      if (kRagged && 32 * hk + ared[j] >= R) off = kOutOfRange;
       const __amdgpu_buffer_rsrc_t r =
-          __builtin_amdgcn_make_buffer_rsrc((void*)sgpr_ptr(abase + hk * ahalf), 0, -1, kBufferFlags);
+          __builtin_amdgcn_make_buffer_rsrc((void*)sgpr_ptr(abase + hk * ahalf), 0, kRange, kBufferFlags);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, KAIO_GEMM_LDS(st + (j * 4 + wave) * 64), 16,
-                                               vgpr_u32(aoff[j]), 0, 0, 0);
+                                               vgpr_u32(off), 0, 0, 0);
     } else {
+      uint32_t off = boff[j - 4];
+      if (kRagged && 32 * hk + bred[j - 4] >= R) off = kOutOfRange;
       const __amdgpu_buffer_rsrc_t r =
-          __builtin_amdgcn_make_buffer_rsrc((void*)sgpr_ptr(bbase + hk * bhalf), 0, -1, kBufferFlags);
+          __builtin_amdgcn_make_buffer_rsrc((void*)sgpr_ptr(bbase + hk * bhalf), 0, kRange, kBufferFlags);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, KAIO_GEMM_LDS(st + HSLOTS + ((j - 4) * 4 + wave) * 64), 16,
-                                               vgpr_u32(boff[j - 4]), 0, 0, 0);
+                                               vgpr_u32(off), 0, 0, 0);
     }
   };
   auto issue_half = [&](uint32_t kt, uint32_t h) {
@@ -435,7 +468,7 @@ gemm_dma_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
   // stage the loads reload consumed stages into their own buffers and the
   // reads of "the next stage" read a buffer whose contents go unused (no
   // branches around either).
-  const uint32_t nk = R / DBK;
+  const uint32_t nk = (R + DBK - 1) / DBK;
   // the epilogue's kernel arguments, loaded here rather than inside the loop,
   // where a pending scalar load would again force full LDS waits
   asm volatile("" ::"s"(C), "s"(Mo), "s"(No));
@@ -526,33 +559,13 @@ __global__ void fill_zero_kernel(uint4* __restrict__ dst, size_t n16, uint8_t* _
 
 }  // namespace
 
-hipError_t launch_gemm_f16f32(const uint16_t* a, const uint16_t* b, float* c,
-                              uint32_t m, uint32_t n, uint32_t k, hipStream_t stream) {
-  const uint32_t mtiles = (m + BM - 1) / BM;
-  const uint32_t ntiles = (n + BN - 1) / BN;
-  const dim3 grid(mtiles * ntiles), block(THREADS);
-  // DMA path: 32-bit per-lane byte offsets need 256 * k * 2 and 64 * n * 2 below 2^31
-  if (k > 0 && k % DBK == 0 && n % 8 == 0 && k < (1u << 22) && n < (1u << 24)) {
-    const size_t lds = (size_t)8 * HSLOTS * 16;
-    auto* kern = &gemm_dma_kernel<false, true, float>;
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(kern, grid, block, lds, stream, a, k, b, n, c, m, n, k, mtiles, ntiles);
-  } else if (k % 8 == 0 && n % 8 == 0)
-    hipLaunchKernelGGL(gemm_f16f32_kernel<true>, grid, block, 0, stream, a, b, c, m, n, k, mtiles);
-  else
-    hipLaunchKernelGGL(gemm_f16f32_kernel<false>, grid, block, 0, stream, a, b, c, m, n, k, mtiles);
-  return hipGetLastError();
-}
-
 namespace {
-template <bool kATr, bool kBTr>
-hipError_t launch_dma_f16out(const uint16_t* a, uint32_t lda, const uint16_t* b, uint32_t ldb, uint16_t* c,
-                             uint32_t mo, uint32_t no, uint32_t r, hipStream_t stream) {
+template <bool kATr, bool kBTr, typename OutT, bool kRagged>
+hipError_t launch_dma(const uint16_t* a, uint32_t lda, const uint16_t* b, uint32_t ldb, OutT* c, uint32_t mo,
+                      uint32_t no, uint32_t r, hipStream_t stream) {
   const uint32_t mtiles = (mo + BM - 1) / BM, ntiles = (no + BN - 1) / BN;
   const size_t lds = (size_t)8 * HSLOTS * 16;
-  auto* kern = &gemm_dma_kernel<kATr, kBTr, uint16_t>;
+  auto* kern = &gemm_dma_kernel<kATr, kBTr, OutT, kRagged>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
@@ -561,6 +574,33 @@ hipError_t launch_dma_f16out(const uint16_t* a, uint32_t lda, const uint16_t* b,
   return hipGetLastError();
 }
 
+// the direct-to-LDS kernel, whole 64-k stages only when the reduction allows
+template <bool kATr, bool kBTr, typename OutT>
+hipError_t launch_dma_any(const uint16_t* a, uint32_t lda, const uint16_t* b, uint32_t ldb, OutT* c, uint32_t mo,
+                          uint32_t no, uint32_t r, hipStream_t stream) {
+  return r % DBK == 0 ? launch_dma<kATr, kBTr, OutT, false>(a, lda, b, ldb, c, mo, no, r, stream)
+                      : launch_dma<kATr, kBTr, OutT, true>(a, lda, b, ldb, c, mo, no, r, stream);
+}
+}  // namespace
+
+hipError_t launch_gemm_f16f32(const uint16_t* a, const uint16_t* b, float* c,
+                              uint32_t m, uint32_t n, uint32_t k, hipStream_t stream) {
+  const uint32_t mtiles = (m + BM - 1) / BM;
+  const uint32_t ntiles = (n + BN - 1) / BN;
+  const dim3 grid(mtiles * ntiles), block(THREADS);
+  // Direct-to-LDS path: A's 16-byte reduction chunks need k % 8 == 0 (a chunk
+  // never straddles the end of the reduction), B's index chunks n % 8 == 0;
+  // 32-bit per-lane byte offsets need 256 * k * 2 and 64 * n * 2 below 2^31.
+  if (k > 0 && k % 8 == 0 && n % 8 == 0 && k < (1u << 22) && n < (1u << 24))
+    return launch_dma_any<false, true, float>(a, k, b, n, c, m, n, k, stream);
+  if (k % 8 == 0 && n % 8 == 0)
+    hipLaunchKernelGGL(gemm_f16f32_kernel<true>, grid, block, 0, stream, a, b, c, m, n, k, mtiles);
+  else
+    hipLaunchKernelGGL(gemm_f16f32_kernel<false>, grid, block, 0, stream, a, b, c, m, n, k, mtiles);
+  return hipGetLastError();
+}
+
+namespace {
 hipError_t launch_strided_f16out(const uint16_t* a, size_t a_i, size_t a_r, const uint16_t* b, size_t b_r,
                                  size_t b_j, uint16_t* c, uint32_t mo, uint32_t no, uint32_t r, hipStream_t stream) {
   const size_t total = (size_t)mo * no;
@@ -583,16 +623,18 @@ hipError_t launch_gemm_f16f32_bwd(const uint16_t* a, const uint16_t* b, const fl
   if (blocks == 0) blocks = 1;
   hipLaunchKernelGGL(cast_f16_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, grad, grad16, mn, vec);
   if (hipError_t e = hipGetLastError()) return e;
-  // grad_a[m, k] = grad16[m, n] . b[k, n]^T: both operands reduction (n) contiguous
+  // grad_a[m, k] = grad16[m, n] . b[k, n]^T: both operands reduction (n)
+  // contiguous, so n % 8 == 0 (no 16-byte chunk straddles the end of a row)
   hipError_t e;
-  if (n % DBK == 0 && n < (1u << 22))
-    e = launch_dma_f16out<false, false>(grad16, n, b, n, grad_a, m, k, n, stream);
+  if (n % 8 == 0 && n < (1u << 22))
+    e = launch_dma_any<false, false, uint16_t>(grad16, n, b, n, grad_a, m, k, n, stream);
   else
     e = launch_strided_f16out(grad16, n, 1, b, 1, n, grad_a, m, k, n, stream);
   if (e != hipSuccess) return e;
-  // grad_b[k, n] = a[m, k]^T . grad16[m, n]: both operands index contiguous
-  if (m % DBK == 0 && k % 8 == 0 && n % 8 == 0 && k < (1u << 24) && n < (1u << 24))
-    e = launch_dma_f16out<true, true>(a, k, grad16, n, grad_b, k, n, m, stream);
+  // grad_b[k, n] = a[m, k]^T . grad16[m, n]: both operands index contiguous;
+  // any m (whole reduction rows past m read as zeros)
+  if (k % 8 == 0 && n % 8 == 0 && k < (1u << 24) && n < (1u << 24))
+    e = launch_dma_any<true, true, uint16_t>(a, k, grad16, n, grad_b, k, n, m, stream);
   else
     e = launch_strided_f16out(a, 1, k, grad16, n, 1, grad_b, k, n, m, stream);
   return e;

@@ -41,7 +41,10 @@ def test_identity_and_exact_integers():
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 7), (300, 200, 100), (257, 259, 72), (100, 100, 4096),
                                    (513, 300, 520), (16, 1000, 33), (256, 256, 64),
                                    # k % 64 == 0 and n % 8 == 0: the direct-to-LDS path, ragged m and n
-                                   (300, 264, 128), (513, 136, 192), (40, 520, 64), (257, 8, 256)])
+                                   (300, 264, 128), (513, 136, 192), (40, 520, 64), (257, 8, 256),
+                                   # k % 8 == 0, k % 64 != 0: the direct-to-LDS path with a ragged last stage
+                                   (300, 264, 200), (257, 136, 72), (64, 64, 8), (1, 8, 8), (513, 520, 4104),
+                                   (40, 1024, 4000)])
 def test_ragged_shapes(M, N, K):
     a, b = workloads.gemm_inputs(M, N, K, seed=M + N + K)
     c, t = gemm(a, b)
@@ -67,3 +70,14 @@ def test_config_4096_sampled():
     assert bad == 0, f"{bad} outside tolerance, max ratio {ratio:.3f}"
     print(f"gemm 4096^3 ({rows.size} entries): max |d|/tol = {ratio:.4f}")
     assert np.array_equal(run(a, b), got)          # run-to-run identical
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 136, 72), (64, 256, 4040)])
+def test_ragged_reduction_exact_integers_bitwise(M, N, K):
+    # small integers: every partial sum is exact in f32, so the ragged last stage (k % 64 != 0)
+    # must reproduce the exact product bit for bit -- the chunks past k read as zeros
+    rng = np.random.default_rng(M + K)
+    a = rng.integers(-4, 5, size=(M, K)).astype(np.float16)
+    b = rng.integers(-4, 5, size=(K, N)).astype(np.float16)
+    c, _ = gemm(a, b)
+    assert np.array_equal(run(a, b), c.astype(np.float32))

@@ -3,8 +3,8 @@
 grad_a = f16(f16(G) . B^T), grad_b = f16(A^T . f16(G)); tolerance per element
 |d - Y*| <= ulp16(Y*) + 1e-5 * T against the unrounded float64 oracle value.
 Cases whose exact results are representable in f16 are compared bit for bit.
-Shapes cover the direct-to-LDS paths (reduction a multiple of 64, strides
-multiples of 8) and the any-shape fallback for each gradient.
+Shapes cover the direct-to-LDS paths (strides multiples of 8; whole 64-k stages and a
+ragged last stage) and the any-shape fallback for each gradient (n or k not a multiple of 8).
 """
 import numpy as np
 import pytest
@@ -50,9 +50,10 @@ def test_golden_handworked_bitwise():
 @pytest.mark.parametrize("M,N,K", [
     (256, 256, 256),      # both gradients on the direct-to-LDS path
     (320, 192, 520),      # both direct, ragged output tiles
-    (300, 128, 136),      # grad_a direct, grad_b fallback (m % 64 != 0)
-    (192, 72, 264),       # grad_a fallback (n % 64 != 0), grad_b direct
-    (5, 7, 9), (1, 64, 1), (64, 64, 8), (130, 64, 3),
+    (300, 128, 136),      # grad_a direct, grad_b direct with a ragged last stage (m % 64 != 0)
+    (192, 72, 264),       # grad_a direct with a ragged last stage (n % 64 != 0), grad_b direct
+    (1000, 520, 776), (37, 200, 64), (65, 72, 80), (2, 8, 8),   # both ragged
+    (5, 7, 9), (1, 64, 1), (64, 64, 8), (130, 64, 3),           # n or k % 8 != 0: the strided fallback
 ])
 def test_shapes(M, N, K):
     a, b, g = inputs(M, N, K, M * 31 + N * 7 + K)
@@ -69,6 +70,32 @@ def test_exact_integers_bitwise():
     ga, gb = run(a, b, g)
     (da, _), (db, _) = gemm_bwd(a, b, g)
     assert np.array_equal(ga, da.astype(np.float16)) and np.array_equal(gb, db.astype(np.float16))
+
+
+def test_ragged_exact_integers_bitwise():
+    # both gradients through the ragged last stage (n = 72, m = 100): exact small-integer sums
+    rng = np.random.default_rng(23)
+    M, N, K = 100, 72, 200
+    a = rng.integers(-4, 5, size=(M, K)).astype(np.float16)
+    b = rng.integers(-4, 5, size=(K, N)).astype(np.float16)
+    g = rng.integers(-4, 5, size=(M, N)).astype(np.float32)
+    ga, gb = run(a, b, g)
+    (da, _), (db, _) = gemm_bwd(a, b, g)
+    assert np.array_equal(ga, da.astype(np.float16)) and np.array_equal(gb, db.astype(np.float16))
+
+
+def test_large_ragged_sampled():
+    # m = 4000 (grad_b's reduction, 62.5 stages) and n = 4040 (grad_a's, 63.1 stages) at full width
+    M, N, K = 4000, 4040, 4096
+    a, b, g = inputs(M, N, K, 4242)
+    ga, gb = run(a, b, g)
+    rng = np.random.default_rng(4243)
+    ra, ca = rng.integers(0, M, 2048), rng.integers(0, K, 2048)
+    rb, cb = rng.integers(0, K, 2048), rng.integers(0, N, 2048)
+    (pa, ta), (pb, tb) = gemm_bwd_at(a, b, g, ra, ca, rb, cb)
+    for name, x, y, t in (("grad_a", ga[ra, ca], pa, ta), ("grad_b", gb[rb, cb], pb, tb)):
+        bad, ratio = compare.excess(x, y, compare.f16_tolerance(y, t))
+        assert bad == 0, f"{name}: {bad} outside tolerance, max ratio {ratio:.3f}"
 
 
 def test_config_4096_sampled():
