@@ -42,6 +42,8 @@
 // (plus 68 KiB of x slices): m <= 16: 1 x 1, 64, 16 (8 x rows kept when
 // m <= 8); m <= 32: 2 x 1, 64, 8; m <= 64: 2 x 2, 64, 8; m <= 128: 2 x 4, 64, 8.
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -59,6 +61,15 @@ template <> struct WordVec<1> { using T = uint32_t; };
 template <> struct WordVec<2> { using T = u32x2; };
 template <> struct WordVec<4> { using T = u32x4; };
 
+// Loads.  In the 16-wave configurations (straight-line, two groups per wave)
+// every load is a buffer load: a wave-uniform base (a descriptor in SGPRs)
+// plus one 32-bit per-lane byte offset fixed for the whole kernel, instead of
+// a 64-bit per-lane address -- fewer VGPRs and no 64-bit address VALU (m = 8:
+// 108 -> 100 VGPRs, 7.47 -> 7.20 us; W8A16 fits 16 waves without spilling).
+// The 8-wave configurations loop over their groups, and rebuilding
+// descriptors there cost 12-20%: they keep global loads.  Buffer offsets stay
+// below 2^32 by the host-side limits (k < 2^24, n < 2^26, m <= 128): x rows
+// <= 127 of 2k bytes; weights < 8 packed rows of 4n bytes.
 // Packed weights that one wave alone reads (rows not split across waves) carry
 // the non-temporal hint: they stream past the caches instead of displacing the
 // small x that every workgroup re-reads (n = k = 4096: m = 8 7.94 -> 7.37 us,
@@ -70,8 +81,25 @@ __device__ __forceinline__ T load_w(const T* p) {
   if constexpr (kOnce) return __builtin_nontemporal_load(p);
   else return *p;
 }
+constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, kBufferFlags);
+}
+template <int V, int kPolicy>
+__device__ __forceinline__ typename WordVec<V>::T buf_words(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (V == 4) return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kPolicy);
+  else if constexpr (V == 2) return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kPolicy);
+  else return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kPolicy);
+}
 template <int V> struct HalfVec { typedef uint16_t T __attribute__((ext_vector_type(V))); };
 template <> struct HalfVec<1> { typedef uint16_t T; };
+template <int V>
+__device__ __forceinline__ typename HalfVec<V>::T buf_halves(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  using HV = typename HalfVec<V>::T;
+  if constexpr (V == 4) return __builtin_bit_cast(HV, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  else if constexpr (V == 2) return __builtin_bit_cast(HV, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  else return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
 
 // kFull: n % BN == 0, so every strip is complete and the vector loads of
 // weights (VEC words) and scales (VEC halves) stay inside their rows.
@@ -118,8 +146,8 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   const uint32_t g_begin = (uint32_t)(((uint64_t)kpart * G) / KSPLIT);
   const uint32_t g_end = (uint32_t)(((uint64_t)(kpart + 1) * G) / KSPLIT);
 
-  const uint32_t* __restrict__ w = q == 0 ? p.w[0] : (q == 1 ? p.w[1] : p.w[2]);
-  const uint16_t* __restrict__ s = q == 0 ? p.s[0] : (q == 1 ? p.s[1] : p.s[2]);
+  const uint32_t* w = q == 0 ? p.w[0] : (q == 1 ? p.w[1] : p.w[2]);
+  const uint16_t* s = q == 0 ? p.s[0] : (q == 1 ? p.s[1] : p.s[2]);
   const uint32_t colv = n0 + VEC * l16;     // first of the lane's VEC columns
   // x of a group reaches the MFMAs through a wave-private LDS slice: load j
   // brings rows 4j .. 4j+3 of the wave's row block, 256 contiguous bytes each
@@ -133,11 +161,10 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   // do not mix).  Every load is issued, whatever M (repeated rows read the same
   // addresses): a load under a branch would make the compiler wait for all
   // loads in flight, the next group's included, before the first LDS write.
-  // (element offsets: m <= 128 and k < 2^24 keep them below 2^31)
   const uint32_t xbase = 16 * RT * rblk;
   const uint32_t xvalid = M > xbase ? (M - xbase < (uint32_t)XROWS ? M - xbase : XROWS) : 1;  // rows kept
-  // element offset of load j's chunk in group 0 (computed at each load: few
-  // registers are free in the widest configuration)
+  // element offset of load j's chunk within a group's x columns (computed at
+  // each load: few registers are free in the widest configuration)
   auto xoff = [&](int j) {
     const uint32_t lr = 4 * j + kb;
     const uint32_t row = xbase + (lr < xvalid ? lr : xvalid - 1);
@@ -151,8 +178,13 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   }
   uint4* const xw = xl[wave];
   // lane (kb, c) of k-step ks holds packed rows WPK*(4ks + kb) + j, j < WPK:
-  // the 8 consecutive k of its B operand
-  const uint32_t* wlane = w + (size_t)(WPK * kb) * N + colv;   // + (PR*g + 4*WPK*ks + j) * N
+  // the 8 consecutive k of its B operand.  Byte offset from the row
+  // PR*g + 4*WPK*ks + j of the load's base:
+  const uint32_t woff = ((WPK * kb) * N + colv) * 4;
+  const uint32_t* wlane = w + (size_t)(WPK * kb) * N + colv;   // the same, as an address
+  constexpr int kWPolicy = RSPLIT == 1 ? 2 : 0;   // non-temporal when one wave reads each word
+  constexpr bool kBuf = WAVES == 16;              // buffer loads (see above)
+  using ScT = std::conditional_t<kBuf, uint16_t, uint32_t>;
 
   floatx4 acc[VEC][RT];
 #pragma unroll
@@ -163,7 +195,9 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   struct Chunk {
     uint32_t wv[GCHUNK][4][WPK][VEC];
     uint4 xs[GCHUNK][XROWS / 4];     // x rows 4j .. 4j+3 of the group, 16 bytes per lane
-    uint32_t sc[GCHUNK][VEC];
+    // f16 bits of the scales: packed two per register in the 16-wave
+    // configurations (register budget), one per register otherwise (1-2% faster there)
+    ScT sc[GCHUNK][VEC];
   };
   // Loads of GCHUNK groups starting at g0.  Groups past the wave's range are
   // clamped to its last group (loaded, never used) so that every chunk issues
@@ -174,32 +208,63 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
       const uint32_t g = (g0 + gi < g_end) ? g0 + gi : g_end - 1;
       // x first: loads complete in issue order, so the LDS copy of x (needed
       // before any MFMA) need not wait for the weights of later k-steps
+      if constexpr (kBuf) {
+        const __amdgpu_buffer_rsrc_t xr = rsrc_of(p.x + (size_t)g * kGroup);
 #pragma unroll
-      for (int j = 0; j < XROWS / 4; ++j)
-        c.xs[gi][j] = *reinterpret_cast<const uint4*>(p.x + xoff(j) + (size_t)g * kGroup);
+        for (int j = 0; j < XROWS / 4; ++j)
+          c.xs[gi][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff(j) * 2, 0, 0));
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int j = 0; j < WPK; ++j) {
-          const size_t roff = ((size_t)g * PR + ks * 4 * WPK + j) * N;
-          if (kFull) {
-            const WV v = load_w<RSPLIT == 1>(reinterpret_cast<const WV*>(wlane + roff));
-            __builtin_memcpy(c.wv[gi][ks][j], &v, sizeof(v));
-          } else {
+          for (int j = 0; j < WPK; ++j) {
+            const __amdgpu_buffer_rsrc_t wr = rsrc_of(w + ((size_t)g * PR + ks * 4 * WPK + j) * N);
+            if (kFull) {
+              const WV v = buf_words<VEC, kWPolicy>(wr, woff);
+              __builtin_memcpy(c.wv[gi][ks][j], &v, sizeof(v));
+            } else {
 #pragma unroll
-            for (int t = 0; t < VEC; ++t) c.wv[gi][ks][j][t] = (colv + t < N) ? load_w<RSPLIT == 1>(wlane + roff + t) : 0u;
+              for (int t = 0; t < VEC; ++t)
+                c.wv[gi][ks][j][t] = (colv + t < N) ? buf_words<1, kWPolicy>(wr, woff + 4 * t) : 0u;
+            }
           }
-        }
-      if (kFull) {
-        using HV = typename HalfVec<VEC>::T;
-        const HV sv = *reinterpret_cast<const HV*>(s + (size_t)g * N + colv);
-        uint16_t sh[VEC];
-        __builtin_memcpy(sh, &sv, sizeof(sv));
+        const __amdgpu_buffer_rsrc_t sr = rsrc_of(s + (size_t)g * N);
+        if (kFull) {
+          const auto sv = buf_halves<VEC>(sr, colv * 2);
+          __builtin_memcpy(c.sc[gi], &sv, sizeof(sv));
+        } else {
 #pragma unroll
-        for (int t = 0; t < VEC; ++t) c.sc[gi][t] = sh[t];
+          for (int t = 0; t < VEC; ++t)
+            c.sc[gi][t] = (colv + t < N) ? buf_halves<1>(sr, (colv + t) * 2) : (uint16_t)0;
+        }
       } else {
 #pragma unroll
-        for (int t = 0; t < VEC; ++t) c.sc[gi][t] = (colv + t < N) ? (uint32_t)s[(size_t)g * N + colv + t] : 0u;
+        for (int j = 0; j < XROWS / 4; ++j)
+          c.xs[gi][j] = *reinterpret_cast<const uint4*>(p.x + xoff(j) + (size_t)g * kGroup);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int j = 0; j < WPK; ++j) {
+            const size_t roff = ((size_t)g * PR + ks * 4 * WPK + j) * N;
+            if (kFull) {
+              const WV v = load_w<RSPLIT == 1>(reinterpret_cast<const WV*>(wlane + roff));
+              __builtin_memcpy(c.wv[gi][ks][j], &v, sizeof(v));
+            } else {
+#pragma unroll
+              for (int t = 0; t < VEC; ++t)
+                c.wv[gi][ks][j][t] = (colv + t < N) ? load_w<RSPLIT == 1>(wlane + roff + t) : 0u;
+            }
+          }
+        if (kFull) {
+          using HV = typename HalfVec<VEC>::T;
+          const HV sv = *reinterpret_cast<const HV*>(s + (size_t)g * N + colv);
+          uint16_t sh[VEC];
+          __builtin_memcpy(sh, &sv, sizeof(sv));
+#pragma unroll
+          for (int t = 0; t < VEC; ++t) c.sc[gi][t] = sh[t];
+        } else {
+#pragma unroll
+          for (int t = 0; t < VEC; ++t) c.sc[gi][t] = (colv + t < N) ? s[(size_t)g * N + colv + t] : (uint16_t)0;
+        }
       }
     }
   };
@@ -296,15 +361,16 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   }
 }
 
-template <int BITS, int RT, int RSPLIT, int VEC, int WAVES, int XR = 16 * RT>
+// kOnlyFull: the caller guarantees n % BN == 0 (only the full-strip kernel is built)
+template <int BITS, int RT, int RSPLIT, int VEC, int WAVES, int XR = 16 * RT, bool kOnlyFull = false>
 hipError_t launch_split_k(const QkvProblem& p, hipStream_t stream) {
   constexpr uint32_t BN = 16 * VEC;
   const uint32_t nstrips = (p.n + BN - 1) / BN;
   const dim3 grid(3 * nstrips), block(WAVES * kWave);
-  if (p.n % BN == 0)
+  if (kOnlyFull || p.n % BN == 0)
     hipLaunchKernelGGL((qkv_decode_kernel<BITS, RT, RSPLIT, VEC, WAVES, true, XR>), grid, block, 0, stream, p,
                        nstrips);
-  else
+  else if constexpr (!kOnlyFull)
     hipLaunchKernelGGL((qkv_decode_kernel<BITS, RT, RSPLIT, VEC, WAVES, false, XR>), grid, block, 0, stream, p,
                        nstrips);
   return hipGetLastError();
@@ -312,8 +378,11 @@ hipError_t launch_split_k(const QkvProblem& p, hipStream_t stream) {
 
 template <int BITS>
 hipError_t launch_decode_bits(const QkvProblem& p, hipStream_t stream) {
-  // INT8 words are twice the registers per group: at m <= 16 its waves keep
-  // the 8-wave register budget (each wave then streams four groups)
+  // INT8 words are twice the registers per group: 16-wave workgroups fit
+  // (128 VGPRs, buffer loads) only with full strips at m <= 8; otherwise INT8
+  // keeps the 8-wave register budget (each wave then streams four groups).
+  // m = 8, n = k = 4096: 12.66 us at 8 waves, 11.57 at 16.
+  if (BITS == 8 && p.m <= 8 && p.n % 64 == 0) return launch_split_k<BITS, 1, 1, 4, 16, 8, true>(p, stream);
   constexpr int kSmallWaves = BITS == 8 ? 8 : 16;
   if (p.m <= 8) return launch_split_k<BITS, 1, 1, 4, kSmallWaves, 8>(p, stream);
   if (p.m <= 16) return launch_split_k<BITS, 1, 1, 4, kSmallWaves>(p, stream);
