@@ -25,11 +25,13 @@
 //   and output when n % 8 == 0), reads its words back and unpacks them to
 //   exact f16 values q * 2^-9 in registers (10 VALU ops per word) -- during
 //   the last two row tiles of the previous group, so that the unpack
-//   overlaps MFMAs; the scales carry the factor 2^9 back, exactly.
+//   overlaps MFMAs; the epilogue takes the factor 2^-9 back, exactly.
 // * Scales are applied per group in f32: the four MFMAs of a group
 //   accumulate a fresh partial sum of x*q*2^-9 (exact small integers, scaled
 //   by a power of two, times f16 activations), then
-//   acc += partial * (512 * scale).  Rounding q*scale to f16
+//   acc += partial * scale (the f16 scale converted inside the FMA;
+//   the accumulators hold 2^-9 times the result until the epilogue's
+//   exact multiply by 512).  Rounding q*scale to f16
 //   before the MFMA would cost up to 2^-12 relative per product, too much
 //   for the f16 output; the partial/scale split keeps every product exact.
 // * Epilogue: f32 -> f16 (RNE), transposed through LDS one output at a time,
@@ -111,12 +113,6 @@ __device__ __forceinline__ const char* uniform(const char* p) {
   asm volatile("" : "+s"(p));
   return p;
 }
-// Same for a per-lane 32-bit offset: re-materialised where it is used, so
-// that base + offset matches the scalar-base load form.
-__device__ __forceinline__ uint32_t lane_offset(uint32_t o) {
-  asm volatile("" : "+v"(o));
-  return o;
-}
 
 // Direct global -> LDS load of `bytes` (4 or 16) per lane from base + off,
 // in the buffer form: while a global (FLAT-encoded) direct load is pending,
@@ -139,11 +135,14 @@ __device__ __forceinline__ void load_a(half8_t (&a)[4], const uint4* __restrict_
   for (int ks = 0; ks < 4; ++ks) a[ks] = __builtin_bit_cast(half8_t, xs[row * KC + ((ks * 4 + kb) ^ (row & 15))]);
 }
 
-__device__ __forceinline__ void fold(floatx4 (&acc)[3], const floatx4 (&pb)[3], const float (&sf)[3]) {
+// acc += p * s with the f16 scale converted inside the FMA (v_fma_mix_f32):
+// the accumulators hold 2^-9 times the result (the unpacked weights carry
+// that factor), which the epilogue takes back exactly.
+__device__ __forceinline__ void fold(floatx4 (&acc)[3], const floatx4 (&pb)[3], const _Float16 (&sf)[3]) {
 #pragma unroll
   for (int q = 0; q < 3; ++q)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[q][i] = __builtin_fmaf(pb[q][i], sf[q], acc[q][i]);
+    for (int i = 0; i < 4; ++i) acc[q][i] = __builtin_fmaf(pb[q][i], (float)sf[q], acc[q][i]);
 }
 
 // The MFMA work of one group.
@@ -161,7 +160,7 @@ __device__ __forceinline__ void fold(floatx4 (&acc)[3], const floatx4 (&pb)[3], 
 // next-group words in LDS, `next_s[q]` at its scales; the wait before the
 // tail covers them (XPENDING = the x loads issued after them).
 template <int BITS, int WAVES, int XPENDING, typename IssueX>
-__device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3][4], float (&sf)[3],
+__device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3][4], _Float16 (&sf)[3],
                                           const uint4* __restrict__ xs, const uint32_t* __restrict__ next_w,
                                           const uint16_t* const (&next_s)[3], uint32_t l16, uint32_t kb,
                                           uint32_t lane, IssueX issue_x_part) {
@@ -223,7 +222,7 @@ __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3
   fold(acc[RT - 2], pbuf[0], sf);
   fold(acc[RT - 1], pbuf[1], sf);
 #pragma unroll
-  for (int q = 0; q < 3; ++q) sf[q] = h2f(ns16[q]) * kUnpackScaledInv;
+  for (int q = 0; q < 3; ++q) sf[q] = __builtin_bit_cast(_Float16, ns16[q]);
 }
 
 // BITS = 4 (W4A16) or 8 (W8A16: two packed words per 8 k of a column).
@@ -306,11 +305,11 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
       if (kAligned) {
 #pragma unroll
         for (int j = 0; j < WPK; ++j)
-          dma_to_lds(uniform(wg + (size_t)j * 64 * N), lane_offset(woff), wst + q * WAVES * WW + j * 256, 1);
+          dma_to_lds(uniform(wg + (size_t)j * 64 * N), woff, wst + q * WAVES * WW + j * 256, 1);
       } else {
 #pragma unroll
         for (int i = 0; i < 4 * WPK; ++i)
-          dma_to_lds(uniform(wg + (size_t)i * 16 * N), lane_offset((i & 1) ? woff_odd : woff),
+          dma_to_lds(uniform(wg + (size_t)i * 16 * N), (i & 1) ? woff_odd : woff,
                      wst + q * WAVES * WW + i * 64, 0);
       }
     }
@@ -322,14 +321,14 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
     const uint32_t off = (gi * N + s8c) * 2;
 #pragma unroll
     for (int q = 0; q < 3; ++q)
-      dma_to_lds(uniform(reinterpret_cast<const char*>(p.s[q] + (size_t)c0 * N)), lane_offset(off),
+      dma_to_lds(uniform(reinterpret_cast<const char*>(p.s[q] + (size_t)c0 * N)), off,
                  sbuf + (q * WAVES + wave) * SCHUNK * 16, 1);
   };
   // Load i of x of group g (clamped likewise) into x slot g % (XDIST+1).
   auto issue_x_one = [&](uint32_t g, int i) {
     uint4* xst = xslot(g);
     const char* xsrc = uniform(xblk + (size_t)(g < G ? g : G - 1) * kGroup * 2);
-    dma_to_lds(xsrc, lane_offset(xoff[i]), xst + (i * WAVES + wave) * 64, 1);
+    dma_to_lds(xsrc, xoff[i], xst + (i * WAVES + wave) * 64, 1);
   };
   auto issue_x = [&](uint32_t g) {
 #pragma unroll
@@ -351,7 +350,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
 
   // Prologue: x of groups 0 .. XDIST-1 in flight, group 0 in place and unpacked.
   half8_t bq[3][4];
-  float sf[3];
+  _Float16 sf[3];
   if (kAligned) issue_s(0);
   issue_w(0);
 #pragma unroll
@@ -371,7 +370,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
     const uint16_t* ns[3];
     scale_src(0, ns);
 #pragma unroll
-    for (int q = 0; q < 3; ++q) sf[q] = h2f(*ns[q]) * kUnpackScaledInv;
+    for (int q = 0; q < 3; ++q) sf[q] = __builtin_bit_cast(_Float16, *ns[q]);
   }
 
   // Per group g, after one barrier: weights of g+1 and x of g+XDIST are
@@ -415,7 +414,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         tile[(r * 16 + 4 * kb + i) * OUT_LD + wave * 16 + l16] =
-            __builtin_bit_cast(uint16_t, (_Float16)acc[r][q][i]);
+            __builtin_bit_cast(uint16_t, (_Float16)(acc[r][q][i] * kUnpackScaledInv));
     __syncthreads();
     uint16_t* out = p.out[q];
     if (kAligned) {
