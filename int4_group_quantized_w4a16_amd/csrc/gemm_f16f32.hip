@@ -231,8 +231,7 @@ __device__ __forceinline__ uint32_t vgpr_u32(uint32_t o) {
 // reduction indices.
 //   kTr = false: stored [index][reduction] (reduction contiguous, row stride
 //     ld): LDS [256][4 chunks], chunk kc of index row i at slot
-//     i*4 + (kc ^ ((i >> 2) & 3)) -- the 16 rows of one 16-byte fragment read
-//     fill one 256-byte pass of the banks; a fragment is one 16-byte read.
+//     i*4 + (kc ^ idx_swz(i)); a fragment is one 16-byte read.
 //   kTr = true: stored [reduction][index] (index contiguous, row stride ld):
 //     LDS [32][32 chunks], chunk c of reduction row r at slot r*32 + (c ^ tr_swz(r));
 //     a fragment is two transposing reads.
@@ -245,6 +244,15 @@ __device__ __forceinline__ uint32_t vgpr_u32(uint32_t o) {
 // second term rows j and 8 + j shared their banks: two-way conflicts on
 // every transposing read.)
 __device__ __forceinline__ uint32_t tr_swz(uint32_t r) { return (2 * (r & 3)) ^ (8 * ((r >> 3) & 1)); }
+// Chunk swizzle of the reduction-contiguous layout.  A fragment read has
+// lanes 16j + l read index rows i0 + l (l < 16), chunk j, and the LDS serves
+// 16-byte reads eight lanes at a time over 128 bytes of banks (counters: the
+// earlier swizzle (i >> 2) & 3, distinct over 16 lanes and 256 bytes but not
+// over 8 and 128, read two conflict cycles per instruction).  This one puts
+// the 8 rows of every aligned 8-lane group in 8 distinct 16-byte bank groups
+// mod 128 bytes, and the 16 rows of every 16-lane group in 16 distinct ones
+// mod 256 bytes.
+__device__ __forceinline__ uint32_t idx_swz(uint32_t i) { return ((i >> 1) & 3) ^ (((i >> 3) & 1) * 3); }
 
 template <bool kTr>
 struct DmaOperand {
@@ -253,7 +261,7 @@ struct DmaOperand {
                                          uint32_t ld) {
     const uint32_t s = (i * 4 + wave) * 64 + lane;
     if (!kTr) {
-      const uint32_t r = s >> 2, kc = (s & 3) ^ ((r >> 2) & 3);
+      const uint32_t r = s >> 2, kc = (s & 3) ^ idx_swz(r);
       const uint32_t rc = (idx0 + r < nidx) ? r : nidx - 1 - idx0;   // rows past the end repeat a valid one
       return (rc * ld + kc * 8) * 2;
     }
@@ -266,7 +274,7 @@ struct DmaOperand {
     const uint32_t s = (i * 4 + wave) * 64 + lane;
     if (!kTr) {
       const uint32_t r = s >> 2;
-      return ((s & 3) ^ ((r >> 2) & 3)) * 8;   // an 8-element chunk of one index row
+      return ((s & 3) ^ idx_swz(r)) * 8;   // an 8-element chunk of one index row
     }
     return s >> 5;                            // one reduction row, 8 indices
   }
@@ -286,7 +294,7 @@ struct DmaOperand {
   __device__ static half8_t frag(const char* __restrict__ st, uint32_t idx, uint32_t kb, uint32_t l16) {
     if (!kTr) {
       const uint4* t = reinterpret_cast<const uint4*>(st);
-      return __builtin_bit_cast(half8_t, t[idx * 4 + (kb ^ ((idx >> 2) & 3))]);
+      return __builtin_bit_cast(half8_t, t[idx * 4 + (kb ^ idx_swz(idx))]);
     }
     // transposing read: within each 16-lane group, lane i receives element
     // i % 4 of the 8-byte chunks that lanes 4j + i / 4 address (j = 0..3).
