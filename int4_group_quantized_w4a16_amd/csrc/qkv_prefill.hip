@@ -234,11 +234,12 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   constexpr int PR = 16 * WPK;                   // packed rows per group
   constexpr int BN = 16 * WAVES;
   constexpr int XPER = X_CHUNKS / THREADS;       // x loads per thread per stage
-  constexpr int OUT_LD = BN + 8;                 // padded f16 row of the epilogue tile
+  constexpr int OUT_LD = BN;                     // f16 row of the epilogue tile (column-swizzled)
   using L = RingLayout<BITS, WAVES, XDIST>;
   constexpr int WW = L::kWWords;
   static_assert(XPER * THREADS == X_CHUNKS, "x stage must split evenly");
   static_assert(BM * OUT_LD * 2 <= L::kSize * 16, "epilogue tile must fit in the ring");
+  static_assert(BN % 64 == 0, "the epilogue's column swizzle stays inside the tile row");
   static_assert(XPER < 64, "vmcnt range");
   extern __shared__ uint4 smem[];
 
@@ -408,12 +409,15 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
 #pragma unroll
   for (int q = 0; q < 3; ++q) {
     __syncthreads();   // ring (or the previous output's tile) no longer read
-    // D layout of a 16x16 MFMA tile: lane holds column (lane & 15), rows 4*(lane >> 4) + i
+    // D layout of a 16x16 MFMA tile: lane holds column (lane & 15), rows 4*(lane >> 4) + i.
+    // Column c of tile row t sits at c ^ (16 * ((t >> 2) & 3)): the four row
+    // groups of one 2-byte store (rows 4 apart) land in four different
+    // 32-byte bank windows, and each 16-byte row read stays inside its row.
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        tile[(r * 16 + 4 * kb + i) * OUT_LD + wave * 16 + l16] =
+        tile[(r * 16 + 4 * kb + i) * OUT_LD + ((wave * 16 + l16) ^ (16 * kb))] =
             __builtin_bit_cast(uint16_t, (_Float16)(acc[r][q][i] * kUnpackScaledInv));
     __syncthreads();
     uint16_t* out = p.out[q];
@@ -426,13 +430,13 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
         const uint32_t gr = m0 + row, gc = n0 + cc * 8;
         if (gr < M && gc < N)
           *reinterpret_cast<uint4*>(out + (size_t)gr * N + gc) =
-              *reinterpret_cast<const uint4*>(tile + row * OUT_LD + cc * 8);
+              *reinterpret_cast<const uint4*>(tile + row * OUT_LD + ((cc * 8) ^ (16 * ((row >> 2) & 3))));
       }
     } else {
       for (uint32_t e = tid; e < (uint32_t)(BM * BN); e += THREADS) {
         const uint32_t row = e / BN, c = e % BN;
         const uint32_t gr = m0 + row, gc = n0 + c;
-        if (gr < M && gc < N) out[(size_t)gr * N + gc] = tile[row * OUT_LD + c];
+        if (gr < M && gc < N) out[(size_t)gr * N + gc] = tile[row * OUT_LD + (c ^ (16 * ((row >> 2) & 3)))];
       }
     }
   }
