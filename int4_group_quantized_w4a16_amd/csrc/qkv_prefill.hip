@@ -12,8 +12,8 @@
 //   128 rows, so the waves share one x tile in LDS and never unpack the same
 //   weight twice.
 // * Everything a group of 128 k needs is staged into LDS rings with direct
-//   global->LDS loads (no registers, no VALU): x two groups ahead, the packed
-//   weights and scales one group ahead.  Each address is a wave-uniform base
+//   global->LDS loads (no registers, no VALU): x and the packed weights one
+//   group ahead, the scales 32 groups at a time.  Each address is a wave-uniform base
 //   in SGPRs plus a 32-bit lane offset.  One barrier per group; the only
 //   waits on the vector-memory counter are explicit.
 // * x: chunk kc of row r lands in slot r*16 + (kc ^ (r & 15)), which makes
@@ -34,8 +34,8 @@
 //   exact multiply by 512).  Rounding q*scale to f16
 //   before the MFMA would cost up to 2^-12 relative per product, too much
 //   for the f16 output; the partial/scale split keeps every product exact.
-// * Epilogue: f32 -> f16 (RNE), transposed through LDS one output at a time,
-//   16-byte row stores.
+// * Epilogue: f32 -> f16 (RNE), transposed through LDS one output at a time
+//   (unpadded rows, columns swizzled per 4-row group), 16-byte row stores.
 
 #include "common.hpp"
 #include "launch.hpp"
