@@ -266,7 +266,38 @@ def roof_lib():
     L.kaio_roof_clock_probe.restype = ctypes.c_int
     L.kaio_roof_wall_clock_khz.argtypes = []
     L.kaio_roof_wall_clock_khz.restype = ctypes.c_int
+    L.kaio_roof_strip_read.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_uint, ctypes.c_uint, ctypes.c_int,
+                                                               ctypes.c_void_p, ctypes.c_void_p]
+    L.kaio_roof_strip_read.restype = ctypes.c_int
+    L.kaio_roof_strip_sink_bytes.argtypes = [ctypes.c_uint, ctypes.c_int]
+    L.kaio_roof_strip_sink_bytes.restype = ctypes.c_size_t
     return L
+
+
+def strip_roof(wsets, replays, stream, dev):
+    """Read of the rotated packed-weight sets themselves by column strips, timed like decode:
+    64-column strips of one array (the decode kernel's weight reads, 256-byte row segments) and
+    16-column strips of all three (64-byte segments).  us per call and GB/s of the weights."""
+    import ctypes
+    import torch
+    L = roof_lib()
+    if L is None:
+        return None
+    rows, cols = wsets[0][0].shape
+    nbytes = 3 * rows * cols * 4
+    res = {"bytes": nbytes}
+    for sc in (64, 16):
+        sink = torch.empty((L.kaio_roof_strip_sink_bytes(cols, sc) // 4 + 1,), dtype=torch.int32, device=dev)
+
+        def call(i, sc=sc, sink=sink):
+            w = wsets[i % len(wsets)]
+            st = L.kaio_roof_strip_read(w[0].data_ptr(), w[1].data_ptr(), w[2].data_ptr(), rows, cols, sc,
+                                        sink.data_ptr(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"kaio_roof_strip_read failed ({st})")
+        ms = timed_graph(call, 4 * len(wsets), replays, stream)
+        res[f"strip{sc}"] = {"us_per_call": round(ms * 1e3, 3), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    return res
 
 
 # (loads per thread, threads); a negative count: the same shape with non-temporal loads
@@ -504,6 +535,10 @@ def main():
         rr = None if args.no_roof else read_roof(dbytes, R, replays, stream, dev)
         if rr:
             log(f"[bench] plain read of the same {dbytes} bytes: {rr['us_per_call']:.2f} us/call, {rr['gbs']:.0f} GB/s")
+        sr = None if args.no_roof else strip_roof([st[0] for st in sets], replays, stream, dev)
+        if sr:
+            log(f"[bench] the weights read by 64-column strips: {sr['strip64']['us_per_call']:.2f} us/call; "
+                f"by 16-column strips: {sr['strip16']['us_per_call']:.2f} us/call")
         secondary["qkv_decode"] = {
             "workload": "x f16[8,4096], 3x u32[512,4096], 3x f16[32,4096]; 21 rotated weight sets, "
                         "84 calls per HIP graph replay",
@@ -511,7 +546,8 @@ def main():
             "bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
             "algorithmic_bytes": dbytes, "tflops": round(2.0 * M * N * K * 3 / (dms * 1e-3) / 1e12, 3),
             "traffic": measured_traffic("qkv_decode", "qkv_decode.hip", dbytes),
-            "read_roof": rr, "frac_of_read_roof": round(rr["us_per_call"] / (dms * 1e3), 4) if rr else None}
+            "read_roof": rr, "frac_of_read_roof": round(rr["us_per_call"] / (dms * 1e3), 4) if rr else None,
+            "strip_read_roof": sr}
         # batched decode (split-K kernel up to m = 128) on the same rotated weights
         batched = []
         for bm in ((16, 32, 64, 128) if args.only != "decode" else ()):
@@ -558,7 +594,8 @@ def main():
                         "sets, 44 calls per HIP graph replay",
             "us_per_call": round(dms * 1e3, 3), "value": round(gbs, 1), "unit": "GB/s", "bound": "hbm",
             "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": dbytes,
-            "read_roof": rr, "frac_of_read_roof": round(rr["us_per_call"] / (dms * 1e3), 4) if rr else None}
+            "read_roof": rr, "frac_of_read_roof": round(rr["us_per_call"] / (dms * 1e3), 4) if rr else None,
+            "strip_read_roof": sr}
         del sets, x, outs
         c = workloads.QKV8_PREFILL
         M, N, K = c["M"], c["N"], c["K"]

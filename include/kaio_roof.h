@@ -2,8 +2,9 @@
  * kaio_roof.h -- measurement aid shipped beside libkaio (libkaio_roof.so).
  *
  * Not an operation of the pages and not part of libkaio's ABI: a plain
- * streaming read of device memory, used by the benchmark as the measured
- * ceiling an HBM-bound kernel moving the same bytes is compared with.
+ * streaming read of device memory and a read of the packed-weight layout by
+ * column strips, used by the benchmark as the measured ceilings an HBM-bound
+ * kernel moving the same bytes is compared with, and a shader-clock probe.
  */
 #ifndef KAIO_ROOF_H
 #define KAIO_ROOF_H
@@ -29,6 +30,25 @@ extern "C" {
 int kaio_roof_stream_read(const void* src, size_t bytes, void* sink, int loads_per_thread, int threads,
                           void* stream);
 size_t kaio_roof_sink_bytes(size_t bytes, int loads_per_thread, int threads);
+
+/*
+ * Reads three arrays of `rows` x `cols` u32 (row major, 16-byte aligned
+ * device buffers a0, a1, a2; rows a multiple of 128, cols of 64, both at most
+ * 2^20) by column strips, with non-temporal loads:
+ *   strip_cols = 64: 3*cols/64 workgroups of 16 waves, one per 64-column
+ *     strip of one array; each wave a contiguous row range, 16-byte loads, so
+ *     each row is read in 256-byte segments (the packed-weight reads of the
+ *     decode kernel);
+ *   strip_cols = 16: cols/16 workgroups of 8 waves, one per 16-column strip
+ *     of all three arrays; 4-byte loads, 64-byte row segments.
+ * `sink` must be a device buffer of kaio_roof_strip_sink_bytes(cols,
+ * strip_cols) bytes (the kernel may store there).  Returns 0 on a queued
+ * launch, 1 for a bad pointer or size, 2 for an unsupported strip width, 3 if
+ * the launch failed.
+ */
+int kaio_roof_strip_read(const void* a0, const void* a1, const void* a2, unsigned rows, unsigned cols,
+                         int strip_cols, void* sink, void* stream);
+size_t kaio_roof_strip_sink_bytes(unsigned cols, int strip_cols);
 
 /*
  * One wave that reads the shader-clock counter and the constant-rate real-time

@@ -63,6 +63,47 @@ __global__ void __launch_bounds__(64) clock_probe_kernel(unsigned long long* __r
   out[4 * blockIdx.x + 3] = r1;
 }
 
+// Reads of three packed-weight arrays (`rows` rows x `cols` u32 each, row
+// major) by column strips, with non-temporal loads, XORed and stored only on
+// a value the data never yields (as above):
+//   SC = 64: one workgroup of 16 waves per 64-column strip of one array
+//     (3 * cols / 64 workgroups); wave w reads rows [w*rows/16, (w+1)*rows/16),
+//     lane (kb, c) the four u32 of columns 4c .. 4c+3 at rows 4i + kb, i.e.
+//     256-byte row segments: the weight reads of the decode kernel.
+//   SC = 16: one workgroup of 8 waves per 16-column strip of all three
+//     arrays (cols / 16 workgroups, neighbouring strips on one XCD); wave w
+//     reads rows [w*rows/8, (w+1)*rows/8) of each array, lane (kb, c) the u32
+//     of column c: 64-byte row segments.
+template <int SC>
+__global__ void __launch_bounds__(SC == 64 ? 1024 : 512)
+strip_read_kernel(const uint32_t* __restrict__ a0, const uint32_t* __restrict__ a1,
+                  const uint32_t* __restrict__ a2, uint32_t rows, uint32_t cols, uint32_t* __restrict__ sink) {
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6, kb = lane >> 4, c = lane & 15;
+  uint32_t acc = 0;
+  if (SC == 64) {
+    const uint32_t strips = cols / 64, q = blockIdx.x / strips, s = blockIdx.x % strips;
+    const uint32_t* a = q == 0 ? a0 : (q == 1 ? a1 : a2);
+    const uint32_t r0 = wave * (rows / 16);
+#pragma unroll 8
+    for (uint32_t i = 0; i < rows / 64; ++i) {
+      const u32x4_t v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(a + (size_t)(r0 + 4 * i + kb) * cols + 64 * s + 4 * c));
+      acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+  } else {
+    const uint32_t nb = gridDim.x, per = nb / 8;
+    const uint32_t s = blockIdx.x < per * 8 ? (blockIdx.x % 8) * per + blockIdx.x / 8 : blockIdx.x;
+    const uint32_t r0 = wave * (rows / 8), col = 16 * s + c;
+#pragma unroll 8
+    for (uint32_t i = 0; i < rows / 32; ++i) {
+      acc ^= __builtin_nontemporal_load(a0 + (size_t)(r0 + 4 * i + kb) * cols + col);
+      acc ^= __builtin_nontemporal_load(a1 + (size_t)(r0 + 4 * i + kb) * cols + col);
+      acc ^= __builtin_nontemporal_load(a2 + (size_t)(r0 + 4 * i + kb) * cols + col);
+    }
+  }
+  if (acc == 0x9E3779B9u) sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
 template <int U, int THREADS>
 int launch(const void* src, size_t bytes, void* sink, bool nt, hipStream_t stream) {
   const size_t n16 = bytes / 16;
@@ -103,6 +144,32 @@ int kaio_roof_stream_read(const void* src, size_t bytes, void* sink, int loads_p
   KAIO_ROOF_CASE(4, 1024) KAIO_ROOF_CASE(8, 1024) KAIO_ROOF_CASE(16, 1024)
 #undef KAIO_ROOF_CASE
   return 2;
+}
+
+size_t kaio_roof_strip_sink_bytes(unsigned cols, int strip_cols) {
+  if (strip_cols == 64) return (size_t)3 * (cols / 64) * 1024 * 4;
+  if (strip_cols == 16) return (size_t)(cols / 16) * 512 * 4;
+  return 0;
+}
+
+int kaio_roof_strip_read(const void* a0, const void* a1, const void* a2, unsigned rows, unsigned cols,
+                         int strip_cols, void* sink, void* stream) {
+  if (!a0 || !a1 || !a2 || !sink) return 1;
+  if ((reinterpret_cast<uintptr_t>(a0) | reinterpret_cast<uintptr_t>(a1) | reinterpret_cast<uintptr_t>(a2)) & 15)
+    return 1;
+  if (rows == 0 || cols == 0 || rows % 128 || cols % 64 || rows > (1u << 20) || cols > (1u << 20)) return 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint32_t* p0 = static_cast<const uint32_t*>(a0);
+  const uint32_t* p1 = static_cast<const uint32_t*>(a1);
+  const uint32_t* p2 = static_cast<const uint32_t*>(a2);
+  uint32_t* sk = static_cast<uint32_t*>(sink);
+  if (strip_cols == 64)
+    hipLaunchKernelGGL(strip_read_kernel<64>, dim3(3 * (cols / 64)), dim3(1024), 0, s, p0, p1, p2, rows, cols, sk);
+  else if (strip_cols == 16)
+    hipLaunchKernelGGL(strip_read_kernel<16>, dim3(cols / 16), dim3(512), 0, s, p0, p1, p2, rows, cols, sk);
+  else
+    return 2;
+  return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 
 int kaio_roof_clock_probe(void* out, unsigned long long ticks, void* stream) {

@@ -37,11 +37,11 @@ def declared_functions(header=HEADER):
 
 
 def test_measurement_library_exports_its_header():
-    # libkaio_roof.so: the benchmark's plain-read and clock-probe kernels (not libkaio's ABI)
+    # libkaio_roof.so: the benchmark's plain-read, strip-read and clock-probe kernels (not libkaio's ABI)
     header = os.path.join(os.path.dirname(HEADER), "kaio_roof.h")
     names = declared_functions(header)
     assert set(names) == {"kaio_roof_stream_read", "kaio_roof_sink_bytes", "kaio_roof_clock_probe",
-                          "kaio_roof_wall_clock_khz"}
+                          "kaio_roof_wall_clock_khz", "kaio_roof_strip_read", "kaio_roof_strip_sink_bytes"}
     L = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(kaio.__file__)), "libkaio_roof.so"))
     for n in names:
         assert hasattr(L, n), n
@@ -52,6 +52,16 @@ def test_measurement_library_exports_its_header():
                                         ctypes.c_int, ctypes.c_void_p]
     assert L.kaio_roof_stream_read(A, 100, A + STEP, 4, 256, None) == 1      # not a multiple of 16
     assert L.kaio_roof_stream_read(A, 1024, A + STEP, 3, 256, None) == 2     # unsupported shape
+    L.kaio_roof_strip_sink_bytes.restype = ctypes.c_size_t
+    L.kaio_roof_strip_sink_bytes.argtypes = [ctypes.c_uint, ctypes.c_int]
+    assert L.kaio_roof_strip_sink_bytes(4096, 64) == 3 * 64 * 1024 * 4
+    assert L.kaio_roof_strip_sink_bytes(4096, 16) == 256 * 512 * 4
+    L.kaio_roof_strip_read.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_uint, ctypes.c_uint, ctypes.c_int,
+                                                               ctypes.c_void_p, ctypes.c_void_p]
+    # validation happens before any launch: no GPU needed
+    assert L.kaio_roof_strip_read(A, A + STEP, A + 2 * STEP, 100, 4096, 64, A + 3 * STEP, None) == 1  # rows % 128
+    assert L.kaio_roof_strip_read(A, A + STEP, A + 2 * STEP, 512, 4000, 64, A + 3 * STEP, None) == 1  # cols % 64
+    assert L.kaio_roof_strip_read(A, None, A + 2 * STEP, 512, 4096, 64, A + 3 * STEP, None) == 1      # null array
 
 
 def test_every_declared_symbol_is_exported():
