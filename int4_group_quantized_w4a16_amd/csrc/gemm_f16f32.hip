@@ -10,10 +10,14 @@
 //
 // gfx950 design
 // -------------
-// * Workgroup = 4 waves, tile 256 x 256; each wave owns a 128 x 128 sub-tile
-//   = 8 x 8 v_mfma_f32_16x16x32_f16 accumulators (256 f32 per lane, held in
-//   the accumulation registers), the largest tile the register file allows,
-//   which keeps LDS traffic per MFMA lowest.
+// * Direct-to-LDS path: workgroup = 8 waves, tile 256 x 256; each wave owns a
+//   128 x 64 sub-tile = 8 x 4 v_mfma_f32_16x16x32_f16 accumulators (128 f32
+//   per lane, held in the accumulation registers), so two waves share each
+//   SIMD and one issues MFMAs while the other waits at a barrier or on an LDS
+//   read (the 4-wave form with 128 x 128 sub-tiles, one wave per SIMD and the
+//   least LDS traffic per MFMA, remains as WN = 2: 0.4-2% slower at
+//   4096^3, 14% slower when the grid covers half the compute units).
+//   The register-staged fallback keeps 4 waves of 128 x 128.
 // * Main path (reduction % 64 == 0, strides % 8 == 0): both operand tiles
 //   land in LDS via 16-byte direct loads into four 32-k half-stage buffers;
 //   each half-stage of MFMAs reads the next fragments and loads the half
@@ -211,9 +215,10 @@ constexpr int DBK = 64;
 constexpr int kBufferFlags = 0x00020000;
 constexpr int HSLOTS = 1024;   // 16-byte slots of one operand's 32-k half-stage tile (256 x 32 f16)
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
-// lgkmcnt 11:8): at most 16 loads outstanding and no LDS read; nothing outstanding
-constexpr int kWait16 = 0x4070;
+// lgkmcnt 11:8): nothing outstanding
 constexpr int kWait0 = 0x0070;
+// s_waitcnt immediate for "at most vm loads outstanding, no LDS read"
+constexpr int wait_vm_imm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | 0x70; }
 
 __device__ __forceinline__ const char* sgpr_ptr(const char* p) {
   asm volatile("" : "+s"(p));
@@ -256,10 +261,12 @@ __device__ __forceinline__ uint32_t idx_swz(uint32_t i) { return ((i >> 1) & 3) 
 
 template <bool kTr>
 struct DmaOperand {
-  // byte offset, within a half-stage's source window, of this lane's load i (0..3)
+  // byte offset, within a half-stage's source window, of this lane's load i
+  // (0 .. 1024 / (64 * NW) - 1) of a workgroup of NW waves
+  template <int NW>
   __device__ static uint32_t lane_offset(int i, uint32_t wave, uint32_t lane, uint32_t idx0, uint32_t nidx,
                                          uint32_t ld) {
-    const uint32_t s = (i * 4 + wave) * 64 + lane;
+    const uint32_t s = (i * NW + wave) * 64 + lane;
     if (!kTr) {
       const uint32_t r = s >> 2, kc = (s & 3) ^ idx_swz(r);
       const uint32_t rc = (idx0 + r < nidx) ? r : nidx - 1 - idx0;   // rows past the end repeat a valid one
@@ -270,8 +277,9 @@ struct DmaOperand {
     return (r * ld + cc) * 2;
   }
   // reduction offset, within a 32-k half, of the first element of this lane's load i
+  template <int NW>
   __device__ static uint32_t lane_reduction(int i, uint32_t wave, uint32_t lane) {
-    const uint32_t s = (i * 4 + wave) * 64 + lane;
+    const uint32_t s = (i * NW + wave) * 64 + lane;
     if (!kTr) {
       const uint32_t r = s >> 2;
       return ((s & 3) ^ idx_swz(r)) * 8;   // an 8-element chunk of one index row
@@ -283,10 +291,8 @@ struct DmaOperand {
   }
   // bytes between the sources of consecutive 32-k halves
   __device__ static size_t half_stride(uint32_t ld) { return kTr ? (size_t)32 * ld * 2 : (size_t)32 * 2; }
-  // lane part of the fragment index for 16-wide tile t of a 128-wide wave block
-  __device__ static uint32_t lane_index(uint32_t wblock, uint32_t l16) {
-    return wblock * WT + (kTr ? 4 * (l16 & 3) : l16);
-  }
+  // lane part of the fragment index for 16-wide tile t of the wave block at index w0
+  __device__ static uint32_t lane_index(uint32_t w0, uint32_t l16) { return w0 + (kTr ? 4 * (l16 & 3) : l16); }
   // The fragment for index `idx` (lane_index + 16 t) from a half-stage buffer.
   // The buffer pointer is restrict-qualified: that tells the compiler the read
   // does not touch the buffers the loads in flight are writing, so it does not
@@ -313,8 +319,9 @@ struct DmaOperand {
   }
 };
 
+template <int TM, int TN>
 struct GemmFrags {
-  half8_t a[TT], b[TT];
+  half8_t a[TM], b[TN];
 };
 
 // The accumulating MFMAs of the direct-to-LDS kernel are issued through asm
@@ -335,15 +342,21 @@ __device__ __forceinline__ void mfma_inplace(floatx4& acc, const half8_t& a, con
 // Each row of accumulators passes through an asm that takes it as an in/out
 // operand and waits 2 * (NOP + 1) cycles, so no access to a row can move
 // across its wait, and the wait exceeds what an 8-pass MFMA needs.
-template <int NOP>
-__device__ __forceinline__ void hazard_guard(floatx4 (&acc)[TT][TT]) {
-  static_assert(TT == 8, "one asm operand per accumulator of a row");
+template <int NOP, int TM, int TN>
+__device__ __forceinline__ void hazard_guard(floatx4 (&acc)[TM][TN]) {
+  static_assert(TN == 8 || TN == 4, "one asm operand per accumulator of a row");
 #pragma unroll
-  for (int r = 0; r < TT; ++r)
-    asm volatile("s_nop %8\n\ts_nop %8"
-                 : "+a"(acc[r][0]), "+a"(acc[r][1]), "+a"(acc[r][2]), "+a"(acc[r][3]),
-                   "+a"(acc[r][4]), "+a"(acc[r][5]), "+a"(acc[r][6]), "+a"(acc[r][7])
-                 : "i"(NOP));
+  for (int r = 0; r < TM; ++r) {
+    if constexpr (TN == 8)
+      asm volatile("s_nop %8\n\ts_nop %8"
+                   : "+a"(acc[r][0]), "+a"(acc[r][1]), "+a"(acc[r][2]), "+a"(acc[r][3]),
+                     "+a"(acc[r][4]), "+a"(acc[r][5]), "+a"(acc[r][6]), "+a"(acc[r][7])
+                   : "i"(NOP));
+    else
+      asm volatile("s_nop %4\n\ts_nop %4"
+                   : "+a"(acc[r][0]), "+a"(acc[r][1]), "+a"(acc[r][2]), "+a"(acc[r][3])
+                   : "i"(NOP));
+  }
 }
 
 __device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
@@ -358,32 +371,43 @@ __device__ __forceinline__ void store_out(uint16_t* p, float v) { *p = __builtin
 // chunks past R are then zero.  A lane whose chunk starts at or past R
 // points its direct load past the end of the descriptor's range, and a
 // buffer load out of range returns zeros, which land in LDS like data.  No
-// load is skipped, so every wave still issues exactly 8 loads per half-stage
+// load is skipped, so every wave still issues exactly 2 * LPL loads per half-stage
 // and the fixed vmcnt waits below stay exact.
-template <bool kATr, bool kBTr, typename OutT, bool kRagged>
-__global__ void __launch_bounds__(THREADS, 1)
+//
+// WN = waves along the tile's columns: 2 (4 waves, 128 x 128 wave tiles, one
+// wave per SIMD) or 4 (8 waves, 128 x 64 wave tiles, two per SIMD).
+template <bool kATr, bool kBTr, typename OutT, bool kRagged, int WN>
+__global__ void __launch_bounds__(128 * WN, 1)
 gemm_dma_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __restrict__ B, uint32_t ldb,
                 OutT* __restrict__ C, uint32_t Mo, uint32_t No, uint32_t R, uint32_t mtiles, uint32_t ntiles) {
+  static_assert(WN == 2 || WN == 4, "waves along n");
+  constexpr int NW = 2 * WN;                 // waves
+  constexpr int LPL = HSLOTS / (64 * NW);    // direct loads per lane per operand per half-stage
+  constexpr int TM = WT / 16;                // 16x16 tiles per wave along m (128 rows)
+  constexpr int WTN = BN / WN;               // wave tile columns
+  constexpr int TN = WTN / 16;
+  constexpr int kWaitHalves = wait_vm_imm(2 * 2 * LPL);   // two half-stages of loads in flight
   using OA = DmaOperand<kATr>;
   using OB = DmaOperand<kBTr>;
+  using Frags = GemmFrags<TM, TN>;
   extern __shared__ uint4 smem[];
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t kb = lane >> 4, l16 = lane & 15;
-  const uint32_t wm = wave >> 1, wn = wave & 1;
+  const uint32_t wm = wave / WN, wn = wave % WN;
 
   uint32_t tm, tn;
   tile_of<KAIO_GEMM_SM, KAIO_GEMM_SN>(blockIdx.x, gridDim.x, mtiles, ntiles, tm, tn);
   const uint32_t m0 = tm * BM, n0 = tn * BN;
 
-  uint32_t aoff[4], boff[4], ared[4], bred[4];
+  uint32_t aoff[LPL], boff[LPL], ared[LPL], bred[LPL];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    aoff[i] = OA::lane_offset(i, wave, lane, m0, Mo, lda);
-    boff[i] = OB::lane_offset(i, wave, lane, n0, No, ldb);
-    ared[i] = OA::lane_reduction(i, wave, lane);
-    bred[i] = OB::lane_reduction(i, wave, lane);
+  for (int i = 0; i < LPL; ++i) {
+    aoff[i] = OA::template lane_offset<NW>(i, wave, lane, m0, Mo, lda);
+    boff[i] = OB::template lane_offset<NW>(i, wave, lane, n0, No, ldb);
+    ared[i] = OA::template lane_reduction<NW>(i, wave, lane);
+    bred[i] = OB::template lane_reduction<NW>(i, wave, lane);
   }
   // kRagged: descriptors span 2 GiB (every in-bounds lane offset is below
   // 2^31, by the host-side size limits); kOutOfRange lies past that
@@ -395,7 +419,7 @@ gemm_dma_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
 
   // half-stage buffer of stage kt, half h (A part first, B part HSLOTS later)
   auto hbuf = [&](uint32_t kt, uint32_t h) { return smem + ((kt & 1) * 2 + h) * (2 * HSLOTS); };
-  // load j (0..3: A chunks, 4..7: B chunks) of this lane's share of half h of
+  // load j (0..LPL-1: A chunks, LPL..2LPL-1: B chunks) of this lane's share of half h of
   // stage kt.  The buffer form of the direct-to-LDS load is used, not the
   // global one: while a global (FLAT-encoded) load is pending the compiler can
   // no longer order the LDS counter and turns every wait for a fragment read
@@ -405,42 +429,42 @@ gemm_dma_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
   auto issue_one = [&](uint32_t kt, uint32_t h, int j) {
     uint4* st = hbuf(kt, h);
     const uint32_t hk = 2 * kt + h;   // 32-k half index
-    if (j < 4) {
+    if (j < LPL) {
       uint32_t off = aoff[j];
       if (kRagged && 32 * hk + ared[j] >= R) off = kOutOfRange;
       const __amdgpu_buffer_rsrc_t r =
           __builtin_amdgcn_make_buffer_rsrc((void*)sgpr_ptr(abase + hk * ahalf), 0, kRange, kBufferFlags);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, KAIO_GEMM_LDS(st + (j * 4 + wave) * 64), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, KAIO_GEMM_LDS(st + (j * NW + wave) * 64), 16,
                                                vgpr_u32(off), 0, 0, 0);
     } else {
-      uint32_t off = boff[j - 4];
-      if (kRagged && 32 * hk + bred[j - 4] >= R) off = kOutOfRange;
+      uint32_t off = boff[j - LPL];
+      if (kRagged && 32 * hk + bred[j - LPL] >= R) off = kOutOfRange;
       const __amdgpu_buffer_rsrc_t r =
           __builtin_amdgcn_make_buffer_rsrc((void*)sgpr_ptr(bbase + hk * bhalf), 0, kRange, kBufferFlags);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, KAIO_GEMM_LDS(st + HSLOTS + ((j - 4) * 4 + wave) * 64), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, KAIO_GEMM_LDS(st + HSLOTS + ((j - LPL) * NW + wave) * 64), 16,
                                                vgpr_u32(off), 0, 0, 0);
     }
   };
   auto issue_half = [&](uint32_t kt, uint32_t h) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) issue_one(kt, h, j);
+    for (int j = 0; j < 2 * LPL; ++j) issue_one(kt, h, j);
   };
 
-  floatx4 acc[TT][TT];
+  floatx4 acc[TM][TN];
 #pragma unroll
-  for (int r = 0; r < TT; ++r)
+  for (int r = 0; r < TM; ++r)
 #pragma unroll
-    for (int c = 0; c < TT; ++c) acc[r][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < TN; ++c) acc[r][c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   hazard_guard<4>(acc);
-  const uint32_t ai0 = OA::lane_index(wm, l16), bi0 = OB::lane_index(wn, l16);
-  auto load_frags = [&](const uint4* hb, GemmFrags& f) {
+  const uint32_t ai0 = OA::lane_index(wm * WT, l16), bi0 = OB::lane_index(wn * WTN, l16);
+  auto load_frags = [&](const uint4* hb, Frags& f) {
     const char* as = reinterpret_cast<const char*>(hb);
     const char* bs = reinterpret_cast<const char*>(hb + HSLOTS);
 #pragma unroll
-    for (int c = 0; c < TT; ++c) f.b[c] = OB::frag(bs, bi0 + c * 16, kb, l16);
+    for (int c = 0; c < TN; ++c) f.b[c] = OB::frag(bs, bi0 + c * 16, kb, l16);
 #pragma unroll
-    for (int r = 0; r < TT; ++r) f.a[r] = OA::frag(as, ai0 + r * 16, kb, l16);
+    for (int r = 0; r < TM; ++r) f.a[r] = OA::frag(as, ai0 + r * 16, kb, l16);
   };
   // The MFMAs on fragments f, row by row, with the reads of the next
   // fragments nf (from half-stage buffer nb) spread between the rows: all B
@@ -448,15 +472,15 @@ gemm_dma_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
   // read then has at least a row of MFMAs (128 cycles) before its use, and no
   // wait ever covers a read issued just before it.  The 8 direct loads of
   // half h of stage kt go between the rows too, one per row.
-  auto mma_read = [&](const GemmFrags& f, const uint4* nb, GemmFrags& nf, uint32_t kt, uint32_t h) {
+  auto mma_read = [&](const Frags& f, const uint4* nb, Frags& nf, uint32_t kt, uint32_t h) {
     const char* as = reinterpret_cast<const char*>(nb);
     const char* bs = reinterpret_cast<const char*>(nb + HSLOTS);
 #pragma unroll
-    for (int r = 0; r < TT; ++r) {
+    for (int r = 0; r < TM; ++r) {
 #pragma unroll
-      for (int c = 0; c < TT; ++c) mfma_inplace(acc[r][c], f.a[r], f.b[c]);
-      issue_one(kt, h, r);
-      if (r < TT / 2) {
+      for (int c = 0; c < TN; ++c) mfma_inplace(acc[r][c], f.a[r], f.b[c]);
+      if (r < 2 * LPL) issue_one(kt, h, r);
+      if (r < TN / 2) {
         nf.b[2 * r] = OB::frag(bs, bi0 + 2 * r * 16, kb, l16);
         nf.b[2 * r + 1] = OB::frag(bs, bi0 + (2 * r + 1) * 16, kb, l16);
       }
@@ -470,8 +494,8 @@ gemm_dma_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
   //                f0 came from (every wave read it before the last barrier);
   //   second half: MFMAs on f1, reads of f0 (stage kt+1, k 0-31), loads of
   //                stage kt+2's second half into the buffer f1 came from.
-  // Loads are issued in a fixed order, 8 per half per lane, so "at most 16
-  // outstanding" at a barrier means everything issued more than two halves
+  // Loads are issued in a fixed order, 2 * LPL per half per lane, so "at most
+  // 4 * LPL outstanding" at a barrier means everything issued more than two halves
   // ago has landed -- exactly the half the next half reads.  Past the last
   // stage the loads reload consumed stages into their own buffers and the
   // reads of "the next stage" read a buffer whose contents go unused (no
@@ -480,7 +504,7 @@ gemm_dma_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
   // the epilogue's kernel arguments, loaded here rather than inside the loop,
   // where a pending scalar load would again force full LDS waits
   asm volatile("" ::"s"(C), "s"(Mo), "s"(No));
-  GemmFrags f0, f1;
+  Frags f0, f1;
   const uint32_t s1 = nk > 1 ? 1 : 0;
   issue_half(0, 0);
   issue_half(0, 1);
@@ -489,33 +513,33 @@ gemm_dma_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
   // stage 0 in place (with a single stage, all loads; the repeat would
   // rewrite the buffers being read)
   if (nk > 1)
-    __builtin_amdgcn_s_waitcnt(kWait16);
+    __builtin_amdgcn_s_waitcnt(kWaitHalves);
   else
     __builtin_amdgcn_s_waitcnt(kWait0);
   __builtin_amdgcn_s_barrier();
   load_frags(hbuf(0, 0), f0);
   // every wave holds its f0 before the first half's loads overwrite that buffer
-  __builtin_amdgcn_s_waitcnt(kWait16);
+  __builtin_amdgcn_s_waitcnt(kWaitHalves);
   __builtin_amdgcn_s_barrier();
   for (uint32_t kt = 0; kt < nk; ++kt) {
     // stage kt+2 goes into stage kt's buffers; past the end, stage kt itself
     // is reloaded there (consumed, never read again)
     const uint32_t kn = kt + 2 < nk ? kt + 2 : kt;
     mma_read(f0, hbuf(kt, 1), f1, kn, 0);
-    __builtin_amdgcn_s_waitcnt(kWait16);
+    __builtin_amdgcn_s_waitcnt(kWaitHalves);
     __builtin_amdgcn_s_barrier();
     mma_read(f1, hbuf(kt + 1, 0), f0, kn, 1);
-    __builtin_amdgcn_s_waitcnt(kWait16);
+    __builtin_amdgcn_s_waitcnt(kWaitHalves);
     __builtin_amdgcn_s_barrier();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   hazard_guard<7>(acc);
 
 #pragma unroll
-  for (int r = 0; r < TT; ++r)
+  for (int r = 0; r < TM; ++r)
 #pragma unroll
-    for (int c = 0; c < TT; ++c) {
-      const uint32_t gc = n0 + wn * WT + c * 16 + l16;
+    for (int c = 0; c < TN; ++c) {
+      const uint32_t gc = n0 + wn * WTN + c * 16 + l16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t gr = m0 + wm * WT + r * 16 + 4 * kb + i;
@@ -568,17 +592,21 @@ __global__ void fill_zero_kernel(uint4* __restrict__ dst, size_t n16, uint8_t* _
 }  // namespace
 
 namespace {
+#ifndef KAIO_GEMM_WN
+#define KAIO_GEMM_WN 4
+#endif
 template <bool kATr, bool kBTr, typename OutT, bool kRagged>
 hipError_t launch_dma(const uint16_t* a, uint32_t lda, const uint16_t* b, uint32_t ldb, OutT* c, uint32_t mo,
                       uint32_t no, uint32_t r, hipStream_t stream) {
+  constexpr int WN = KAIO_GEMM_WN;
   const uint32_t mtiles = (mo + BM - 1) / BM, ntiles = (no + BN - 1) / BN;
   const size_t lds = (size_t)8 * HSLOTS * 16;
-  auto* kern = &gemm_dma_kernel<kATr, kBTr, OutT, kRagged>;
+  auto* kern = &gemm_dma_kernel<kATr, kBTr, OutT, kRagged, WN>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(mtiles * ntiles), dim3(THREADS), lds, stream, a, lda, b, ldb, c, mo, no, r, mtiles,
-                     ntiles);
+  hipLaunchKernelGGL(kern, dim3(mtiles * ntiles), dim3(128 * WN), lds, stream, a, lda, b, ldb, c, mo, no, r,
+                     mtiles, ntiles);
   return hipGetLastError();
 }
 
