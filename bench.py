@@ -47,11 +47,17 @@ def log(*a):
 
 
 def kernel_source_hash(name: str) -> str:
+    """Hash of a kernel source and common.hpp with comments and blank space removed, so that a
+    comment edit does not void counters taken on the same code."""
+    import re
     path = os.path.join(ROOT, "int4_group_quantized_w4a16_amd", "csrc", name)
     h = hashlib.sha256()
     for p in (path, os.path.join(ROOT, "int4_group_quantized_w4a16_amd", "csrc", "common.hpp")):
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 
