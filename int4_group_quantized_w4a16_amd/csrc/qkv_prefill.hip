@@ -128,11 +128,18 @@ __device__ __forceinline__ void dma_to_lds(const char* base, uint32_t off, void*
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, KAIO_LDS(lds), 4, off, 0, 0, 0);
 }
 
-__device__ __forceinline__ void load_a(half8_t (&a)[4], const uint4* __restrict__ xs, int r, uint32_t l16,
-                                       uint32_t kb) {
-  const uint32_t row = r * 16 + l16;
+// A fragments of row tile r: lane (kb, l16) reads row 16r + l16, chunk
+// 4ks + kb, stored at (4ks + kb) ^ l16 in that row.  xl[ks] points at row
+// l16's chunk of k-step ks in the group's x slot, so every tile's reads are
+// those four addresses plus an immediate offset.
+__device__ __forceinline__ void x_lanes(const uint4* const (&xl)[4], half8_t (&a)[4], int r) {
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) a[ks] = __builtin_bit_cast(half8_t, xs[row * KC + ((ks * 4 + kb) ^ (row & 15))]);
+  for (int ks = 0; ks < 4; ++ks) a[ks] = __builtin_bit_cast(half8_t, xl[ks][r * 16 * KC]);
+}
+__device__ __forceinline__ void lane_rows(const uint4* __restrict__ xs, uint32_t l16, uint32_t kb,
+                                          const uint4* (&xl)[4]) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) xl[ks] = xs + l16 * KC + ((ks * 4 + kb) ^ l16);
 }
 
 // acc += p * s with the f16 scale converted inside the FMA (v_fma_mix_f32):
@@ -168,11 +175,13 @@ __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3
   // in buffers (RT-2) % 3 and (RT-1) % 3 during tiles RT-4 and RT-3.
   half8_t abuf[3][4];
   floatx4 pbuf[2][3];
-  load_a(abuf[0], xs, 0, l16, kb);
-  load_a(abuf[1], xs, 1, l16, kb);
+  const uint4* xl[4];
+  lane_rows(xs, l16, kb, xl);
+  x_lanes(xl, abuf[0], 0);
+  x_lanes(xl, abuf[1], 1);
 #pragma unroll
   for (int r = 0; r < RT - 2; ++r) {
-    load_a(abuf[(r + 2) % 3], xs, r + 2, l16, kb);
+    x_lanes(xl, abuf[(r + 2) % 3], r + 2);
     // a later group's x: load i goes out during tile i mod (RT - 2), so every
     // one of the XPENDING loads is issued before the tail's wait counts them
 #pragma unroll
