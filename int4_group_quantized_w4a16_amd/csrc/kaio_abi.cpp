@@ -189,7 +189,7 @@ kaio_status qkv(const char* op, uint32_t bits, const void* x, const uint32_t* w_
   uint64_t out_bytes = 0, x_bytes = 0, w_bytes = 0, s_bytes = 0;
   const bool decode = m <= kaio::kDecodeMaxM;
   const uint64_t wgs = decode ? 3ull * ((n + kaio::decode_bn(m) - 1) / kaio::decode_bn(m))
-                              : (uint64_t)((m + kaio::kPrefillBM - 1) / kaio::kPrefillBM) *
+                              : (uint64_t)((m + kaio::prefill_bm(m, n) - 1) / kaio::prefill_bm(m, n)) *
                                     ((n + kaio::prefill_bn(m, n) - 1) / kaio::prefill_bn(m, n));
   if (!bytes_of(m, n, 2, &out_bytes) || !bytes_of(m, k, 2, &x_bytes) || !bytes_of(k / (32 / bits), n, 4, &w_bytes) ||
       !bytes_of(k / 128, n, 2, &s_bytes) || wgs > kaio::kMaxWorkgroups || n >= kaio::kMaxN ||

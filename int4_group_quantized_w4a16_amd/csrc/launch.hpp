@@ -30,6 +30,12 @@ constexpr int prefill_waves(uint32_t m, uint32_t n) {
 }
 // columns of each output per tile-kernel workgroup
 constexpr uint32_t prefill_bn(uint32_t m, uint32_t n) { return 16u * prefill_waves(m, n); }
+// Rows per tile-kernel workgroup: 64 when a grid of 4-wave 64-row workgroups
+// still fits one pass over the compute units (then the 128-row grid would
+// leave many idle: 128 < m <= 256 at n = 4096), else 128.
+constexpr uint32_t prefill_bm(uint32_t m, uint32_t n) {
+  return (uint64_t)((m + 63) / 64) * ((n + 63) / 64) <= kComputeUnits ? 64u : kPrefillBM;
+}
 constexpr uint32_t kMaxN = 1u << 26;   // keeps 32-bit per-lane byte offsets in range (16 rows x N x 4 B)
 constexpr uint32_t kMaxK = 1u << 24;
 #ifndef KAIO_SK_MAXM

@@ -43,10 +43,7 @@
 namespace kaio {
 namespace {
 
-constexpr int BM = kPrefillBM;          // 128 rows per workgroup
-constexpr int RT = BM / 16;             // row tiles per wave
 constexpr int KC = kGroup / 8;          // 16-byte chunks per row per group
-constexpr int X_CHUNKS = BM * KC;       // 16-byte chunks of x per stage (32 KiB)
 
 #ifndef KAIO_PREFILL_XDIST
 #define KAIO_PREFILL_XDIST 1
@@ -85,8 +82,9 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // group g+1: one weight slot is enough, and INT8 (twice the words) uses one so
 // that the ring fits in LDS.  INT4 keeps two.
 constexpr int SCHUNK = 32;
-template <int BITS, int WAVES, int XDIST>
+template <int BITS, int WAVES, int XDIST, int BM>
 struct RingLayout {
+  static constexpr int X_CHUNKS = BM * KC;                // 16-byte chunks of x per stage
   static constexpr int kXSlots = XDIST + 1;
   static constexpr int kWSlots = BITS == 4 ? 2 : 1;
   static constexpr int kWWords = 256 * (BITS / 4);       // words per output per wave per group
@@ -166,7 +164,7 @@ __device__ __forceinline__ void fold(floatx4 (&acc)[3], const floatx4 (&pb)[3], 
 // stalling the start of the next group.  `next_w` points at this wave's
 // next-group words in LDS, `next_s[q]` at its scales; the wait before the
 // tail covers them (XPENDING = the x loads issued after them).
-template <int BITS, int WAVES, int XPENDING, typename IssueX>
+template <int BITS, int WAVES, int XPENDING, int RT, typename IssueX>
 __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3][4], _Float16 (&sf)[3],
                                           const uint4* __restrict__ xs, const uint32_t* __restrict__ next_w,
                                           const uint16_t* const (&next_s)[3], uint32_t l16, uint32_t kb,
@@ -235,16 +233,22 @@ __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3
 }
 
 // BITS = 4 (W4A16) or 8 (W8A16: two packed words per 8 k of a column).
-template <int BITS, int WAVES, int XDIST, bool kAligned>
+// BM = rows of x per workgroup: 128, or 64 when a grid of such tiles still
+// fits one pass over the compute units and one of 128-row tiles would leave
+// many of them idle (128 < m <= 256 at n = 4096).
+template <int BITS, int WAVES, int XDIST, bool kAligned, int BM>
 __global__ void __launch_bounds__(WAVES * 64, 1)
 qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   constexpr int THREADS = WAVES * 64;
+  constexpr int RT = BM / 16;                    // row tiles per wave
+  static_assert(RT >= 3, "two tail tiles after at least one pipelined tile");
   constexpr int WPK = BITS / 4;                  // packed words per 8 k of a column
   constexpr int PR = 16 * WPK;                   // packed rows per group
   constexpr int BN = 16 * WAVES;
+  using L = RingLayout<BITS, WAVES, XDIST, BM>;
+  constexpr int X_CHUNKS = L::X_CHUNKS;
   constexpr int XPER = X_CHUNKS / THREADS;       // x loads per thread per stage
   constexpr int OUT_LD = BN;                     // f16 row of the epilogue tile (column-swizzled)
-  using L = RingLayout<BITS, WAVES, XDIST>;
   constexpr int WW = L::kWWords;
   static_assert(XPER * THREADS == X_CHUNKS, "x stage must split evenly");
   static_assert(BM * OUT_LD * 2 <= L::kSize * 16, "epilogue tile must fit in the ring");
@@ -408,7 +412,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
     const uint16_t* ns[3];
     scale_src(g + 1, ns);
     // x of g + XDIST goes out one load per row tile, between MFMAs
-    group_mma<BITS, WAVES, XPER>(acc, bq, sf, xslot(g), wave_words(g + 1), ns, l16, kb, lane,
+    group_mma<BITS, WAVES, XPER, RT>(acc, bq, sf, xslot(g), wave_words(g + 1), ns, l16, kb, lane,
                            [&](int i) { issue_x_one(g + XDIST, i); });
   }
   wait_vm_barrier<0>();   // no load is still writing the ring the epilogue reuses
@@ -451,14 +455,14 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   }
 }
 
-template <int BITS, int WAVES, int XDIST, bool kAligned>
+template <int BITS, int WAVES, int XDIST, bool kAligned, int BM>
 hipError_t launch_variant(const QkvProblem& p, hipStream_t stream) {
   constexpr int BN = 16 * WAVES;
   const uint32_t mtiles = (p.m + BM - 1) / BM;
   const uint32_t ntiles = (p.n + BN - 1) / BN;
-  const size_t lds = (size_t)RingLayout<BITS, WAVES, XDIST>::kSize * 16;
+  const size_t lds = (size_t)RingLayout<BITS, WAVES, XDIST, BM>::kSize * 16;
   const dim3 grid(mtiles * ntiles), block(WAVES * 64);
-  auto* kern = &qkv_prefill_kernel<BITS, WAVES, XDIST, kAligned>;
+  auto* kern = &qkv_prefill_kernel<BITS, WAVES, XDIST, kAligned, BM>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
@@ -466,15 +470,19 @@ hipError_t launch_variant(const QkvProblem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int BITS, int WAVES, int BM>
+hipError_t launch_aligned_or_not(const QkvProblem& p, hipStream_t stream) {
+  // 16-byte output rows and f16-pair scale loads need n % 8 == 0
+  return p.n % 8 == 0 ? launch_variant<BITS, WAVES, KAIO_PREFILL_XDIST, true, BM>(p, stream)
+                      : launch_variant<BITS, WAVES, KAIO_PREFILL_XDIST, false, BM>(p, stream);
+}
+
 template <int BITS>
 hipError_t launch_prefill_bits(const QkvProblem& p, hipStream_t stream) {
-  // 16-byte output rows and f16-pair scale loads need n % 8 == 0
-  const bool aligned = p.n % 8 == 0;
   if (prefill_waves(p.m, p.n) == 4)
-    return aligned ? launch_variant<BITS, 4, KAIO_PREFILL_XDIST, true>(p, stream)
-                   : launch_variant<BITS, 4, KAIO_PREFILL_XDIST, false>(p, stream);
-  return aligned ? launch_variant<BITS, 8, KAIO_PREFILL_XDIST, true>(p, stream)
-                 : launch_variant<BITS, 8, KAIO_PREFILL_XDIST, false>(p, stream);
+    return prefill_bm(p.m, p.n) == 64 ? launch_aligned_or_not<BITS, 4, 64>(p, stream)
+                                      : launch_aligned_or_not<BITS, 4, 128>(p, stream);
+  return launch_aligned_or_not<BITS, 8, 128>(p, stream);
 }
 
 }  // namespace

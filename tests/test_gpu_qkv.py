@@ -69,8 +69,9 @@ def test_tiny_config_all_outputs():
     (16, 128, 512), (17, 64, 256), (24, 200, 384), (32, 130, 384), (33, 64, 512), (48, 96, 1152),
     (63, 40, 256), (64, 200, 256), (65, 64, 256), (96, 136, 384), (127, 72, 256), (128, 64, 640),
     (129, 64, 256),
-    # tile kernel with 8 waves (the 4-wave grid would not fit in one pass), ragged and n % 8 != 0
-    (2100, 1000, 256), (2100, 1001, 128),
+    # tile kernel with 128-row tiles and 4 waves (64-row tiles would not fit in one pass), then
+    # 8 waves (neither 4-wave grid would); ragged and n % 8 != 0
+    (1100, 1000, 256), (1100, 1001, 128), (2100, 1000, 256), (2100, 1001, 128),
     # split-K: waves with exactly two groups on ragged strips (the straight-line path), and
     # waves with three or more groups, odd counts included (the loop; 8 and 16 x rows kept)
     (6, 65, 4096), (15, 100, 4096), (5, 72, 8320), (8, 64, 6272), (12, 64, 6272), (40, 72, 4480),
@@ -98,6 +99,8 @@ def test_prefill_config_all_outputs():
 
 
 @pytest.mark.parametrize("M,N,K", [
+    (256, 4096, 4096),    # 4-wave tile kernel, 64-row tiles: 4 x 64 tiles of 64 x 64
+    (200, 4096, 4096),    # the same with a ragged last row tile (8 of its 64 rows)
     (512, 4096, 4096),    # 4-wave tile kernel: 4 x 64 tiles of 128 x 64, walked in 4 x 8 super-blocks
     (1024, 4096, 1024),   # 8-wave tile kernel: 8 x 32 tiles of 128 x 128, walked in 4 x 8 super-blocks
 ])
