@@ -72,6 +72,8 @@ def test_tiny_config_all_outputs():
     # tile kernel with 128-row tiles and 4 waves (64-row tiles would not fit in one pass), then
     # 8 waves (neither 4-wave grid would); ragged and n % 8 != 0
     (1100, 1000, 256), (1100, 1001, 128), (2100, 1000, 256), (2100, 1001, 128),
+    # more than 32 groups in 64-row and in 128-row 4-wave tiles (scale chunk reloads)
+    (200, 520, 12416), (1100, 1000, 4480),
     # split-K: waves with exactly two groups on ragged strips (the straight-line path), and
     # waves with three or more groups, odd counts included (the loop; 8 and 16 x rows kept)
     (6, 65, 4096), (15, 100, 4096), (5, 72, 8320), (8, 64, 6272), (12, 64, 6272), (40, 72, 4480),

@@ -61,9 +61,10 @@ def test_workloads_all_outputs(cfg):
     # m <= 16, <= 32, <= 64, <= 128 (one, two and four row blocks), full and ragged
     (9, 100, 128), (16, 128, 512), (12, 64, 6272), (24, 200, 384), (32, 130, 384), (33, 64, 512),
     (48, 96, 1152), (64, 200, 256), (65, 64, 256), (100, 136, 384), (128, 64, 640), (40, 72, 4480),
-    # tile kernel: 4 waves and 8 waves, n % 8 == 0 and not, more than 32 groups (scale chunk reload)
+    # tile kernel: 64-row tiles (4 waves), 128-row tiles with 4 and with 8 waves, n % 8 == 0 and
+    # not, more than 32 groups (scale chunk reload)
     (129, 64, 256), (130, 200, 256), (300, 24, 640), (200, 1000, 1024), (129, 136, 8320),
-    (2100, 1000, 256), (2100, 1001, 128),
+    (1100, 1000, 4480), (1100, 1001, 256), (2100, 1000, 256), (2100, 1001, 128),
 ])
 def test_ragged_shapes(M, N, K):
     inp = workloads.qkv8_inputs(M, N, K, seed=M * 7919 + N * 31 + K + 1)
