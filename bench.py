@@ -341,6 +341,29 @@ def read_roof(nbytes, sets, replays, stream, dev):
             "shapes_tried": len(READ_SHAPES)}
 
 
+def vendor_dense(m, n, k, out_f32, steps, stream, dev):
+    """The dense f16 product of the same shape through torch (the ROCm BLAS library), timed the same
+    way: context for the fused kernels (a dense f16 weight matrix is 4x the packed INT4 bytes and
+    needs no unpack).  Returns None when torch cannot run it."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(7)
+    a = torch.randn((m, k), generator=g, device=dev, dtype=torch.float16)
+    b = torch.randn((k, n), generator=g, device=dev, dtype=torch.float16)
+    fn = (lambda i: torch.mm(a, b, out_dtype=torch.float32)) if out_f32 else (lambda i: torch.mm(a, b))
+    try:
+        fn(0)
+        torch.cuda.synchronize()
+    except (RuntimeError, TypeError) as e:
+        log(f"[bench] vendor dense {m}x{n}x{k} not timed: {str(e).splitlines()[0][:120]}")
+        return None
+    ms, _ = timed(fn, steps, 3, stream)
+    tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+    log(f"[bench] vendor dense f16 {m}x{n}x{k} ({'f32' if out_f32 else 'f16'} out): "
+        f"{ms * 1e3:.1f} us/call, {tf:.1f} TFLOP/s")
+    return {"what": f"torch.mm f16[{m},{k}] x f16[{k},{n}] -> {'f32' if out_f32 else 'f16'} (dense weights)",
+            "us_per_call": round(ms * 1e3, 2), "tflops": round(tf, 2)}
+
+
 def summarize(dirs):
     """Per-kernel summary of rocprofv3 CSV output (kernel_stats.csv or counter_collection.csv)."""
     import csv
@@ -505,6 +528,9 @@ def main():
             f"(peak there {peak_clk:.0f} TFLOP/s)")
         roof.update({"sclk": clock, "peak_at_sclk": round(peak_clk, 1),
                      "frac_at_sclk": round(tflops / peak_clk, 4)})
+    if not args.no_roof:
+        # Q|K|V as one dense [K, 3N] f16 matrix through the vendor library
+        roof["vendor_dense_f16"] = vendor_dense(M, 3 * N, K, False, args.steps, stream, dev)
     result.update({
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -633,6 +659,9 @@ def main():
                                     "us_per_call": round(gms * 1e3, 2), "value": round(gtf, 2),
                                     "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_F16_TFLOPS,
                                     "frac": round(gtf / PEAK_F16_TFLOPS, 4)}
+        if not args.no_roof:
+            secondary["gemm_f16f32"]["vendor"] = [
+                vendor_dense(M, N, K, f32, max(10, args.steps // 2), stream, dev) for f32 in (True, False)]
         # backward of the same product: grad f32[M,N] -> grad_a f16[M,K], grad_b f16[K,N]
         g = np.random.default_rng(c["seed"] + 1).standard_normal((M, N)).astype(np.float32)
         gd = t(g)
