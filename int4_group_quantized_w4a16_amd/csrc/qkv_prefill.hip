@@ -236,10 +236,15 @@ __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3
 // BM = rows of x per workgroup: 128, or 64 when a grid of such tiles still
 // fits one pass over the compute units and one of 128-row tiles would leave
 // many of them idle (128 < m <= 256 at n = 4096).
-template <int BITS, int WAVES, int XDIST, bool kAligned, int BM>
-__global__ void __launch_bounds__(WAVES * 64, 1)
+// KS = 1, or 2: the workgroup holds two sets of WAVES waves, each with its
+// own ring, that run the same loop over the two halves of the groups (so two
+// waves share each SIMD and hide each other's waits); the second set's
+// accumulators are added to the first's through LDS before the epilogue, in
+// one fixed order.  Needs an even group count.
+template <int BITS, int WAVES, int XDIST, bool kAligned, int BM, int KS>
+__global__ void __launch_bounds__(KS * WAVES * 64, 1)
 qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
-  constexpr int THREADS = WAVES * 64;
+  constexpr int THREADS = WAVES * 64;            // threads of one set
   constexpr int RT = BM / 16;                    // row tiles per wave
   static_assert(RT >= 3, "two tail tiles after at least one pipelined tile");
   constexpr int WPK = BITS / 4;                  // packed words per 8 k of a column
@@ -254,11 +259,16 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   static_assert(BM * OUT_LD * 2 <= L::kSize * 16, "epilogue tile must fit in the ring");
   static_assert(BN % 64 == 0, "the epilogue's column swizzle stays inside the tile row");
   static_assert(XPER < 64, "vmcnt range");
+  static_assert(KS == 1 || KS == 2, "one or two sets of waves");
+  static_assert(KS == 1 || WAVES * RT * 12 * 64 * 4 <= KS * L::kSize * 16, "the second set's sums must fit in LDS");
   extern __shared__ uint4 smem[];
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
-  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t set = wave_id / WAVES;          // which half of the groups (KS = 2)
+  const uint32_t wave = wave_id % WAVES;         // wave within its set: its 16 columns
+  uint4* const ring = smem + set * L::kSize;
   const uint32_t kb = lane >> 4;          // 8-k block of the 32-k MFMA step
   const uint32_t l16 = lane & 15;
 
@@ -267,13 +277,17 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   const uint32_t m0 = tm * BM;
   const uint32_t n0 = tn * BN;
   const uint32_t M = p.m, N = p.n, K = p.k;
-  const uint32_t G = K / kGroup;
+  const uint32_t G = K / kGroup / KS;            // groups of this set
+  const uint32_t g0 = set * G;                   // its first group
+  const uint32_t* const wsrc[3] = {p.w[0] + (size_t)g0 * PR * N, p.w[1] + (size_t)g0 * PR * N,
+                                   p.w[2] + (size_t)g0 * PR * N};
+  const uint16_t* const ssrc[3] = {p.s[0] + (size_t)g0 * N, p.s[1] + (size_t)g0 * N, p.s[2] + (size_t)g0 * N};
 
   // ---- per-lane DMA sources -----------------------------------------------------
   // Each source address is a wave-uniform base plus a 32-bit per-lane byte
   // offset (the host-side size limits keep the offsets below 2^32), which the
   // loads take in their scalar-base form: no per-lane 64-bit address math.
-  const char* xblk = reinterpret_cast<const char*>(p.x + (size_t)m0 * K);
+  const char* xblk = reinterpret_cast<const char*>(p.x + (size_t)m0 * K + (size_t)g0 * kGroup);
   uint32_t xoff[XPER];         // byte offset (within row block m0, group 0) of this lane's chunk
 #pragma unroll
   for (int i = 0; i < XPER; ++i) {
@@ -303,10 +317,10 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   const uint32_t s8c = s8 < N ? s8 : N - 8;
   const uint32_t sgi = lane >> 1;     // group within the chunk
 
-  auto xslot = [&](uint32_t g) { return smem + (g % L::kXSlots) * X_CHUNKS; };
-  auto wslot = [&](uint32_t g) { return smem + L::kWBase + (g % L::kWSlots) * L::kWSize; };
+  auto xslot = [&](uint32_t g) { return ring + (g % L::kXSlots) * X_CHUNKS; };
+  auto wslot = [&](uint32_t g) { return ring + L::kWBase + (g % L::kWSlots) * L::kWSize; };
   auto wave_words = [&](uint32_t g) { return reinterpret_cast<const uint32_t*>(wslot(g)) + wave * WW; };
-  uint16_t* const sbuf = reinterpret_cast<uint16_t*>(smem + L::kSBase);
+  uint16_t* const sbuf = reinterpret_cast<uint16_t*>(ring + L::kSBase);
 
   // Weights of group g (clamped to the last group: a repeat lands in a slot
   // nobody reads) into weight slot g % kWSlots.
@@ -315,7 +329,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
     uint32_t* wst = reinterpret_cast<uint32_t*>(wslot(g)) + wave * WW;
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
-      const char* wg = uniform(reinterpret_cast<const char*>(p.w[q] + (size_t)gc * PR * N));
+      const char* wg = uniform(reinterpret_cast<const char*>(wsrc[q] + (size_t)gc * PR * N));
       if (kAligned) {
 #pragma unroll
         for (int j = 0; j < WPK; ++j)
@@ -335,7 +349,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
     const uint32_t off = (gi * N + s8c) * 2;
 #pragma unroll
     for (int q = 0; q < 3; ++q)
-      dma_to_lds(uniform(reinterpret_cast<const char*>(p.s[q] + (size_t)c0 * N)), off,
+      dma_to_lds(uniform(reinterpret_cast<const char*>(ssrc[q] + (size_t)c0 * N)), off,
                  sbuf + (q * WAVES + wave) * SCHUNK * 16, 1);
   };
   // Load i of x of group g (clamped likewise) into x slot g % (XDIST+1).
@@ -353,7 +367,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
 #pragma unroll
     for (int q = 0; q < 3; ++q)
       ns[q] = kAligned ? sbuf + ((q * WAVES + wave) * SCHUNK + g % SCHUNK) * 16 + l16
-                       : p.s[q] + (size_t)(g < G ? g : G - 1) * N + colc;
+                       : ssrc[q] + (size_t)(g < G ? g : G - 1) * N + colc;
   };
 
   floatx4 acc[RT][3];
@@ -404,7 +418,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
     // The second of each pair issues first through the pipelined tiles (its
     // priority drops again before its tail), so its tail overlaps the other
     // wave's MFMAs (~3% at 2048 x 4096 x 4096).
-    if (WAVES == 8 && wave >= 4) __builtin_amdgcn_s_setprio(1);
+    if (KS * WAVES == 8 && wave_id >= 4) __builtin_amdgcn_s_setprio(1);
     issue_w(g + 1);
     // the next scale chunk replaces this one once the tail of g-1 has read
     // the last scale it needed (the scale of g, before the barrier)
@@ -417,28 +431,58 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   }
   wait_vm_barrier<0>();   // no load is still writing the ring the epilogue reuses
 
+  // ---- the second set's sums into the first's (KS = 2) -------------------------
+  // Wave w of set 1 holds the same accumulator elements, lane for lane, as
+  // wave w of set 0: one f32 per lane and element, lane-contiguous.
+  if constexpr (KS == 2) {
+    constexpr int E = RT * 3 * 4;
+    float* const red = reinterpret_cast<float*>(smem) + wave * E * 64 + lane;
+    __syncthreads();   // rings no longer read
+    if (set == 1) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[((r * 3 + q) * 4 + i) * 64] = acc[r][q][i];
+    }
+    __syncthreads();
+    if (set == 0) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[r][q][i] += red[((r * 3 + q) * 4 + i) * 64];
+    }
+  }
+
   // ---- epilogue: one output at a time through LDS -----------------------------
+  constexpr int TT = KS * THREADS;               // every thread of the workgroup stores
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
   for (int q = 0; q < 3; ++q) {
-    __syncthreads();   // ring (or the previous output's tile) no longer read
+    __syncthreads();   // ring (or the sums, or the previous output's tile) no longer read
     // D layout of a 16x16 MFMA tile: lane holds column (lane & 15), rows 4*(lane >> 4) + i.
     // Column c of tile row t sits at c ^ (16 * ((t >> 2) & 3)): the four row
     // groups of one 2-byte store (rows 4 apart) land in four different
     // 32-byte bank windows, and each 16-byte row read stays inside its row.
+    if (set == 0) {
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
+      for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        tile[(r * 16 + 4 * kb + i) * OUT_LD + ((wave * 16 + l16) ^ (16 * kb))] =
-            __builtin_bit_cast(uint16_t, (_Float16)(acc[r][q][i] * kUnpackScaledInv));
+        for (int i = 0; i < 4; ++i)
+          tile[(r * 16 + 4 * kb + i) * OUT_LD + ((wave * 16 + l16) ^ (16 * kb))] =
+              __builtin_bit_cast(uint16_t, (_Float16)(acc[r][q][i] * kUnpackScaledInv));
+    }
     __syncthreads();
     uint16_t* out = p.out[q];
     if (kAligned) {
       constexpr int CPR = BN / 8;                    // 16-byte chunks per tile row
+      static_assert(BM * CPR % TT == 0, "row chunks split evenly over the threads");
 #pragma unroll
-      for (int i = 0; i < BM * CPR / THREADS; ++i) {
-        const uint32_t c = i * THREADS + tid;
+      for (int i = 0; i < BM * CPR / TT; ++i) {
+        const uint32_t c = i * TT + tid;
         const uint32_t row = c / CPR, cc = c % CPR;
         const uint32_t gr = m0 + row, gc = n0 + cc * 8;
         if (gr < M && gc < N)
@@ -446,7 +490,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
               *reinterpret_cast<const uint4*>(tile + row * OUT_LD + ((cc * 8) ^ (16 * ((row >> 2) & 3))));
       }
     } else {
-      for (uint32_t e = tid; e < (uint32_t)(BM * BN); e += THREADS) {
+      for (uint32_t e = tid; e < (uint32_t)(BM * BN); e += TT) {
         const uint32_t row = e / BN, c = e % BN;
         const uint32_t gr = m0 + row, gc = n0 + c;
         if (gr < M && gc < N) out[(size_t)gr * N + gc] = tile[row * OUT_LD + (c ^ (16 * ((row >> 2) & 3)))];
@@ -455,14 +499,14 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   }
 }
 
-template <int BITS, int WAVES, int XDIST, bool kAligned, int BM>
+template <int BITS, int WAVES, int XDIST, bool kAligned, int BM, int KS>
 hipError_t launch_variant(const QkvProblem& p, hipStream_t stream) {
   constexpr int BN = 16 * WAVES;
   const uint32_t mtiles = (p.m + BM - 1) / BM;
   const uint32_t ntiles = (p.n + BN - 1) / BN;
-  const size_t lds = (size_t)RingLayout<BITS, WAVES, XDIST, BM>::kSize * 16;
-  const dim3 grid(mtiles * ntiles), block(WAVES * 64);
-  auto* kern = &qkv_prefill_kernel<BITS, WAVES, XDIST, kAligned, BM>;
+  const size_t lds = (size_t)KS * RingLayout<BITS, WAVES, XDIST, BM>::kSize * 16;
+  const dim3 grid(mtiles * ntiles), block(KS * WAVES * 64);
+  auto* kern = &qkv_prefill_kernel<BITS, WAVES, XDIST, kAligned, BM, KS>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
@@ -470,19 +514,19 @@ hipError_t launch_variant(const QkvProblem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BITS, int WAVES, int BM>
+template <int BITS, int WAVES, int BM, int KS>
 hipError_t launch_aligned_or_not(const QkvProblem& p, hipStream_t stream) {
   // 16-byte output rows and f16-pair scale loads need n % 8 == 0
-  return p.n % 8 == 0 ? launch_variant<BITS, WAVES, KAIO_PREFILL_XDIST, true, BM>(p, stream)
-                      : launch_variant<BITS, WAVES, KAIO_PREFILL_XDIST, false, BM>(p, stream);
+  return p.n % 8 == 0 ? launch_variant<BITS, WAVES, KAIO_PREFILL_XDIST, true, BM, KS>(p, stream)
+                      : launch_variant<BITS, WAVES, KAIO_PREFILL_XDIST, false, BM, KS>(p, stream);
 }
 
 template <int BITS>
 hipError_t launch_prefill_bits(const QkvProblem& p, hipStream_t stream) {
-  if (prefill_waves(p.m, p.n) == 4)
-    return prefill_bm(p.m, p.n) == 64 ? launch_aligned_or_not<BITS, 4, 64>(p, stream)
-                                      : launch_aligned_or_not<BITS, 4, 128>(p, stream);
-  return launch_aligned_or_not<BITS, 8, 128>(p, stream);
+  if (prefill_waves(p.m, p.n) == 8) return launch_aligned_or_not<BITS, 8, 128, 1>(p, stream);
+  if (prefill_bm(p.m, p.n) == 128) return launch_aligned_or_not<BITS, 4, 128, 1>(p, stream);
+  return prefill_ksplit(p.m, p.n, p.k) == 2 ? launch_aligned_or_not<BITS, 4, 64, 2>(p, stream)
+                                            : launch_aligned_or_not<BITS, 4, 64, 1>(p, stream);
 }
 
 }  // namespace

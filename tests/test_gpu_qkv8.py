@@ -65,6 +65,8 @@ def test_workloads_all_outputs(cfg):
     # not, more than 32 groups (scale chunk reload)
     (129, 64, 256), (130, 200, 256), (300, 24, 640), (200, 1000, 1024), (129, 136, 8320),
     (1100, 1000, 4480), (1100, 1001, 256), (2100, 1000, 256), (2100, 1001, 128),
+    # 64-row tiles with the groups split over two sets of waves (even group counts)
+    (150, 264, 8448), (150, 261, 8448), (256, 4096, 4096),
 ])
 def test_ragged_shapes(M, N, K):
     inp = workloads.qkv8_inputs(M, N, K, seed=M * 7919 + N * 31 + K + 1)
