@@ -341,10 +341,11 @@ def read_roof(nbytes, sets, replays, stream, dev):
             "shapes_tried": len(READ_SHAPES)}
 
 
-def vendor_dense(m, n, k, out_f32, steps, stream, dev):
+def vendor_dense(m, n, k, out_f32, steps, stream, dev, clock=False):
     """The dense f16 product of the same shape through torch (the ROCm BLAS library), timed the same
     way: context for the fused kernels (a dense f16 weight matrix is 4x the packed INT4 bytes and
-    needs no unpack).  Returns None when torch cannot run it."""
+    needs no unpack).  With `clock`, also the shader clock under it, measured as for the prefill.
+    Returns None when torch cannot run it."""
     import torch
     g = torch.Generator(device=dev).manual_seed(7)
     a = torch.randn((m, k), generator=g, device=dev, dtype=torch.float16)
@@ -356,12 +357,22 @@ def vendor_dense(m, n, k, out_f32, steps, stream, dev):
     except (RuntimeError, TypeError) as e:
         log(f"[bench] vendor dense {m}x{n}x{k} not timed: {str(e).splitlines()[0][:120]}")
         return None
+    clk = None
+    if clock:
+        def sustained(part):
+            for i in range(20 if part == 0 else 300):
+                fn(i)
+        clk = shader_clock_under(sustained, stream, dev)
     ms, _ = timed(fn, steps, 3, stream)
     tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
     log(f"[bench] vendor dense f16 {m}x{n}x{k} ({'f32' if out_f32 else 'f16'} out): "
-        f"{ms * 1e3:.1f} us/call, {tf:.1f} TFLOP/s")
-    return {"what": f"torch.mm f16[{m},{k}] x f16[{k},{n}] -> {'f32' if out_f32 else 'f16'} (dense weights)",
-            "us_per_call": round(ms * 1e3, 2), "tflops": round(tf, 2)}
+        f"{ms * 1e3:.1f} us/call, {tf:.1f} TFLOP/s"
+        + (f", shader clock {clk['median_mhz']:.0f} MHz" if clk else ""))
+    r = {"what": f"torch.mm f16[{m},{k}] x f16[{k},{n}] -> {'f32' if out_f32 else 'f16'} (dense weights)",
+         "us_per_call": round(ms * 1e3, 2), "tflops": round(tf, 2)}
+    if clk:
+        r["sclk_median_mhz"] = clk["median_mhz"]
+    return r
 
 
 def summarize(dirs):
@@ -530,7 +541,7 @@ def main():
                      "frac_at_sclk": round(tflops / peak_clk, 4)})
     if not args.no_roof:
         # Q|K|V as one dense [K, 3N] f16 matrix through the vendor library
-        roof["vendor_dense_f16"] = vendor_dense(M, 3 * N, K, False, args.steps, stream, dev)
+        roof["vendor_dense_f16"] = vendor_dense(M, 3 * N, K, False, args.steps, stream, dev, clock=True)
     result.update({
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
