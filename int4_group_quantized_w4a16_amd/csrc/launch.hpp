@@ -36,10 +36,11 @@ constexpr uint32_t prefill_bn(uint32_t m, uint32_t n) { return 16u * prefill_wav
 constexpr uint32_t prefill_bm(uint32_t m, uint32_t n) {
   return (uint64_t)((m + 63) / 64) * ((n + 63) / 64) <= kComputeUnits ? 64u : kPrefillBM;
 }
-// 64-row tiles run the groups as two halves on two sets of 4 waves when the
-// group count is even, else on one set
-constexpr int prefill_ksplit(uint32_t m, uint32_t n, uint32_t k) {
-  return prefill_bm(m, n) == 64 && (k / 128) % 2 == 0 ? 2 : 1;
+// 4-wave tiles run the groups as two halves on two sets of 4 waves when the
+// group count is even (128-row tiles: INT4 only, whose two rings fit in LDS),
+// else on one set
+constexpr int prefill_ksplit(uint32_t m, uint32_t n, uint32_t k, uint32_t bits) {
+  return prefill_waves(m, n) == 4 && (k / 128) % 2 == 0 && (prefill_bm(m, n) == 64 || bits == 4) ? 2 : 1;
 }
 constexpr uint32_t kMaxN = 1u << 26;   // keeps 32-bit per-lane byte offsets in range (16 rows x N x 4 B)
 constexpr uint32_t kMaxK = 1u << 24;

@@ -71,8 +71,8 @@ __device__ __forceinline__ void wait_vm_barrier() {
 }
 
 // LDS, in 16-byte units.  x of a group is fetched XDIST groups ahead (ring
-// of XDIST+1 slots), the packed weights one group ahead (2 slots), and the
-// scales SCHUNK groups at a time:
+// of XDIST+1 slots), the packed weights one group ahead (WSLOTS slots), and
+// the scales SCHUNK groups at a time:
 //   x  [XDIST+1][X_CHUNKS]            swizzled rows of x
 //   w  [WSLOTS][3][WAVES][PR][16] u32 packed rows x columns of output q, wave w
 //   s  [3][WAVES][SCHUNK][16] f16     scales of the wave's 16 columns (n % 8 == 0)
@@ -80,19 +80,26 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // words it loaded itself and has consumed (unpacked into registers) the words
 // of group g before the barrier that starts group g, after which it loads
 // group g+1: one weight slot is enough, and INT8 (twice the words) uses one so
-// that the ring fits in LDS.  INT4 keeps two.
-constexpr int SCHUNK = 32;
-template <int BITS, int WAVES, int XDIST, int BM>
+// that the ring fits in LDS.  INT4 keeps two, or one in a tight ring.
+// TIGHT: one weight slot and 8-group scale chunks, for two rings of 128-row
+// tiles in one workgroup.
+template <int BITS, int WAVES, int XDIST, int BM, bool TIGHT = false>
 struct RingLayout {
   static constexpr int X_CHUNKS = BM * KC;                // 16-byte chunks of x per stage
   static constexpr int kXSlots = XDIST + 1;
-  static constexpr int kWSlots = BITS == 4 ? 2 : 1;
+  static constexpr int kWSlots = BITS == 4 && !TIGHT ? 2 : 1;
+  static constexpr int kSChunk = TIGHT ? 8 : 32;         // SCHUNK
   static constexpr int kWWords = 256 * (BITS / 4);       // words per output per wave per group
   static constexpr int kWBase = kXSlots * X_CHUNKS;
   static constexpr int kWSize = 3 * WAVES * kWWords / 4;
   static constexpr int kSBase = kWBase + kWSlots * kWSize;
-  static constexpr int kSize = kSBase + 3 * WAVES * SCHUNK * 16 * 2 / 16;   // uint4
+  static constexpr int kSize = kSBase + 3 * WAVES * kSChunk * 16 * 2 / 16;   // uint4
 };
+constexpr int kLdsBytes = 160 * 1024;   // per workgroup
+// the ring of one set of waves: tight when two of the usual ones would not fit
+template <int BITS, int WAVES, int XDIST, int BM, int KS>
+using SetRing = RingLayout<BITS, WAVES, XDIST, BM,
+                           (KS == 2 && 2 * RingLayout<BITS, WAVES, XDIST, BM>::kSize * 16 > kLdsBytes)>;
 
 // LDS row position of packed row r within a wave's [PR][16] word block.  INT8
 // B operands take rows 8ks + 2kb + j (k-step ks, 8-k block kb, word j), which
@@ -250,7 +257,8 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   constexpr int WPK = BITS / 4;                  // packed words per 8 k of a column
   constexpr int PR = 16 * WPK;                   // packed rows per group
   constexpr int BN = 16 * WAVES;
-  using L = RingLayout<BITS, WAVES, XDIST, BM>;
+  using L = SetRing<BITS, WAVES, XDIST, BM, KS>;
+  constexpr int SCHUNK = L::kSChunk;
   constexpr int X_CHUNKS = L::X_CHUNKS;
   constexpr int XPER = X_CHUNKS / THREADS;       // x loads per thread per stage
   constexpr int OUT_LD = BN;                     // f16 row of the epilogue tile (column-swizzled)
@@ -261,6 +269,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   static_assert(XPER < 64, "vmcnt range");
   static_assert(KS == 1 || KS == 2, "one or two sets of waves");
   static_assert(KS == 1 || WAVES * RT * 12 * 64 * 4 <= KS * L::kSize * 16, "the second set's sums must fit in LDS");
+  static_assert(KS * L::kSize * 16 <= kLdsBytes, "rings must fit in LDS");
   extern __shared__ uint4 smem[];
 
   const uint32_t tid = threadIdx.x;
@@ -315,7 +324,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   // SCHUNK groups.
   const uint32_t s8 = n0 + wave * 16 + 8 * (lane & 1);
   const uint32_t s8c = s8 < N ? s8 : N - 8;
-  const uint32_t sgi = lane >> 1;     // group within the chunk
+  const uint32_t sgi = lane >> 1;     // group within the chunk (lanes 0..2*SCHUNK-1)
 
   auto xslot = [&](uint32_t g) { return ring + (g % L::kXSlots) * X_CHUNKS; };
   auto wslot = [&](uint32_t g) { return ring + L::kWBase + (g % L::kWSlots) * L::kWSize; };
@@ -343,14 +352,18 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
     }
   };
   // Scales of groups c0 .. c0+SCHUNK-1 (clamped to the last group) for the
-  // wave's columns into the scale buffer (n % 8 == 0 only).
+  // wave's columns into the scale buffer (n % 8 == 0 only).  With shorter
+  // chunks only lanes 0 .. 2*SCHUNK-1 load (a lane's bytes land at its own
+  // 16-byte offset from the buffer, so the others would overrun it).
   auto issue_s = [&](uint32_t c0) {
     const uint32_t gi = c0 + sgi < G ? sgi : G - 1 - c0;
     const uint32_t off = (gi * N + s8c) * 2;
+    if (SCHUNK == 32 || lane < 2 * SCHUNK) {
 #pragma unroll
-    for (int q = 0; q < 3; ++q)
-      dma_to_lds(uniform(reinterpret_cast<const char*>(ssrc[q] + (size_t)c0 * N)), off,
-                 sbuf + (q * WAVES + wave) * SCHUNK * 16, 1);
+      for (int q = 0; q < 3; ++q)
+        dma_to_lds(uniform(reinterpret_cast<const char*>(ssrc[q] + (size_t)c0 * N)), off,
+                   sbuf + (q * WAVES + wave) * SCHUNK * 16, 1);
+    }
   };
   // Load i of x of group g (clamped likewise) into x slot g % (XDIST+1).
   auto issue_x_one = [&](uint32_t g, int i) {
@@ -504,7 +517,7 @@ hipError_t launch_variant(const QkvProblem& p, hipStream_t stream) {
   constexpr int BN = 16 * WAVES;
   const uint32_t mtiles = (p.m + BM - 1) / BM;
   const uint32_t ntiles = (p.n + BN - 1) / BN;
-  const size_t lds = (size_t)KS * RingLayout<BITS, WAVES, XDIST, BM>::kSize * 16;
+  const size_t lds = (size_t)KS * SetRing<BITS, WAVES, XDIST, BM, KS>::kSize * 16;
   const dim3 grid(mtiles * ntiles), block(KS * WAVES * 64);
   auto* kern = &qkv_prefill_kernel<BITS, WAVES, XDIST, kAligned, BM, KS>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -524,9 +537,13 @@ hipError_t launch_aligned_or_not(const QkvProblem& p, hipStream_t stream) {
 template <int BITS>
 hipError_t launch_prefill_bits(const QkvProblem& p, hipStream_t stream) {
   if (prefill_waves(p.m, p.n) == 8) return launch_aligned_or_not<BITS, 8, 128, 1>(p, stream);
-  if (prefill_bm(p.m, p.n) == 128) return launch_aligned_or_not<BITS, 4, 128, 1>(p, stream);
-  return prefill_ksplit(p.m, p.n, p.k) == 2 ? launch_aligned_or_not<BITS, 4, 64, 2>(p, stream)
-                                            : launch_aligned_or_not<BITS, 4, 64, 1>(p, stream);
+  const bool split = prefill_ksplit(p.m, p.n, p.k, BITS) == 2;
+  if (prefill_bm(p.m, p.n) == 128) {
+    if constexpr (BITS == 4)
+      if (split) return launch_aligned_or_not<BITS, 4, 128, 2>(p, stream);
+    return launch_aligned_or_not<BITS, 4, 128, 1>(p, stream);
+  }
+  return split ? launch_aligned_or_not<BITS, 4, 64, 2>(p, stream) : launch_aligned_or_not<BITS, 4, 64, 1>(p, stream);
 }
 
 }  // namespace

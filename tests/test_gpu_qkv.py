@@ -75,6 +75,9 @@ def test_tiny_config_all_outputs():
     # more than 32 groups in 64-row and in 128-row 4-wave tiles (scale chunk reloads); 64-row
     # tiles split the groups over two sets of waves when their count is even (66: 33 per set)
     (200, 520, 12416), (1100, 1000, 4480), (150, 264, 8448), (150, 261, 8448),
+    # 128-row 4-wave tiles with the groups split over two sets (tight rings: one weight slot,
+    # 8-group scale chunks; 17 groups per set)
+    (1100, 1000, 4352), (1100, 1001, 4352),
     # split-K: waves with exactly two groups on ragged strips (the straight-line path), and
     # waves with three or more groups, odd counts included (the loop; 8 and 16 x rows kept)
     (6, 65, 4096), (15, 100, 4096), (5, 72, 8320), (8, 64, 6272), (12, 64, 6272), (40, 72, 4480),
@@ -104,7 +107,7 @@ def test_prefill_config_all_outputs():
 @pytest.mark.parametrize("M,N,K", [
     (256, 4096, 4096),    # 64-row tiles (4 x 64 tiles of 64 x 64), groups split over two sets of 4 waves
     (200, 4096, 4096),    # the same with a ragged last row tile (8 of its 64 rows)
-    (512, 4096, 4096),    # 4-wave tile kernel: 4 x 64 tiles of 128 x 64, walked in 4 x 8 super-blocks
+    (512, 4096, 4096),    # 4 x 64 tiles of 128 x 64 in 4 x 8 super-blocks, groups split over two sets
     (1024, 4096, 1024),   # 8-wave tile kernel: 8 x 32 tiles of 128 x 128, walked in 4 x 8 super-blocks
 ])
 def test_tile_kernel_super_block_grids_all_outputs(M, N, K):
