@@ -591,9 +591,10 @@ def main():
             "traffic": measured_traffic("qkv_decode", "qkv_decode.hip", dbytes),
             "read_roof": rr, "frac_of_read_roof": round(rr["us_per_call"] / (dms * 1e3), 4) if rr else None,
             "strip_read_roof": sr}
-        # batched decode (split-K kernel up to m = 128) on the same rotated weights
+        # batched decode and short prefill chunks on the same rotated weights (split-K kernel up
+        # to m = 128, the tile kernel's 64-row and 128-row 4-wave forms at 256 and 512)
         batched = []
-        for bm in ((16, 32, 64, 128) if args.only != "decode" else ()):
+        for bm in ((16, 32, 64, 128, 256, 512) if args.only != "decode" else ()):
             xb = t(np.random.default_rng(c["seed"] + 100 + bm).standard_normal((bm, K)).astype(np.float16))
             ob = [torch.empty((bm, N), dtype=torch.float16, device=dev) for _ in range(3)]
             bstep = lambda i: kaio.kaio_qkv_w4a16(xb, *sets[i % R][0], *sets[i % R][1], *ob)
@@ -607,7 +608,7 @@ def main():
             del xb, ob
         if batched:
             secondary["qkv_batched_decode"] = {
-                "workload": "x f16[m,4096] for m = 16, 32, 64, 128; weights and rotation as qkv_decode",
+                "workload": "x f16[m,4096] for m = 16, 32, 64, 128, 256, 512; weights and rotation as qkv_decode",
                 "points": batched, "bound": "hbm"}
         del sets, x, outs
 
