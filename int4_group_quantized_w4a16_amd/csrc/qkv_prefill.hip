@@ -7,15 +7,17 @@
 //
 // gfx950 design
 // -------------
-// * Workgroup = WAVES waves, tile = 128 rows of x by 16*WAVES columns of EACH
-//   output.  Wave w owns columns [16w, 16w+16) of all three outputs and all
-//   128 rows, so the waves share one x tile in LDS and never unpack the same
-//   weight twice.
+// * Workgroup = WAVES waves, tile = BM (128, or 64 for small grids) rows of
+//   x by 16*WAVES columns of EACH output.  Wave w owns columns [16w, 16w+16)
+//   of all three outputs and all BM rows, so the waves share one x tile in
+//   LDS and never unpack the same weight twice.  Small grids of 4-wave tiles
+//   run two such sets of waves per workgroup, one per half of the groups,
+//   each with its own ring, their sums added in LDS at the end.
 // * Everything a group of 128 k needs is staged into LDS rings with direct
 //   global->LDS loads (no registers, no VALU): x and the packed weights one
-//   group ahead, the scales 32 groups at a time.  Each address is a wave-uniform base
-//   in SGPRs plus a 32-bit lane offset.  One barrier per group; the only
-//   waits on the vector-memory counter are explicit.
+//   group ahead, the scales 32 (or 8) groups at a time.  Each address is a
+//   wave-uniform base in SGPRs plus a 32-bit lane offset.  One barrier per
+//   group; the only waits on the vector-memory counter are explicit.
 // * x: chunk kc of row r lands in slot r*16 + (kc ^ (r & 15)), which makes
 //   the MFMA A-operand reads bank-conflict free.  A fragments are read two
 //   row tiles ahead of the MFMAs that use them.
