@@ -5,6 +5,7 @@
  *
  *   kaio_qkv_w4a16          W4A16 group-quantized fused tri-output QKV projection
  *   kaio_qkv_w8a16          its W8A16 sibling (INT8 weights, same contract)
+ *                           (kaio_qkv_plan: which kernel form a call of given sizes runs)
  *   kaio_gemm_f16f32        dense f16 x f16 -> f32 matmul
  *   kaio_gemm_f16f32_bwd    its backward: f16 gradients of A and B
  *                           (kaio_gemm_f16f32_bwd_noalloc: the same without a workspace)
@@ -222,6 +223,21 @@ kaio_status kaio_dequant_group_bwd(kaio_dtype dtype, int32_t outer, int32_t axis
                                    const void* dy, const void* scale, void* dq,
                                    void* workspace, size_t workspace_bytes,
                                    void* stream);
+
+/*
+ * Which kernel form a kaio_qkv_w4a16 (bits 4) or kaio_qkv_w8a16 (bits 8)
+ * call of these sizes runs, for tests and tuning; host only, no device
+ * touched, nothing launched.  On KAIO_OK:
+ *   plan[0]  0: the split-K kernel (m <= 128), 1: the tile kernel
+ *   plan[1]  tile kernel: waves per set; split-K: 0
+ *   plan[2]  tile kernel: rows of x per tile; split-K: columns per strip
+ *   plan[3]  tile kernel: sets of waves per workgroup (2: the 128-k groups
+ *            are split in halves over two sets); split-K: 1
+ *   plan[4]  workgroups the launch has
+ * m == 0 or n == 0 is an empty call (plan[0..4] = 0).  bits other than 4 or
+ * 8, or a null plan -> INVALID_ARGUMENT; k % 128 != 0 -> INVALID_PROBLEM.
+ */
+kaio_status kaio_qkv_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t bits, uint32_t plan[5]);
 
 /* Message of the calling thread's most recent failed call ("" after a success). */
 const char* kaio_last_error(void);

@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.kaio_gemm_f16f32_bwd_workspace_size.restype = ctypes.c_size_t
         L.kaio_dequant_group_bwd.argtypes = [ctypes.c_int, i32, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.kaio_dequant_group_bwd.restype = ctypes.c_int
+        L.kaio_qkv_plan.argtypes = [u32] * 4 + [vp]
+        L.kaio_qkv_plan.restype = ctypes.c_int
         L.kaio_last_error.argtypes = []
         L.kaio_last_error.restype = ctypes.c_char_p
         L.kaio_version.argtypes = []
@@ -77,6 +79,14 @@ def kaio_last_error() -> str:
 
 def kaio_version() -> str:
     return lib().kaio_version().decode()
+
+
+def kaio_qkv_plan(m: int, n: int, k: int, bits: int = 4) -> dict:
+    """The kernel form a QKV call of these sizes runs (kaio_qkv_plan; host only)."""
+    plan = (ctypes.c_uint32 * 5)()
+    _check(lib().kaio_qkv_plan(m, n, k, bits, plan))
+    return {"kernel": "tile" if plan[0] else "split_k", "waves": plan[1], "rows": plan[2], "sets": plan[3],
+            "workgroups": plan[4]}
 
 
 def _check(status: int):

@@ -189,8 +189,7 @@ kaio_status qkv(const char* op, uint32_t bits, const void* x, const uint32_t* w_
   uint64_t out_bytes = 0, x_bytes = 0, w_bytes = 0, s_bytes = 0;
   const bool decode = m <= kaio::kDecodeMaxM;
   const uint64_t wgs = decode ? 3ull * ((n + kaio::decode_bn(m) - 1) / kaio::decode_bn(m))
-                              : (uint64_t)((m + kaio::prefill_bm(m, n) - 1) / kaio::prefill_bm(m, n)) *
-                                    ((n + kaio::prefill_bn(m, n) - 1) / kaio::prefill_bn(m, n));
+                              : kaio::prefill_wgs(kaio::prefill_form(m, n, k, bits), m, n);
   if (!bytes_of(m, n, 2, &out_bytes) || !bytes_of(m, k, 2, &x_bytes) || !bytes_of(k / (32 / bits), n, 4, &w_bytes) ||
       !bytes_of(k / 128, n, 2, &s_bytes) || wgs > kaio::kMaxWorkgroups || n >= kaio::kMaxN ||
       k >= kaio::kMaxK)
@@ -358,6 +357,31 @@ kaio_status kaio_dequant_group_bwd(kaio_dtype dtype, int32_t outer, int32_t axis
   (void)hipGetLastError();
   return launched(op, kaio::launch_dequant_group_bwd(dt, outer, axis, group_size, dy, scale, dq,
                                                      static_cast<hipStream_t>(stream)));
+}
+
+kaio_status kaio_qkv_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t bits, uint32_t plan[5]) {
+  static const char* op = "qkv_plan";
+  if (bits != 4 && bits != 8) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "bits (%u) must be 4 or 8", bits);
+  if (!plan) return fail(KAIO_ERR_INVALID_ARGUMENT, op, "plan is null");
+  if (k % 128 != 0)
+    return fail(KAIO_ERR_INVALID_PROBLEM, op, "K (%u) must be a multiple of group_size (128)", k);
+  for (int i = 0; i < 5; ++i) plan[i] = 0;
+  if (m == 0 || n == 0) return ok();
+  if (m <= kaio::kDecodeMaxM) {
+    const uint32_t bn = kaio::decode_bn(m);
+    plan[2] = bn;
+    plan[3] = 1;
+    plan[4] = (uint32_t)(3ull * ((n + bn - 1) / bn));
+  } else {
+    const kaio::PrefillForm f = kaio::prefill_form(m, n, k, bits);
+    plan[0] = 1;
+    plan[1] = f.waves;
+    plan[2] = f.bm;
+    plan[3] = f.sets;
+    const uint64_t wgs = kaio::prefill_wgs(f, m, n);
+    plan[4] = wgs > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)wgs;
+  }
+  return ok();
 }
 
 const char* kaio_last_error(void) { return g_last_error.c_str(); }

@@ -20,27 +20,53 @@ struct QkvProblem {
 };
 
 // Tile geometry, shared with the host-side grid-size checks.
-constexpr uint32_t kPrefillBM = 128;   // rows of x per workgroup
 constexpr uint64_t kComputeUnits = 256;  // MI355X
-// Waves per tile-kernel workgroup (each owns 16 columns of every output):
-// 8, unless the grid of 4-wave workgroups (64 columns) still fits in one pass
-// over the compute units -- then the narrower tiles double the workgroups.
-constexpr int prefill_waves(uint32_t m, uint32_t n) {
-  return (uint64_t)((m + kPrefillBM - 1) / kPrefillBM) * ((n + 63) / 64) <= kComputeUnits ? 4 : 8;
+// Forms of the tile kernel: waves per set (each wave owns 16 columns of every
+// output), rows per tile, and sets of waves per workgroup (2: the groups are
+// split in halves over two sets, which needs an even group count).  Every
+// form holds one workgroup per compute unit.  pass_cost: the time of one
+// full pass of the form over the compute units, relative to 8 waves x 128
+// rows (1000), measured at n = k = 4096 (16x16x32 f16 MFMA, 8 waves of 128
+// rows: ~85 us per pass).  Small tiles cost more per output (the unpack is
+// amortised over fewer rows), so the choice trades tile efficiency against
+// how well the grid fills whole passes.
+struct PrefillForm {
+  uint32_t waves, bm, sets;
+};
+struct PrefillFormCost {
+  PrefillForm f;
+  uint32_t pass_cost;
+};
+constexpr PrefillFormCost kPrefillForms[] = {
+    {{8, 128, 1}, 1000}, {{8, 96, 1}, 780}, {{4, 128, 2}, 555}, {{4, 96, 2}, 450},
+    {{4, 64, 2}, 355},   {{4, 128, 1}, 640}, {{4, 96, 1}, 520}, {{4, 64, 1}, 400}};
+// two sets need an even group count; two INT8 rings of 128-row tiles do not fit in LDS
+constexpr bool prefill_form_ok(PrefillForm f, uint32_t k, uint32_t bits) {
+  return f.sets == 1 || ((k / 128) % 2 == 0 && (bits == 4 || f.bm <= 96));
 }
-// columns of each output per tile-kernel workgroup
-constexpr uint32_t prefill_bn(uint32_t m, uint32_t n) { return 16u * prefill_waves(m, n); }
-// Rows per tile-kernel workgroup: 64 when a grid of 4-wave 64-row workgroups
-// still fits one pass over the compute units (then the 128-row grid would
-// leave many idle: 128 < m <= 256 at n = 4096), else 128.
-constexpr uint32_t prefill_bm(uint32_t m, uint32_t n) {
-  return (uint64_t)((m + 63) / 64) * ((n + 63) / 64) <= kComputeUnits ? 64u : kPrefillBM;
+constexpr uint64_t prefill_wgs(PrefillForm f, uint32_t m, uint32_t n) {
+  return (uint64_t)((m + f.bm - 1) / f.bm) * ((n + 16 * f.waves - 1) / (16 * f.waves));
 }
-// 4-wave tiles run the groups as two halves on two sets of 4 waves when the
-// group count is even (128-row tiles: INT4 only, whose two rings fit in LDS),
-// else on one set
-constexpr int prefill_ksplit(uint32_t m, uint32_t n, uint32_t k, uint32_t bits) {
-  return prefill_waves(m, n) == 4 && (k / 128) % 2 == 0 && (prefill_bm(m, n) == 64 || bits == 4) ? 2 : 1;
+// predicted time: whole passes at the full cost, a partial last pass at
+// 0.7 + 0.3 x its share of the compute units (fewer workgroups contend less)
+constexpr uint64_t prefill_cost(const PrefillFormCost& c, uint32_t m, uint32_t n) {
+  const uint64_t wgs = prefill_wgs(c.f, m, n);
+  const uint64_t full = wgs / kComputeUnits, rem = wgs % kComputeUnits;
+  return c.pass_cost * (1000 * full + (rem ? 700 + 300 * rem / kComputeUnits : 0));
+}
+// the form with the least predicted time (the first of equals)
+constexpr PrefillForm prefill_form(uint32_t m, uint32_t n, uint32_t k, uint32_t bits) {
+  PrefillForm best = kPrefillForms[0].f;
+  uint64_t best_cost = ~0ull;
+  for (const PrefillFormCost& c : kPrefillForms) {
+    if (!prefill_form_ok(c.f, k, bits)) continue;
+    const uint64_t t = prefill_cost(c, m, n);
+    if (t < best_cost) {
+      best_cost = t;
+      best = c.f;
+    }
+  }
+  return best;
 }
 constexpr uint32_t kMaxN = 1u << 26;   // keeps 32-bit per-lane byte offsets in range (16 rows x N x 4 B)
 constexpr uint32_t kMaxK = 1u << 24;

@@ -242,9 +242,8 @@ __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3
 }
 
 // BITS = 4 (W4A16) or 8 (W8A16: two packed words per 8 k of a column).
-// BM = rows of x per workgroup: 128, or 64 when a grid of such tiles still
-// fits one pass over the compute units and one of 128-row tiles would leave
-// many of them idle (128 < m <= 256 at n = 4096).
+// BM = rows of x per workgroup: 128, 96 or 64 (see prefill_form: smaller
+// tiles where a grid of larger ones would fill the compute units badly).
 // KS = 1, or 2: the workgroup holds two sets of WAVES waves, each with its
 // own ring, that run the same loop over the two halves of the groups (so two
 // waves share each SIMD and hide each other's waits); the second set's
@@ -494,13 +493,13 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
     uint16_t* out = p.out[q];
     if (kAligned) {
       constexpr int CPR = BN / 8;                    // 16-byte chunks per tile row
-      static_assert(BM * CPR % TT == 0, "row chunks split evenly over the threads");
+      constexpr int NCH = BM * CPR;                  // 16-byte chunks of the tile
 #pragma unroll
-      for (int i = 0; i < BM * CPR / TT; ++i) {
+      for (int i = 0; i < (NCH + TT - 1) / TT; ++i) {
         const uint32_t c = i * TT + tid;
         const uint32_t row = c / CPR, cc = c % CPR;
         const uint32_t gr = m0 + row, gc = n0 + cc * 8;
-        if (gr < M && gc < N)
+        if ((NCH % TT == 0 || c < (uint32_t)NCH) && gr < M && gc < N)
           *reinterpret_cast<uint4*>(out + (size_t)gr * N + gc) =
               *reinterpret_cast<const uint4*>(tile + row * OUT_LD + ((cc * 8) ^ (16 * ((row >> 2) & 3))));
       }
@@ -536,16 +535,24 @@ hipError_t launch_aligned_or_not(const QkvProblem& p, hipStream_t stream) {
                       : launch_variant<BITS, WAVES, KAIO_PREFILL_XDIST, false, BM, KS>(p, stream);
 }
 
+// the form prefill_form() picks for this problem
 template <int BITS>
 hipError_t launch_prefill_bits(const QkvProblem& p, hipStream_t stream) {
-  if (prefill_waves(p.m, p.n) == 8) return launch_aligned_or_not<BITS, 8, 128, 1>(p, stream);
-  const bool split = prefill_ksplit(p.m, p.n, p.k, BITS) == 2;
-  if (prefill_bm(p.m, p.n) == 128) {
-    if constexpr (BITS == 4)
-      if (split) return launch_aligned_or_not<BITS, 4, 128, 2>(p, stream);
-    return launch_aligned_or_not<BITS, 4, 128, 1>(p, stream);
+  const PrefillForm f = prefill_form(p.m, p.n, p.k, BITS);
+  switch (f.waves * 10000 + f.bm * 10 + f.sets) {
+    case 81281: return launch_aligned_or_not<BITS, 8, 128, 1>(p, stream);
+    case 80961: return launch_aligned_or_not<BITS, 8, 96, 1>(p, stream);
+    case 41282:
+      if constexpr (BITS == 4) return launch_aligned_or_not<BITS, 4, 128, 2>(p, stream);
+      break;
+    case 40962: return launch_aligned_or_not<BITS, 4, 96, 2>(p, stream);
+    case 40642: return launch_aligned_or_not<BITS, 4, 64, 2>(p, stream);
+    case 41281: return launch_aligned_or_not<BITS, 4, 128, 1>(p, stream);
+    case 40961: return launch_aligned_or_not<BITS, 4, 96, 1>(p, stream);
+    case 40641: return launch_aligned_or_not<BITS, 4, 64, 1>(p, stream);
+    default: break;
   }
-  return split ? launch_aligned_or_not<BITS, 4, 64, 2>(p, stream) : launch_aligned_or_not<BITS, 4, 64, 1>(p, stream);
+  return hipErrorInvalidValue;   // a form without a kernel (prefill_form_ok rules it out)
 }
 
 }  // namespace

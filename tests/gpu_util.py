@@ -26,3 +26,26 @@ def qkv_on_gpu(x, w, s, bits=4, **kw):
     outs = fn(to_dev(x), *[to_dev(a) for a in w], *[to_dev(a) for a in s], **kw)
     torch.cuda.synchronize()
     return [to_host(o) for o in outs]
+
+
+# Forms of the tile kernel (waves per set, rows per tile, sets of waves), as kaio_qkv_plan reports them.
+TILE_FORMS = [(8, 128, 1), (8, 96, 1), (4, 128, 2), (4, 96, 2), (4, 64, 2), (4, 128, 1), (4, 96, 1), (4, 64, 1)]
+
+
+def shape_for_form(form, bits, aligned, ks=(256, 384, 512, 640)):
+    """The smallest problem (m * n * k) of a coarse grid -- m ragged against every tile height,
+    n % 8 == 0 or not -- on which the library's plan runs the tile kernel in `form`; None if
+    no problem of the grid does."""
+    import int4_group_quantized_w4a16_amd as kaio
+    best = None
+    for k in ks:
+        for j in range(1, 33):
+            n = 64 * j if aligned else 64 * j - 3
+            for m in range(129, 2601, 13):
+                if best is not None and m * n * k >= best[0]:
+                    break
+                p = kaio.kaio_qkv_plan(m, n, k, bits)
+                if (p["waves"], p["rows"], p["sets"]) == tuple(form):
+                    best = (m * n * k, m, n, k)
+                    break
+    return None if best is None else best[1:]

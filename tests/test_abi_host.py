@@ -271,3 +271,30 @@ def test_binding_refuses_cpu_tensors():
         kaio.kaio_gemm_f16f32(torch.zeros(2, 2, dtype=torch.float16), torch.zeros(2, 2, dtype=torch.float16))
     with pytest.raises(ValueError, match="no CPU fallback"):
         kaio.kaio_dequant_group_bwd(torch.zeros(2, 4), torch.zeros(2, 1), 4)
+
+
+def test_qkv_plan_validation_and_forms():
+    L = kaio.lib()
+    plan = (ctypes.c_uint32 * 5)()
+    assert L.kaio_qkv_plan(256, 64, 256, 5, plan) == 1 and "bits" in kaio.kaio_last_error()
+    assert L.kaio_qkv_plan(256, 64, 256, 4, None) == 1 and "plan is null" in kaio.kaio_last_error()
+    assert L.kaio_qkv_plan(256, 64, 200, 4, plan) == 2 and "multiple of group_size" in kaio.kaio_last_error()
+    assert L.kaio_qkv_plan(0, 64, 256, 4, plan) == 0 and list(plan) == [0, 0, 0, 0, 0]
+    # m <= 128: the split-K kernel, 3 outputs x strips
+    p = kaio.kaio_qkv_plan(8, 4096, 4096)
+    assert p["kernel"] == "split_k" and p["workgroups"] == 3 * 4096 // p["rows"]
+    from tests.gpu_util import TILE_FORMS, shape_for_form
+    for bits in (4, 8):
+        for m, n, k in ((129, 4096, 4096), (777, 1000, 384), (2048, 4096, 4096), (5000, 12288, 4224)):
+            p = kaio.kaio_qkv_plan(m, n, k, bits)
+            assert p["kernel"] == "tile" and (p["waves"], p["rows"], p["sets"]) in TILE_FORMS
+            assert p["workgroups"] == -(-m // p["rows"]) * -(-n // (16 * p["waves"]))
+            if p["sets"] == 2:   # two sets split an even group count; no two INT8 128-row rings
+                assert (k // 128) % 2 == 0 and not (bits == 8 and p["rows"] == 128)
+        # the prefill workload keeps the 8-wave 128-row form
+        p = kaio.kaio_qkv_plan(2048, 4096, 4096, bits)
+        assert (p["waves"], p["rows"], p["sets"]) == (8, 128, 1)
+        # every form the kernels have is chosen for some problem (INT8 has no two-set 128-row form)
+        for f in TILE_FORMS:
+            found = shape_for_form(f, bits, True)
+            assert (found is None) == (bits == 8 and f == (4, 128, 2)), (bits, f, found)

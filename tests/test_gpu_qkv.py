@@ -14,7 +14,7 @@ from oracle import compare
 from oracle.int4 import pack_int4
 from oracle.qkv import qkv_project
 from tests.conftest import load_golden
-from tests.gpu_util import DEV, qkv_on_gpu, to_dev, to_host
+from tests.gpu_util import DEV, TILE_FORMS, qkv_on_gpu, shape_for_form, to_dev, to_host
 from tests.test_oracle_qkv import build_x
 
 pytestmark = pytest.mark.gpu
@@ -69,14 +69,12 @@ def test_tiny_config_all_outputs():
     (16, 128, 512), (17, 64, 256), (24, 200, 384), (32, 130, 384), (33, 64, 512), (48, 96, 1152),
     (63, 40, 256), (64, 200, 256), (65, 64, 256), (96, 136, 384), (127, 72, 256), (128, 64, 640),
     (129, 64, 256),
-    # tile kernel with 128-row tiles and 4 waves (64-row tiles would not fit in one pass), then
-    # 8 waves (neither 4-wave grid would); ragged and n % 8 != 0
+    # tile kernel on larger grids, ragged and n % 8 != 0, one or two groups (test_every_tile_form
+    # covers each form of the tile kernel)
     (1100, 1000, 256), (1100, 1001, 128), (2100, 1000, 256), (2100, 1001, 128),
-    # more than 32 groups in 64-row and in 128-row 4-wave tiles (scale chunk reloads); 64-row
-    # tiles split the groups over two sets of waves when their count is even (66: 33 per set)
+    # more than 32 groups (scale chunk reloads), per set where the groups are split over two sets
+    # of waves (66 and 34 groups: 33 and 17 per set), and odd counts (97, 35: one set)
     (200, 520, 12416), (1100, 1000, 4480), (150, 264, 8448), (150, 261, 8448),
-    # 128-row 4-wave tiles with the groups split over two sets (tight rings: one weight slot,
-    # 8-group scale chunks; 17 groups per set)
     (1100, 1000, 4352), (1100, 1001, 4352),
     # split-K: waves with exactly two groups on ragged strips (the straight-line path), and
     # waves with three or more groups, odd counts included (the loop; 8 and 16 x rows kept)
@@ -111,9 +109,27 @@ def test_prefill_config_all_outputs():
     (1024, 4096, 1024),   # 8-wave tile kernel: 8 x 32 tiles of 128 x 128, walked in 4 x 8 super-blocks
 ])
 def test_tile_kernel_super_block_grids_all_outputs(M, N, K):
+    plan = kaio.kaio_qkv_plan(M, N, K)
+    assert (plan["waves"], plan["rows"], plan["sets"]) == {256: (4, 64, 2), 200: (4, 64, 2), 512: (4, 128, 2),
+                                                           1024: (8, 128, 1)}[M]
     inp = workloads.qkv_inputs(M, N, K, seed=M + N + K)
     worst = check(qkv_on_gpu(inp.x, inp.w, inp.s), inp)
     print(f"{M}x{N}x{K} (all outputs): max |d|/tol = {worst:.3f}")
+
+
+@pytest.mark.parametrize("aligned", [True, False], ids=["n%8==0", "n%8!=0"])
+@pytest.mark.parametrize("form", TILE_FORMS, ids=lambda f: f"{f[0]}w-{f[1]}rows-{f[2]}sets")
+def test_every_tile_form(form, aligned):
+    # the smallest problem of a coarse grid that the plan runs in this form: m ragged against the
+    # tile height, n ragged against the tile width
+    shape = shape_for_form(form, 4, aligned)
+    assert shape is not None, f"no problem selects {form}"
+    M, N, K = shape
+    plan = kaio.kaio_qkv_plan(M, N, K)
+    assert (plan["waves"], plan["rows"], plan["sets"]) == form
+    inp = workloads.qkv_inputs(M, N, K, seed=M * 7 + N * 3 + K + form[1])
+    worst = check(qkv_on_gpu(inp.x, inp.w, inp.s), inp)
+    print(f"{form} {M}x{N}x{K}: max |d|/tol = {worst:.3f}")
 
 
 @pytest.mark.parametrize("M", [4, 40])

@@ -14,7 +14,7 @@ from oracle import compare
 from oracle.int8 import pack_int8
 from oracle.qkv import qkv_project
 from tests.conftest import load_golden
-from tests.gpu_util import DEV, qkv_on_gpu, to_dev, to_host
+from tests.gpu_util import DEV, TILE_FORMS, qkv_on_gpu, shape_for_form, to_dev, to_host
 from tests.test_oracle_qkv8 import golden_inputs
 
 pytestmark = pytest.mark.gpu
@@ -61,16 +61,30 @@ def test_workloads_all_outputs(cfg):
     # m <= 16, <= 32, <= 64, <= 128 (one, two and four row blocks), full and ragged
     (9, 100, 128), (16, 128, 512), (12, 64, 6272), (24, 200, 384), (32, 130, 384), (33, 64, 512),
     (48, 96, 1152), (64, 200, 256), (65, 64, 256), (100, 136, 384), (128, 64, 640), (40, 72, 4480),
-    # tile kernel: 64-row tiles (4 waves), 128-row tiles with 4 and with 8 waves, n % 8 == 0 and
-    # not, more than 32 groups (scale chunk reload)
+    # tile kernel (test_every_tile_form covers each form), n % 8 == 0 and not, more than 32
+    # groups (scale chunk reloads), groups split over two sets of waves (even counts) or not
     (129, 64, 256), (130, 200, 256), (300, 24, 640), (200, 1000, 1024), (129, 136, 8320),
     (1100, 1000, 4480), (1100, 1001, 256), (2100, 1000, 256), (2100, 1001, 128),
-    # 64-row tiles with the groups split over two sets of waves (even group counts)
     (150, 264, 8448), (150, 261, 8448), (256, 4096, 4096),
 ])
 def test_ragged_shapes(M, N, K):
     inp = workloads.qkv8_inputs(M, N, K, seed=M * 7919 + N * 31 + K + 1)
     check(run(inp.x, inp.w, inp.s), inp)
+
+
+@pytest.mark.parametrize("aligned", [True, False], ids=["n%8==0", "n%8!=0"])
+@pytest.mark.parametrize("form", [f for f in TILE_FORMS if f != (4, 128, 2)],
+                         ids=lambda f: f"{f[0]}w-{f[1]}rows-{f[2]}sets")
+def test_every_tile_form(form, aligned):
+    # as for W4A16; INT8 has no two-set 128-row form (two such rings do not fit in LDS)
+    shape = shape_for_form(form, 8, aligned)
+    assert shape is not None, f"no problem selects {form}"
+    M, N, K = shape
+    plan = kaio.kaio_qkv_plan(M, N, K, 8)
+    assert (plan["waves"], plan["rows"], plan["sets"]) == form
+    inp = workloads.qkv8_inputs(M, N, K, M * 7 + N * 3 + K + form[1] + 1)
+    worst = check(run(inp.x, inp.w, inp.s), inp)
+    print(f"W8A16 {form} {M}x{N}x{K}: max |d|/tol = {worst:.3f}")
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 4096, 4096), (1024, 4096, 1024)])
