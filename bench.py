@@ -591,10 +591,10 @@ def main():
             "traffic": measured_traffic("qkv_decode", "qkv_decode.hip", dbytes),
             "read_roof": rr, "frac_of_read_roof": round(rr["us_per_call"] / (dms * 1e3), 4) if rr else None,
             "strip_read_roof": sr}
-        # batched decode and short prefill chunks on the same rotated weights (split-K kernel up
-        # to m = 128, the tile kernel's 64-row and 128-row 4-wave forms at 256 and 512)
+        # batched decode and prefill chunks on the same rotated weights (split-K kernel up to
+        # m = 128, then the tile kernel in the form kaio_qkv_plan reports)
         batched = []
-        for bm in ((16, 32, 64, 128, 256, 512) if args.only != "decode" else ()):
+        for bm in ((16, 32, 64, 128, 256, 512, 768, 1024, 1536) if args.only != "decode" else ()):
             xb = t(np.random.default_rng(c["seed"] + 100 + bm).standard_normal((bm, K)).astype(np.float16))
             ob = [torch.empty((bm, N), dtype=torch.float16, device=dev) for _ in range(3)]
             bstep = lambda i: kaio.kaio_qkv_w4a16(xb, *sets[i % R][0], *sets[i % R][1], *ob)
@@ -603,12 +603,15 @@ def main():
             bgbs = bbytes / (bms * 1e-3) / 1e9
             btf = 2.0 * bm * N * K * 3 / (bms * 1e-3) / 1e12
             log(f"[bench] batched decode m={bm}: {bms * 1e3:.2f} us/call, {bgbs:.0f} GB/s, {btf:.1f} TFLOP/s")
+            pl = kaio.kaio_qkv_plan(bm, N, K)
             batched.append({"m": bm, "us_per_call": round(bms * 1e3, 3), "gbs": round(bgbs, 1),
-                            "tflops": round(btf, 2), "hbm_frac": round(bgbs / PEAK_HBM_GBS, 4)})
+                            "tflops": round(btf, 2), "hbm_frac": round(bgbs / PEAK_HBM_GBS, 4),
+                            "form": pl["kernel"] if pl["kernel"] == "split_k" else
+                            f"tile {pl['waves']} waves x {pl['rows']} rows x {pl['sets']} set(s)"})
             del xb, ob
         if batched:
             secondary["qkv_batched_decode"] = {
-                "workload": "x f16[m,4096] for m = 16, 32, 64, 128, 256, 512; weights and rotation as qkv_decode",
+                "workload": "x f16[m,4096] for m = 16 ... 1536; weights and rotation as qkv_decode",
                 "points": batched, "bound": "hbm"}
         del sets, x, outs
 
