@@ -298,7 +298,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   // offset (the host-side size limits keep the offsets below 2^32), which the
   // loads take in their scalar-base form: no per-lane 64-bit address math.
   const char* xblk = reinterpret_cast<const char*>(p.x + (size_t)m0 * K + (size_t)g0 * kGroup);
-  uint32_t xoff[XPER];         // byte offset (within row block m0, group 0) of this lane's chunk
+  uint32_t xoff[XPER];         // byte offset (row block m0, the set's first group) of this lane's chunk
 #pragma unroll
   for (int i = 0; i < XPER; ++i) {
     const uint32_t slot = (i * WAVES + wave) * 64 + lane;
