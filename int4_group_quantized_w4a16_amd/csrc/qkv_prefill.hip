@@ -536,20 +536,23 @@ hipError_t launch_aligned_or_not(const QkvProblem& p, hipStream_t stream) {
 }
 
 // the form prefill_form() picks for this problem
+constexpr uint32_t form_code(uint32_t waves, uint32_t bm, uint32_t sets) { return (waves * 1000 + bm) * 10 + sets; }
+
+// the form prefill_form() picks for this problem
 template <int BITS>
 hipError_t launch_prefill_bits(const QkvProblem& p, hipStream_t stream) {
   const PrefillForm f = prefill_form(p.m, p.n, p.k, BITS);
-  switch (f.waves * 10000 + f.bm * 10 + f.sets) {
-    case 81281: return launch_aligned_or_not<BITS, 8, 128, 1>(p, stream);
-    case 80961: return launch_aligned_or_not<BITS, 8, 96, 1>(p, stream);
-    case 41282:
+  switch (form_code(f.waves, f.bm, f.sets)) {
+    case form_code(8, 128, 1): return launch_aligned_or_not<BITS, 8, 128, 1>(p, stream);
+    case form_code(8, 96, 1): return launch_aligned_or_not<BITS, 8, 96, 1>(p, stream);
+    case form_code(4, 128, 2):
       if constexpr (BITS == 4) return launch_aligned_or_not<BITS, 4, 128, 2>(p, stream);
       break;
-    case 40962: return launch_aligned_or_not<BITS, 4, 96, 2>(p, stream);
-    case 40642: return launch_aligned_or_not<BITS, 4, 64, 2>(p, stream);
-    case 41281: return launch_aligned_or_not<BITS, 4, 128, 1>(p, stream);
-    case 40961: return launch_aligned_or_not<BITS, 4, 96, 1>(p, stream);
-    case 40641: return launch_aligned_or_not<BITS, 4, 64, 1>(p, stream);
+    case form_code(4, 96, 2): return launch_aligned_or_not<BITS, 4, 96, 2>(p, stream);
+    case form_code(4, 64, 2): return launch_aligned_or_not<BITS, 4, 64, 2>(p, stream);
+    case form_code(4, 128, 1): return launch_aligned_or_not<BITS, 4, 128, 1>(p, stream);
+    case form_code(4, 96, 1): return launch_aligned_or_not<BITS, 4, 96, 1>(p, stream);
+    case form_code(4, 64, 1): return launch_aligned_or_not<BITS, 4, 64, 1>(p, stream);
     default: break;
   }
   return hipErrorInvalidValue;   // a form without a kernel (prefill_form_ok rules it out)
