@@ -636,13 +636,16 @@ def main():
         torch.cuda.synchronize()
         host["w8_decode"] = [o.cpu().numpy() for o in outs]
         rr = None if args.no_roof else read_roof(dbytes, R, replays, stream, dev)
+        sr8 = None if args.no_roof else strip_roof([st[0] for st in sets], replays, stream, dev)
+        if sr8:
+            log(f"[bench] the INT8 weights read by 64-column strips: {sr8['strip64']['us_per_call']:.2f} us/call")
         secondary["qkv8_decode"] = {
             "workload": "W8A16: x f16[8,4096], 3x u32[1024,4096] (INT8), 3x f16[32,4096]; 11 rotated weight "
                         "sets, 44 calls per HIP graph replay",
             "us_per_call": round(dms * 1e3, 3), "value": round(gbs, 1), "unit": "GB/s", "bound": "hbm",
             "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": dbytes,
             "read_roof": rr, "frac_of_read_roof": round(rr["us_per_call"] / (dms * 1e3), 4) if rr else None,
-            "strip_read_roof": sr}
+            "strip_read_roof": sr8}
         del sets, x, outs
         c = workloads.QKV8_PREFILL
         M, N, K = c["M"], c["N"], c["K"]
