@@ -11,7 +11,7 @@ import torch
 import int4_group_quantized_w4a16_amd as kaio
 from int4_group_quantized_w4a16_amd import workloads
 from oracle import compare
-from oracle.int4 import pack_int4
+from oracle.int4 import pack_int4, unpack_int4
 from oracle.qkv import qkv_project
 from tests.conftest import load_golden
 from tests.gpu_util import DEV, TILE_FORMS, qkv_on_gpu, shape_for_form, to_dev, to_host
@@ -130,6 +130,29 @@ def test_every_tile_form(form, aligned):
     inp = workloads.qkv_inputs(M, N, K, seed=M * 7 + N * 3 + K + form[1])
     worst = check(qkv_on_gpu(inp.x, inp.w, inp.s), inp)
     print(f"{form} {M}x{N}x{K}: max |d|/tol = {worst:.3f}")
+
+
+@pytest.mark.parametrize("M", [8, 40, 200])
+def test_non_finite_inputs_stay_in_their_rows(M):
+    # IEEE propagation, row by row: a NaN in x row 1 makes that row NaN everywhere; +inf in row 2
+    # at k0 gives +-inf by the sign of q[k0, n] (NaN where that weight is 0); every other row is
+    # finite and within tolerance (MFMA rows do not mix).  M = 8, 40: split-K kernel; 200: tile.
+    N, K, k0 = 72, 384, 137
+    inp = workloads.qkv_inputs(M, N, K, seed=600 + M)
+    x = inp.x.copy()
+    x[1, 5] = np.float16(np.nan)
+    x[2, k0] = np.float16(np.inf)
+    outs = qkv_on_gpu(x, inp.w, inp.s)
+    finite = [r for r in range(M) if r not in (1, 2)]
+    ys, ts = qkv_project(inp.x[finite], inp.w, inp.s)
+    for o, wq, y, t in zip(outs, inp.w, ys, ts):
+        assert np.isnan(o[1]).all()
+        q = unpack_int4(wq)[k0]                      # signed INT4 values of packed row k0 // 8
+        assert np.array_equal(np.isnan(o[2]), q == 0)
+        assert np.array_equal(np.sign(o[2][q != 0]), np.sign(q[q != 0]).astype(np.float16))
+        assert np.isinf(o[2][q != 0]).all()
+        bad, ratio = compare.excess(o[finite], y, compare.qkv_tolerance(y, t))
+        assert bad == 0, f"{bad} finite outputs outside tolerance, max |d|/tol = {ratio:.3f}"
 
 
 @pytest.mark.parametrize("M", [4, 40])
