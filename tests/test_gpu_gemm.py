@@ -81,3 +81,27 @@ def test_ragged_reduction_exact_integers_bitwise(M, N, K):
     b = rng.integers(-4, 5, size=(K, N)).astype(np.float16)
     c, _ = gemm(a, b)
     assert np.array_equal(run(a, b), c.astype(np.float32))
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 264, 256), (257, 259, 72)])
+def test_non_finite_inputs_stay_in_their_rows_and_columns(M, N, K):
+    # IEEE propagation: NaN in A row 3 -> C row 3 NaN; +inf in B column 7 at k0 -> column 7 is
+    # +-inf by the sign of A[:, k0] (NaN where it is 0 or where row 3's NaN meets it); the rest of
+    # C is finite and matches the oracle (the direct-load path and the register-staged fallback).
+    a, b = workloads.gemm_inputs(M, N, K, 41 + M)
+    k0 = 5
+    a[:, k0] = np.where(np.arange(M) % 5 == 0, np.float16(0), a[:, k0])
+    a[3, 11] = np.float16(np.nan)
+    b[k0, 7] = np.float16(np.inf)
+    c = run(a, b)
+    assert np.isnan(c[3]).all()
+    rows = np.array([r for r in range(M) if r != 3])
+    col7 = c[rows, 7]
+    ak = a[rows, k0].astype(np.float64)
+    assert np.array_equal(np.isnan(col7), ak == 0)
+    assert np.array_equal(np.sign(col7[ak != 0]), np.sign(ak[ak != 0]).astype(np.float32))
+    cols = np.array([j for j in range(N) if j != 7])
+    a2, b2 = a[rows], b[:, cols]
+    ref, t = gemm(a2, b2)
+    bad, ratio = compare.excess(c[np.ix_(rows, cols)], ref, compare.gemm_tolerance(t))
+    assert bad == 0, f"{bad} finite outputs outside tolerance, max |d|/tol = {ratio:.3f}"
