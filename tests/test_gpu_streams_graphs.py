@@ -91,8 +91,9 @@ def capture(fn):
     return g
 
 
-# K = 4096 at M = 8 gives every split-K wave exactly two groups (its straight-line path)
-@pytest.mark.parametrize("M,K", [(8, 384), (8, 4096), (24, 512), (40, 1024), (100, 640), (300, 384)])
+# K = 4096 at M = 8 gives every split-K wave exactly two groups (its straight-line path); M = 300
+# runs the tile kernel with one set of waves (K = 384: 3 groups) and with two (K = 512)
+@pytest.mark.parametrize("M,K", [(8, 384), (8, 4096), (24, 512), (40, 1024), (100, 640), (300, 384), (300, 512)])
 def test_qkv_graph_replay_uses_current_inputs(M, K):
     N = 136
     inp, x, w, s = qkv_case(M, N, K, 7)
