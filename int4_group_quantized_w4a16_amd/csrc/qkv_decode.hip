@@ -82,8 +82,11 @@ __device__ __forceinline__ T load_w(const T* p) {
   else return *p;
 }
 constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, kBufferFlags);
+// records = -1: no range limit (every offset is in bounds by construction);
+// 0: every load through the descriptor is out of range -- it returns zeros
+// without touching memory (still one load for the wait counts)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int records = -1) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, records, kBufferFlags);
 }
 template <int V, int kPolicy>
 __device__ __forceinline__ typename WordVec<V>::T buf_words(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -108,7 +111,10 @@ __device__ __forceinline__ typename HalfVec<V>::T buf_halves(__amdgpu_buffer_rsr
 // XR = rows of x a wave keeps per group (a multiple of 4, at most 16*RT;
 // 8 when m <= 8, which leaves registers for two groups in flight).
 // BITS = 4 (W4A16: one packed word per 8 k of a column) or 8 (W8A16: two).
-template <int BITS, int RT, int RSPLIT, int VEC, int WAVES, bool kFull, int XR>
+// kTrim: some wave's group range is not exactly two chunks (its loop runs
+// past the range), and the weight loads past it go through a zero-range
+// descriptor (16-wave buffer-load configurations, whole strips).
+template <int BITS, int RT, int RSPLIT, int VEC, int WAVES, bool kFull, int XR, bool kTrim = false>
 __global__ void __launch_bounds__(WAVES * 64, 1)
 qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   constexpr int THREADS = WAVES * kWave;
@@ -201,11 +207,16 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   };
   // Loads of GCHUNK groups starting at g0.  Groups past the wave's range are
   // clamped to its last group (loaded, never used) so that every chunk issues
-  // the same loads and the compiler can keep the next chunk in flight.
-  auto load_chunk = [&](uint32_t g0, Chunk& c) {
+  // the same loads and the compiler can keep the next chunk in flight.  With
+  // kTrim, the weight loads of such a group go through a zero-range
+  // descriptor instead: a repeat of streamed (non-temporal) words was often
+  // fetched from memory again (n = 4096, k = 8192, m = 8: 1.17x the
+  // algorithmic bytes).
+  auto load_chunk = [&](uint32_t g0, Chunk& c, bool checked) {
 #pragma unroll
     for (int gi = 0; gi < GCHUNK; ++gi) {
-      const uint32_t g = (g0 + gi < g_end) ? g0 + gi : g_end - 1;
+      const bool live = !checked || g0 + gi < g_end;   // checked = false: inside the range
+      const uint32_t g = live ? g0 + gi : g_end - 1;
       // x first: loads complete in issue order, so the LDS copy of x (needed
       // before any MFMA) need not wait for the weights of later k-steps
       if constexpr (kBuf) {
@@ -217,7 +228,8 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
           for (int j = 0; j < WPK; ++j) {
-            const __amdgpu_buffer_rsrc_t wr = rsrc_of(w + ((size_t)g * PR + ks * 4 * WPK + j) * N);
+            const __amdgpu_buffer_rsrc_t wr =
+                rsrc_of(w + ((size_t)g * PR + ks * 4 * WPK + j) * N, kTrim && kFull && !live ? 0 : -1);
             if (kFull) {
               const WV v = buf_words<VEC, kWPolicy>(wr, woff);
               __builtin_memcpy(c.wv[gi][ks][j], &v, sizeof(v));
@@ -324,18 +336,18 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
     Chunk ca, cb;
     if (g_end - g_begin == 2 * GCHUNK) {
       // exactly two chunks (every wave at m <= 16, k = 4096): straight-line
-      load_chunk(g_begin, ca);
-      load_chunk(g_begin + GCHUNK, cb);
+      load_chunk(g_begin, ca, false);
+      load_chunk(g_begin + GCHUNK, cb, false);
       compute_chunk(g_begin, ca, false);
       compute_chunk(g_begin + GCHUNK, cb, false);
     } else {
-      load_chunk(g_begin, ca);
-      load_chunk(g_begin + GCHUNK, cb);
+      load_chunk(g_begin, ca, true);
+      load_chunk(g_begin + GCHUNK, cb, true);
       for (uint32_t g0 = g_begin; g0 < g_end; g0 += 2 * GCHUNK) {
         compute_chunk(g0, ca, true);
-        load_chunk(g0 + 2 * GCHUNK, ca);
+        load_chunk(g0 + 2 * GCHUNK, ca, true);
         compute_chunk(g0 + GCHUNK, cb, true);
-        load_chunk(g0 + 3 * GCHUNK, cb);
+        load_chunk(g0 + 3 * GCHUNK, cb, true);
       }
     }
   }
@@ -367,6 +379,16 @@ hipError_t launch_split_k(const QkvProblem& p, hipStream_t stream) {
   constexpr uint32_t BN = 16 * VEC;
   const uint32_t nstrips = (p.n + BN - 1) / BN;
   const dim3 grid(3 * nstrips), block(WAVES * kWave);
+  // every wave with exactly two chunks (k = 4096 at 16 waves): the straight-line path only
+  constexpr uint32_t KSPLIT = WAVES / RSPLIT;
+  const bool straight = p.k / kGroup == 2 * GCHUNK * KSPLIT;
+  if constexpr (WAVES == 16) {
+    if ((kOnlyFull || p.n % BN == 0) && !straight) {
+      hipLaunchKernelGGL((qkv_decode_kernel<BITS, RT, RSPLIT, VEC, WAVES, true, XR, true>), grid, block, 0, stream,
+                         p, nstrips);
+      return hipGetLastError();
+    }
+  }
   if (kOnlyFull || p.n % BN == 0)
     hipLaunchKernelGGL((qkv_decode_kernel<BITS, RT, RSPLIT, VEC, WAVES, true, XR>), grid, block, 0, stream, p,
                        nstrips);
