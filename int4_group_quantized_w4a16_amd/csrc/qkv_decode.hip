@@ -114,7 +114,10 @@ __device__ __forceinline__ typename HalfVec<V>::T buf_halves(__amdgpu_buffer_rsr
 // kTrim: some wave's group range is not exactly two chunks (its loop runs
 // past the range), and the weight loads past it go through a zero-range
 // descriptor (16-wave buffer-load configurations, whole strips).
-template <int BITS, int RT, int RSPLIT, int VEC, int WAVES, bool kFull, int XR, bool kTrim = false>
+// NG > 0: every wave issues the loads of all its groups (at most NG) at once
+// and x goes to LDS by direct loads, which frees the registers that holding
+// x would take (16 waves, whole strips, m <= 8, at most NG groups per wave).
+template <int BITS, int RT, int RSPLIT, int VEC, int WAVES, bool kFull, int XR, bool kTrim = false, int NG = 0>
 __global__ void __launch_bounds__(WAVES * 64, 1)
 qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   constexpr int THREADS = WAVES * kWave;
@@ -135,8 +138,26 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   constexpr bool kNatural = RT >= 2 || BITS == 8;
   static_assert(XR % 4 == 0 && XR <= 16 * RT, "x rows per wave");
   constexpr int XLD = kGroup / 8 + 1;           // 16-byte chunks per padded LDS row of x
-  __shared__ float red[KSPLIT][ROWS][BN];
-  __shared__ uint4 xl[WAVES][XROWS * XLD];
+  static_assert(NG == 0 || (WAVES == 16 && kFull && RT == 1 && XR == 8 && BITS == 4 && NG <= 4),
+                "all groups in flight: the 16-wave m <= 8 configuration only");
+  // LDS: the reduction buffer, and per wave either one padded x slice (x
+  // staged through registers) or NG unpadded, swizzled ones (direct loads;
+  // the reduction buffer then reuses them, once every wave is done with x)
+  using RedT = float[KSPLIT][ROWS][BN];
+  RedT* red_p;
+  uint4* xl_base;
+  if constexpr (NG == 0) {
+    __shared__ float red_s[KSPLIT][ROWS][BN];
+    __shared__ uint4 xl[WAVES][XROWS * XLD];
+    red_p = &red_s;
+    xl_base = &xl[0][0];
+  } else {
+    static_assert(KSPLIT * ROWS * BN * 4 <= WAVES * NG * XROWS * 16 * 16, "reduction buffer fits the x slices");
+    __shared__ uint4 xd[WAVES * NG * XROWS * 16];
+    red_p = reinterpret_cast<RedT*>(xd);
+    xl_base = xd;
+  }
+  RedT& red = *red_p;
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
@@ -182,7 +203,7 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
     const uint32_t lr = 16 * r + l16;
     xfrag[r] = (lr < xvalid ? lr : xvalid - 1) * XLD + kb;
   }
-  uint4* const xw = xl[wave];
+  uint4* const xw = xl_base + wave * (NG == 0 ? XROWS * XLD : NG * XROWS * 16);
   // lane (kb, c) of k-step ks holds packed rows WPK*(4ks + kb) + j, j < WPK:
   // the 8 consecutive k of its B operand.  Byte offset from the row
   // PR*g + 4*WPK*ks + j of the load's base:
@@ -327,7 +348,71 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
     }
   };
 
-  if (g_begin < g_end) {
+  if constexpr (NG > 0) {
+    // Every group of the wave in flight at once: per group two direct loads
+    // of x (rows 4j .. 4j+3, 16 chunks each, into slice gi; the chunk of row
+    // r at position c sits at c ^ r, so that a fragment read of 8 rows hits 8
+    // distinct 16-byte bank groups), four weight loads and one scale load.
+    // Groups past the wave's range load through zero-range descriptors.
+    struct WChunk {
+      uint32_t wv[4][VEC];
+      uint16_t sc[VEC];
+    };
+    WChunk c[NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const bool live = g_begin + gi < g_end;
+      const uint32_t g = live ? g_begin + gi : g_begin;
+      const __amdgpu_buffer_rsrc_t xr = rsrc_of(p.x + (size_t)g * kGroup, live ? -1 : 0);
+#pragma unroll
+      for (int j = 0; j < XROWS / 4; ++j) {
+        const uint32_t lr = 4 * j + kb;                 // LDS row of this lane's chunk
+        const uint32_t row = xbase + (lr < xvalid ? lr : xvalid - 1);
+        const uint32_t off = ((row < M ? row : M - 1) * K + (l16 ^ lr) * 8) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xr, (__attribute__((address_space(3))) void*)(xw + (gi * XROWS + 4 * j) * 16), 16, off, 0, 0, 0);
+      }
+      // the load order the waits below count on: x, then the weights and scales, then the next group
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const __amdgpu_buffer_rsrc_t wr = rsrc_of(w + ((size_t)g * PR + ks * 4) * N, live ? -1 : 0);
+        const WV v = buf_words<VEC, kWPolicy>(wr, woff);
+        __builtin_memcpy(c[gi].wv[ks], &v, sizeof(v));
+      }
+      const auto sv = buf_halves<VEC>(rsrc_of(s + (size_t)g * N), colv * 2);
+      __builtin_memcpy(c[gi].sc, &sv, sizeof(sv));
+      asm volatile("" ::: "memory");
+    }
+    const uint32_t frow = l16 < xvalid ? l16 : xvalid - 1;   // the lane's A row (rows past m repeat)
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      if (g_begin + gi < g_end) {   // wave-uniform
+        // x of group gi has landed once at most the loads issued after it
+        // (its own 4 weight and 1 scale loads, and every later group's 7)
+        // are outstanding; loads complete in issue order
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 + 7 * (NG - 1 - gi)) : "memory");
+        floatx4 part[VEC];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const uint32_t ch = 4 * ks + kb;
+          const half8_t a = permute_x_like_int4x8(xw[(gi * XROWS + frow) * 16 + (ch ^ frow)]);
+#pragma unroll
+          for (int t = 0; t < VEC; ++t) {
+            const half8_t b = unpack_int4x8_interleaved(c[gi].wv[ks][t]);
+            part[t] = mfma16x16x32(a, b, ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : part[t]);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < VEC; ++t) {
+          const float sf = h2f(c[gi].sc[t]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[t][0][i] = __builtin_fmaf(part[t][i], sf, acc[t][0][i]);
+        }
+      }
+    }
+    __syncthreads();   // every wave is done with its x slices before the reduction reuses them
+  } else if (g_begin < g_end) {
     // two register buffers used ping-pong: chunk c+1 is in flight while
     // chunk c computes.  Every load is issued unconditionally (past the
     // wave's range they repeat its last group, which the cache holds): a load
@@ -398,8 +483,26 @@ hipError_t launch_split_k(const QkvProblem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// m <= 8, whole 64-column strips, 16 waves owning 3 or 4 groups each: all of
+// a wave's groups in flight, x through direct LDS loads
+template <int NG>
+hipError_t launch_all_groups(const QkvProblem& p, hipStream_t stream) {
+  const uint32_t nstrips = p.n / 64;
+  hipLaunchKernelGGL((qkv_decode_kernel<4, 1, 1, 4, 16, true, 8, false, NG>), dim3(3 * nstrips), dim3(16 * kWave), 0,
+                     stream, p, nstrips);
+  return hipGetLastError();
+}
+
 template <int BITS>
 hipError_t launch_decode_bits(const QkvProblem& p, hipStream_t stream) {
+  if constexpr (BITS == 4) {
+    // It pays once the 16 waves own 2.5 groups or more on average (m = 8,
+    // n = 4096: k = 5120 11.9 -> 11.1 us, 6144 12.7 -> 11.6, 8192 15.1 ->
+    // 14.7); from 33 to 39 groups most waves own two and it gains nothing.
+    const uint32_t groups = p.k / kGroup;
+    if (p.m <= 8 && p.n % 64 == 0 && groups >= 40 && groups <= 64)
+      return groups <= 48 ? launch_all_groups<3>(p, stream) : launch_all_groups<4>(p, stream);
+  }
   // INT8 words are twice the registers per group: 16-wave workgroups fit
   // (128 VGPRs, buffer loads) only with full strips at m <= 8; otherwise INT8
   // keeps the 8-wave register budget (each wave then streams four groups).

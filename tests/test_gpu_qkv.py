@@ -79,6 +79,10 @@ def test_tiny_config_all_outputs():
     # split-K: waves with exactly two groups on ragged strips (the straight-line path), and
     # waves with three or more groups, odd counts included (the loop; 8 and 16 x rows kept)
     (6, 65, 4096), (15, 100, 4096), (5, 72, 8320), (8, 64, 6272), (12, 64, 6272), (40, 72, 4480),
+    # m <= 8 on whole strips with 40 to 64 groups: all of a wave's groups in flight, x through direct
+    # LDS loads (40 and 41 groups: waves with 2 and 3; 48: 3 each; 49 above: 3 and 4; 64: 4 each);
+    # 33 groups stays on the two-chunk path
+    (8, 128, 5120), (3, 64, 5248), (7, 192, 6144), (1, 64, 8192), (8, 4096, 8192), (8, 128, 4224),
 ])
 def test_ragged_shapes(M, N, K):
     inp = workloads.qkv_inputs(M, N, K, seed=M * 7919 + N * 31 + K)
