@@ -9,7 +9,9 @@ line carries:
 
 * ``roofline``     the prefill kernel against the dense f16 MFMA peak, with the
                    shader clock sampled while the kernel runs back to back and
-                   the fraction against the peak at that clock;
+                   the fraction against the peak at that clock, and against
+                   MFMA work alone timed the same way (``mfma_alone``: the rate
+                   the matrix cores sustain at the power limit);
 * ``secondary``    decode (8 rows, weights rotated over 21 sets so every call
                    streams from HBM) next to a plain streaming read of the same
                    bytes, batched decode, the W8A16 sibling (decode and
@@ -277,7 +279,47 @@ def roof_lib():
     L.kaio_roof_strip_read.restype = ctypes.c_int
     L.kaio_roof_strip_sink_bytes.argtypes = [ctypes.c_uint, ctypes.c_int]
     L.kaio_roof_strip_sink_bytes.restype = ctypes.c_size_t
+    L.kaio_roof_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.kaio_roof_mfma.restype = ctypes.c_int
+    L.kaio_roof_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.kaio_roof_mfma_flops.restype = ctypes.c_double
     return L
+
+
+def mfma_roof(steps, stream, dev, iters=256, workgroups=2048):
+    """MFMA work alone (dense f16 16x16x32 MFMAs on register operands, no memory traffic),
+    conditioned and timed like the prefill, with the shader clock under it: the rate the matrix
+    cores sustain under the chip's power limit when nothing else moves.  One launch (256
+    iterations, 2048 workgroups of 4 waves) is ~275 GFLOP, about a prefill call's duration."""
+    import ctypes
+    import torch
+    L = roof_lib()
+    if L is None:
+        return None
+    sink = torch.empty((workgroups * 256,), dtype=torch.float32, device=dev)
+
+    def fn(i):
+        st = L.kaio_roof_mfma(sink.data_ptr(), iters, workgroups, ctypes.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"kaio_roof_mfma failed ({st})")
+
+    def sustained(part):
+        for i in range(20 if part == 0 else 300):
+            fn(i)
+    fn(0)
+    torch.cuda.synchronize()
+    clk = shader_clock_under(sustained, stream, dev)
+    condition(fn, 40.0)
+    ms, _ = timed(fn, steps, 3, stream, conditioned=True)
+    tf = L.kaio_roof_mfma_flops(iters, workgroups) / (ms * 1e-3) / 1e12
+    log(f"[bench] MFMA alone: {ms * 1e3:.1f} us/call, {tf:.1f} TFLOP/s ({tf / PEAK_F16_TFLOPS:.1%} of peak)"
+        + (f", shader clock {clk['median_mhz']:.0f} MHz" if clk else ""))
+    r = {"what": "v_mfma_f32_16x16x32_f16 alone on register operands, 8 chains per wave, "
+                 f"{workgroups} x 4 waves, {iters} x 8 MFMAs per wave (libkaio_roof.so)",
+         "us_per_call": round(ms * 1e3, 2), "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_F16_TFLOPS, 4)}
+    if clk:
+        r["sclk_median_mhz"] = clk["median_mhz"]
+    return r
 
 
 def strip_roof(wsets, replays, stream, dev):
@@ -542,6 +584,10 @@ def main():
     if not args.no_roof:
         # Q|K|V as one dense [K, 3N] f16 matrix through the vendor library
         roof["vendor_dense_f16"] = vendor_dense(M, 3 * N, K, False, args.steps, stream, dev, clock=True)
+        mr = mfma_roof(args.steps, stream, dev)
+        if mr:
+            roof["mfma_alone"] = mr
+            roof["frac_of_mfma_alone"] = round(tflops / mr["tflops"], 4)
     result.update({
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -677,6 +723,9 @@ def main():
                                     "us_per_call": round(gms * 1e3, 2), "value": round(gtf, 2),
                                     "unit": "TFLOP/s", "bound": "mfma", "peak": PEAK_F16_TFLOPS,
                                     "frac": round(gtf / PEAK_F16_TFLOPS, 4)}
+        mfma_alone = result["roofline"].get("mfma_alone")
+        if mfma_alone:
+            secondary["gemm_f16f32"]["frac_of_mfma_alone"] = round(gtf / mfma_alone["tflops"], 4)
         if not args.no_roof:
             secondary["gemm_f16f32"]["vendor"] = [
                 vendor_dense(M, N, K, f32, max(10, args.steps // 2), stream, dev) for f32 in (True, False)]
@@ -697,6 +746,8 @@ def main():
                         "(cast + two GEMM launches)",
             "us_per_call": round(bms * 1e3, 2), "value": round(btf, 2), "unit": "TFLOP/s", "bound": "mfma",
             "peak": PEAK_F16_TFLOPS, "frac": round(btf / PEAK_F16_TFLOPS, 4)}
+        if mfma_alone:
+            secondary["gemm_f16f32_bwd"]["frac_of_mfma_alone"] = round(btf / mfma_alone["tflops"], 4)
         del ad, bd, cd, gd, gad, gbd, wsd
 
     # ---- dequant backward, and a plain copy of the same bytes ---------------------------------

@@ -4,7 +4,8 @@
  * Not an operation of the pages and not part of libkaio's ABI: a plain
  * streaming read of device memory and a read of the packed-weight layout by
  * column strips, used by the benchmark as the measured ceilings an HBM-bound
- * kernel moving the same bytes is compared with, and a shader-clock probe.
+ * kernel moving the same bytes is compared with, MFMA work alone (the same for
+ * the MFMA-bound kernels), and a shader-clock probe.
  */
 #ifndef KAIO_ROOF_H
 #define KAIO_ROOF_H
@@ -60,6 +61,20 @@ size_t kaio_roof_strip_sink_bytes(unsigned cols, int strip_cols);
  * Returns 0 on a queued launch, 1 for a bad pointer, 3 if the launch failed.
  */
 int kaio_roof_clock_probe(void* out, unsigned long long ticks, void* stream);
+/*
+ * MFMA work alone: `workgroups` workgroups of 4 waves, each wave issuing
+ * iters x 8 dense f16 MFMAs (16x16x32, f32 accumulate) on register operands,
+ * with no memory traffic but one 4-byte store per thread at the end, into
+ * `sink` (a device buffer of workgroups * 256 floats, 4-byte aligned).  Its
+ * sustained rate is the ceiling of matrix-core work under the chip's power
+ * limit, against which the MFMA-bound kernels are weighed beside the nominal
+ * peak.  iters: a multiple of 4 in [4, 2^20]; workgroups in [1, 2^20].
+ * Returns 0 on a queued launch, 1 for a bad argument, 3 if the launch failed.
+ * kaio_roof_mfma_flops gives the flops of one launch.
+ */
+int kaio_roof_mfma(void* sink, int iters, int workgroups, void* stream);
+double kaio_roof_mfma_flops(int iters, int workgroups);
+
 /* Rate of the real-time counter of the current device in kHz (0 if unknown). */
 int kaio_roof_wall_clock_khz(void);
 

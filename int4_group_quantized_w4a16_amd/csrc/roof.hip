@@ -63,6 +63,50 @@ __global__ void __launch_bounds__(64) clock_probe_kernel(unsigned long long* __r
   out[4 * blockIdx.x + 3] = r1;
 }
 
+// MFMA work alone at the dense f16 rate: each wave runs 8 independent
+// accumulator chains of v_mfma_f32_16x16x32_f16 on register operands (four A
+// and four B fragments of hashed values, rotated so that no chain repeats a
+// pair within four steps); no memory traffic except one 4-byte store per
+// thread at the end.  Its sustained rate is what the matrix cores deliver
+// under the chip's power limit when nothing else moves.  The MFMAs are asm
+// with the accumulator tied in place (the builtin moves accumulators between
+// register files every step); asm is opaque to the compiler's hazard checks,
+// so the VALU writes of the operands and the reads of the results are
+// separated from the MFMAs by explicit wait states.
+__global__ void __launch_bounds__(256) mfma_roof_kernel(float* __restrict__ sink, uint32_t iters) {
+  typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+  typedef float floatx4 __attribute__((ext_vector_type(4)));
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  half8_t a[4], b[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t h = (t * 2654435761u) ^ (uint32_t)(r * 97 + i * 131);
+      h ^= h >> 13;
+      h *= 0x5bd1e995u;
+      h ^= h >> 15;
+      a[r][i] = (_Float16)((float)((int)(h & 1023) - 512) * 0.001f);
+      b[r][i] = (_Float16)((float)((int)((h >> 10) & 1023) - 512) * 0.001f);
+    }
+  floatx4 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+  asm volatile("s_nop 7" ::: "memory");
+  for (uint32_t it = 0; it < iters; it += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(acc[c]) : "v"(a[(c + u) & 3]), "v"(b[c & 3]));
+  }
+  asm volatile("s_nop 15\n s_nop 15" ::: "memory");
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) sum += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  sink[t] = sum;
+}
+
 // Reads of three packed-weight arrays (`rows` rows x `cols` u32 each, row
 // major) by column strips, with non-temporal loads, XORed and stored only on
 // a value the data never yields (as above):
@@ -177,6 +221,18 @@ int kaio_roof_clock_probe(void* out, unsigned long long ticks, void* stream) {
   hipLaunchKernelGGL(clock_probe_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
                      static_cast<unsigned long long*>(out), ticks);
   return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+int kaio_roof_mfma(void* sink, int iters, int workgroups, void* stream) {
+  if (!sink || (reinterpret_cast<uintptr_t>(sink) & 3)) return 1;
+  if (iters < 4 || iters > (1 << 20) || iters % 4 || workgroups < 1 || workgroups > (1 << 20)) return 1;
+  hipLaunchKernelGGL(mfma_roof_kernel, dim3((uint32_t)workgroups), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<float*>(sink), (uint32_t)iters);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+double kaio_roof_mfma_flops(int iters, int workgroups) {
+  return (double)workgroups * 4 * iters * 8 * (2.0 * 16 * 16 * 32);
 }
 
 int kaio_roof_wall_clock_khz(void) {

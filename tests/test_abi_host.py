@@ -37,11 +37,13 @@ def declared_functions(header=HEADER):
 
 
 def test_measurement_library_exports_its_header():
-    # libkaio_roof.so: the benchmark's plain-read, strip-read and clock-probe kernels (not libkaio's ABI)
+    # libkaio_roof.so: the benchmark's plain-read, strip-read, MFMA-alone and clock-probe kernels
+    # (not libkaio's ABI)
     header = os.path.join(os.path.dirname(HEADER), "kaio_roof.h")
     names = declared_functions(header)
     assert set(names) == {"kaio_roof_stream_read", "kaio_roof_sink_bytes", "kaio_roof_clock_probe",
-                          "kaio_roof_wall_clock_khz", "kaio_roof_strip_read", "kaio_roof_strip_sink_bytes"}
+                          "kaio_roof_wall_clock_khz", "kaio_roof_strip_read", "kaio_roof_strip_sink_bytes",
+                          "kaio_roof_mfma", "kaio_roof_mfma_flops"}
     L = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(kaio.__file__)), "libkaio_roof.so"))
     for n in names:
         assert hasattr(L, n), n
@@ -62,6 +64,13 @@ def test_measurement_library_exports_its_header():
     assert L.kaio_roof_strip_read(A, A + STEP, A + 2 * STEP, 100, 4096, 64, A + 3 * STEP, None) == 1  # rows % 128
     assert L.kaio_roof_strip_read(A, A + STEP, A + 2 * STEP, 512, 4000, 64, A + 3 * STEP, None) == 1  # cols % 64
     assert L.kaio_roof_strip_read(A, None, A + 2 * STEP, 512, 4096, 64, A + 3 * STEP, None) == 1      # null array
+    L.kaio_roof_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.kaio_roof_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.kaio_roof_mfma_flops.restype = ctypes.c_double
+    assert L.kaio_roof_mfma_flops(256, 2048) == 2048 * 4 * 256 * 8 * 2 * 16 * 16 * 32
+    assert L.kaio_roof_mfma(None, 256, 2048, None) == 1          # null sink
+    assert L.kaio_roof_mfma(A, 6, 2048, None) == 1               # iterations not a multiple of 4
+    assert L.kaio_roof_mfma(A, 256, 0, None) == 1                # no workgroups
 
 
 def test_every_declared_symbol_is_exported():
