@@ -84,9 +84,15 @@ __device__ __forceinline__ T load_w(const T* p) {
 constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format
 // records = -1: no range limit (every offset is in bounds by construction);
 // 0: every load through the descriptor is out of range -- it returns zeros
-// without touching memory (still one load for the wait counts)
+// without touching memory (still one load for the wait counts).
+// records must be the same in every lane of the wave (every caller's choice
+// depends on the wave's group range only).  It is read from the first lane so
+// that the compiler keeps the descriptor in scalar registers: a range it
+// computes with a vector select makes it wrap each load in a loop over the
+// lanes' distinct descriptors.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int records = -1) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, records, kBufferFlags);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, __builtin_amdgcn_readfirstlane(records),
+                                           kBufferFlags);
 }
 template <int V, int kPolicy>
 __device__ __forceinline__ typename WordVec<V>::T buf_words(__amdgpu_buffer_rsrc_t r, uint32_t off) {
