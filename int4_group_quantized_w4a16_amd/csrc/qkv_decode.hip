@@ -355,11 +355,15 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   };
 
   if constexpr (NG > 0) {
-    // Every group of the wave in flight at once: per group two direct loads
-    // of x (rows 4j .. 4j+3, 16 chunks each, into slice gi; the chunk of row
-    // r at position c sits at c ^ r, so that a fragment read of 8 rows hits 8
-    // distinct 16-byte bank groups), four weight loads and one scale load.
-    // Groups past the wave's range load through zero-range descriptors.
+    // Every group of the wave in flight at once: first the x of every group,
+    // two direct loads each (rows 4j .. 4j+3, 16 chunks each, into slice gi;
+    // the chunk of row r at position c sits at c ^ r, so that a fragment read
+    // of 8 rows hits 8 distinct 16-byte bank groups), then per group four
+    // weight loads and one scale load.  x goes first because the compiler
+    // makes the first read of any slice wait for every direct load issued
+    // before it (it cannot tell the slices apart), so x issued per group
+    // would hold group 0's compute until later groups' x had landed.  Groups
+    // past the wave's range load through zero-range descriptors.
     struct WChunk {
       uint32_t wv[4][VEC];
       uint16_t sc[VEC];
@@ -378,8 +382,13 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             xr, (__attribute__((address_space(3))) void*)(xw + (gi * XROWS + 4 * j) * 16), 16, off, 0, 0, 0);
       }
-      // the load order the waits below count on: x, then the weights and scales, then the next group
-      asm volatile("" ::: "memory");
+    }
+    // the load order the waits below count on: all x, then the weights and scales group by group
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const bool live = g_begin + gi < g_end;
+      const uint32_t g = live ? g_begin + gi : g_begin;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const __amdgpu_buffer_rsrc_t wr = rsrc_of(w + ((size_t)g * PR + ks * 4) * N, live ? -1 : 0);
@@ -394,10 +403,10 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       if (g_begin + gi < g_end) {   // wave-uniform
-        // x of group gi has landed once at most the loads issued after it
-        // (its own 4 weight and 1 scale loads, and every later group's 7)
-        // are outstanding; loads complete in issue order
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 + 7 * (NG - 1 - gi)) : "memory");
+        // every x has landed, and group gi's weights and scales, once at most
+        // the later groups' 5 loads each are outstanding; loads complete in
+        // issue order
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 * (NG - 1 - gi)) : "memory");
         floatx4 part[VEC];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
