@@ -638,9 +638,9 @@ def main():
             "read_roof": rr, "frac_of_read_roof": round(rr["us_per_call"] / (dms * 1e3), 4) if rr else None,
             "strip_read_roof": sr}
         # batched decode and prefill chunks on the same rotated weights (split-K kernel up to
-        # m = 128, then the tile kernel in the form kaio_qkv_plan reports)
+        # m = 64, then the tile kernel in the form kaio_qkv_plan reports)
         batched = []
-        for bm in ((16, 32, 64, 128, 256, 512, 768, 1024, 1536) if args.only != "decode" else ()):
+        for bm in ((16, 32, 64, 96, 128, 256, 512, 768, 1024, 1536) if args.only != "decode" else ()):
             xb = t(np.random.default_rng(c["seed"] + 100 + bm).standard_normal((bm, K)).astype(np.float16))
             ob = [torch.empty((bm, N), dtype=torch.float16, device=dev) for _ in range(3)]
             bstep = lambda i: kaio.kaio_qkv_w4a16(xb, *sets[i % R][0], *sets[i % R][1], *ob)
@@ -653,7 +653,8 @@ def main():
             batched.append({"m": bm, "us_per_call": round(bms * 1e3, 3), "gbs": round(bgbs, 1),
                             "tflops": round(btf, 2), "hbm_frac": round(bgbs / PEAK_HBM_GBS, 4),
                             "form": pl["kernel"] if pl["kernel"] == "split_k" else
-                            f"tile {pl['waves']} waves x {pl['rows']} rows x {pl['sets']} set(s)"})
+                            f"tile {pl['waves']} waves x {pl['rows']} rows x {pl['sets']} set(s), "
+                            f"{pl['outputs']} output(s) per workgroup"})
             del xb, ob
         if batched:
             secondary["qkv_batched_decode"] = {

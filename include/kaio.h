@@ -81,8 +81,9 @@ typedef enum kaio_dtype {
  * only when k > 0) -> INVALID_ARGUMENT; misaligned pointer ->
  * INVALID_ARGUMENT; an output overlapping an input or another output ->
  * INVALID_ARGUMENT; device -> DEVICE; launch -> LAUNCH.  k == 0 writes
- * zeros.  m <= 128 runs the memory-bound split-K kernel (decode and batched
- * decode), larger m the MFMA tile kernel; both obey this contract.
+ * zeros.  m <= 64 runs the memory-bound split-K kernel (decode and batched
+ * decode), larger m the MFMA tile kernel (up to m = 128 with one output per
+ * workgroup); all obey this contract.
  */
 kaio_status kaio_qkv_w4a16(const void* x,
                            const uint32_t* w_q, const uint32_t* w_k, const uint32_t* w_v,
@@ -109,7 +110,7 @@ kaio_status kaio_qkv_w4a16(const void* x,
  *   q, k_out, v  f16[m, n]   outputs, f32 accumulation rounded once to f16 (RNE)
  *   group_size  must be 128
  *
- * Validation order, limits, dispatch (m <= 128 split-K kernel, else the tile
+ * Validation order, limits, dispatch (m <= 64 split-K kernel, else the tile
  * kernel) and error behaviour: exactly as kaio_qkv_w4a16.
  */
 kaio_status kaio_qkv_w8a16(const void* x,
@@ -228,7 +229,9 @@ kaio_status kaio_dequant_group_bwd(kaio_dtype dtype, int32_t outer, int32_t axis
  * Which kernel form a kaio_qkv_w4a16 (bits 4) or kaio_qkv_w8a16 (bits 8)
  * call of these sizes runs, for tests and tuning; host only, no device
  * touched, nothing launched.  On KAIO_OK:
- *   plan[0]  0: the split-K kernel (m <= 128), 1: the tile kernel
+ *   plan[0]  0: the split-K kernel, 1: the tile kernel (each workgroup
+ *            computes its tile of Q, K and V), 2: the tile kernel with one
+ *            output per workgroup (three times the workgroups)
  *   plan[1]  tile kernel: waves per set; split-K: 0
  *   plan[2]  tile kernel: rows of x per tile; split-K: columns per strip
  *   plan[3]  tile kernel: sets of waves per workgroup (2: the 128-k groups

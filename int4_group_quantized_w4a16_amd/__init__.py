@@ -85,8 +85,8 @@ def kaio_qkv_plan(m: int, n: int, k: int, bits: int = 4) -> dict:
     """The kernel form a QKV call of these sizes runs (kaio_qkv_plan; host only)."""
     plan = (ctypes.c_uint32 * 5)()
     _check(lib().kaio_qkv_plan(m, n, k, bits, plan))
-    return {"kernel": "tile" if plan[0] else "split_k", "waves": plan[1], "rows": plan[2], "sets": plan[3],
-            "workgroups": plan[4]}
+    return {"kernel": ("split_k", "tile", "tile_one_output")[plan[0]], "waves": plan[1], "rows": plan[2],
+            "sets": plan[3], "outputs": 1 if plan[0] == 2 else 3, "workgroups": plan[4]}
 
 
 def _check(status: int):

@@ -178,15 +178,13 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nb) {
   return (b % kXcd) * per + b / kXcd;
 }
 
-// Tile (m, n) of workgroup b for an mtiles x ntiles grid.  After the XCD
-// remap, consecutive ids run concurrently on one XCD; they are walked in
-// SM x SN super-blocks (SM row blocks x SN column blocks) so that the tiles
-// resident on an XCD share both x row blocks and weight column blocks in its
-// L2 instead of spanning every row block of x.
+// Tile (m, n) of remapped id t for an mtiles x ntiles grid.  Consecutive
+// ids run concurrently on one XCD; they are walked in SM x SN super-blocks
+// (SM row blocks x SN column blocks) so that the tiles resident on an XCD
+// share both x row blocks and weight column blocks in its L2 instead of
+// spanning every row block of x.
 template <uint32_t SM, uint32_t SN>
-__device__ __forceinline__ void tile_of(uint32_t b, uint32_t nb, uint32_t mtiles, uint32_t ntiles,
-                                        uint32_t& tm, uint32_t& tn) {
-  const uint32_t t = xcd_remap(b, nb);
+__device__ __forceinline__ void tile_at(uint32_t t, uint32_t mtiles, uint32_t ntiles, uint32_t& tm, uint32_t& tn) {
   if (mtiles % SM == 0 && ntiles % SN == 0) {
     const uint32_t per = SM * SN;
     const uint32_t blk = t / per, in = t % per;
@@ -197,6 +195,13 @@ __device__ __forceinline__ void tile_of(uint32_t b, uint32_t nb, uint32_t mtiles
     tm = t % mtiles;
     tn = t / mtiles;
   }
+}
+
+// Tile (m, n) of workgroup b of nb for an mtiles x ntiles grid.
+template <uint32_t SM, uint32_t SN>
+__device__ __forceinline__ void tile_of(uint32_t b, uint32_t nb, uint32_t mtiles, uint32_t ntiles,
+                                        uint32_t& tm, uint32_t& tn) {
+  tile_at<SM, SN>(xcd_remap(b, nb), mtiles, ntiles, tm, tn);
 }
 
 }  // namespace kaio

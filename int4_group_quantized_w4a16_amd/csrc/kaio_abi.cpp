@@ -189,7 +189,7 @@ kaio_status qkv(const char* op, uint32_t bits, const void* x, const uint32_t* w_
   uint64_t out_bytes = 0, x_bytes = 0, w_bytes = 0, s_bytes = 0;
   const bool decode = m <= kaio::kDecodeMaxM;
   const uint64_t wgs = decode ? 3ull * ((n + kaio::decode_bn(m) - 1) / kaio::decode_bn(m))
-                              : kaio::prefill_wgs(kaio::prefill_form(m, n, k, bits), m, n);
+                              : kaio::prefill_wgs(kaio::tile_form(m, n, k, bits), m, n);
   if (!bytes_of(m, n, 2, &out_bytes) || !bytes_of(m, k, 2, &x_bytes) || !bytes_of(k / (32 / bits), n, 4, &w_bytes) ||
       !bytes_of(k / 128, n, 2, &s_bytes) || wgs > kaio::kMaxWorkgroups || n >= kaio::kMaxN ||
       k >= kaio::kMaxK)
@@ -373,8 +373,8 @@ kaio_status kaio_qkv_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t bits, uin
     plan[3] = 1;
     plan[4] = (uint32_t)(3ull * ((n + bn - 1) / bn));
   } else {
-    const kaio::PrefillForm f = kaio::prefill_form(m, n, k, bits);
-    plan[0] = 1;
+    const kaio::PrefillForm f = kaio::tile_form(m, n, k, bits);
+    plan[0] = f.outs == 1 ? 2 : 1;
     plan[1] = f.waves;
     plan[2] = f.bm;
     plan[3] = f.sets;

@@ -22,30 +22,32 @@ struct QkvProblem {
 // Tile geometry, shared with the host-side grid-size checks.
 constexpr uint64_t kComputeUnits = 256;  // MI355X
 // Forms of the tile kernel: waves per set (each wave owns 16 columns of every
-// output), rows per tile, and sets of waves per workgroup (2: the groups are
-// split in halves over two sets, which needs an even group count).  Every
-// form holds one workgroup per compute unit.  pass_cost: the time of one
+// output it computes), rows per tile, sets of waves per workgroup (2: the
+// groups are split in halves over two sets, which needs an even group count)
+// and outputs per workgroup (3: Q, K and V; 1: one of them, three times the
+// workgroups).  Every form holds one workgroup per compute unit.  pass_cost: the time of one
 // full pass of the form over the compute units, relative to 8 waves x 128
 // rows (1000), measured at n = k = 4096 (16x16x32 f16 MFMA, 8 waves of 128
 // rows: ~85 us per pass).  Small tiles cost more per output (the unpack is
 // amortised over fewer rows), so the choice trades tile efficiency against
 // how well the grid fills whole passes.
 struct PrefillForm {
-  uint32_t waves, bm, sets;
+  uint32_t waves, bm, sets, outs;
 };
 struct PrefillFormCost {
   PrefillForm f;
   uint32_t pass_cost;
 };
 constexpr PrefillFormCost kPrefillForms[] = {
-    {{8, 128, 1}, 1000}, {{8, 96, 1}, 780}, {{4, 128, 2}, 555}, {{4, 96, 2}, 450},
-    {{4, 64, 2}, 355},   {{4, 128, 1}, 640}, {{4, 96, 1}, 520}, {{4, 64, 1}, 400}};
-// two sets need an even group count; two INT8 rings of 128-row tiles do not fit in LDS
+    {{8, 128, 1, 3}, 1000}, {{8, 96, 1, 3}, 780}, {{4, 128, 2, 3}, 555}, {{4, 96, 2, 3}, 450},
+    {{4, 64, 2, 3}, 355},   {{4, 128, 1, 3}, 640}, {{4, 96, 1, 3}, 520}, {{4, 64, 1, 3}, 400}};
+// two sets need an even group count; two three-output INT8 rings of 128-row
+// tiles do not fit in LDS
 constexpr bool prefill_form_ok(PrefillForm f, uint32_t k, uint32_t bits) {
-  return f.sets == 1 || ((k / 128) % 2 == 0 && (bits == 4 || f.bm <= 96));
+  return f.sets == 1 || ((k / 128) % 2 == 0 && (bits == 4 || f.bm <= 96 || f.outs == 1));
 }
 constexpr uint64_t prefill_wgs(PrefillForm f, uint32_t m, uint32_t n) {
-  return (uint64_t)((m + f.bm - 1) / f.bm) * ((n + 16 * f.waves - 1) / (16 * f.waves));
+  return (uint64_t)((m + f.bm - 1) / f.bm) * ((n + 16 * f.waves - 1) / (16 * f.waves)) * (f.outs == 1 ? 3 : 1);
 }
 // predicted time: whole passes at the full cost, a partial last pass at
 // 0.7 + 0.3 x its share of the compute units (fewer workgroups contend less)
@@ -71,9 +73,26 @@ constexpr PrefillForm prefill_form(uint32_t m, uint32_t n, uint32_t k, uint32_t 
 constexpr uint32_t kMaxN = 1u << 26;   // keeps 32-bit per-lane byte offsets in range (16 rows x N x 4 B)
 constexpr uint32_t kMaxK = 1u << 24;
 #ifndef KAIO_SK_MAXM
-#define KAIO_SK_MAXM 128
+#define KAIO_SK_MAXM 64
 #endif
 constexpr uint32_t kDecodeMaxM = KAIO_SK_MAXM;   // m <= this runs the split-K kernel
+// Above it and up to kOneOutMaxM rows the tile kernel runs with one output per
+// workgroup: 4 waves x 16 columns, 96-row tiles up to 96 rows and 128-row
+// tiles beyond, the groups split over two sets of waves when their count is
+// even.  At n = k = 4096 that is 192 workgroups where the three-output forms
+// have 64; each weight word is unpacked once per tile instead of once per 32
+// rows as in the split-K kernel.  Graph replay over rotated weight sets
+// (us, split-K -> this form): m = 72 26.5 -> 20.3, 96 26.9 -> 20.9, 112
+// 27.0 -> 22.6, 128 27.3 -> 23.3; at m <= 64 it was slower (m = 64 17.5 ->
+// 18.3), and so were three-output 64-row tiles (30.3-30.8) and one-output
+// 64-row tiles (32.5-32.9).  Its groups are short (32 MFMAs per wave), so
+// the weights' memory latency, covered only one group ahead, bounds it.
+constexpr uint32_t kOneOutMaxM = 128;
+// the form of the tile kernel for m > kDecodeMaxM
+constexpr PrefillForm tile_form(uint32_t m, uint32_t n, uint32_t k, uint32_t bits) {
+  if (m <= kOneOutMaxM) return PrefillForm{4, m <= 96 ? 96u : 128u, (k / 128) % 2 == 0 ? 2u : 1u, 1};
+  return prefill_form(m, n, k, bits);
+}
 // split-K configuration for 32 < m <= 64: row tiles per wave (the other
 // rows go to other waves), words per lane load, waves per workgroup
 #ifndef KAIO_SK4_RT
@@ -86,14 +105,7 @@ constexpr uint32_t kDecodeMaxM = KAIO_SK_MAXM;   // m <= this runs the split-K k
 #define KAIO_SK4_WAVES 8
 #endif
 // columns of one output per split-K workgroup, by row count
-constexpr uint32_t decode_bn(uint32_t m) { return m <= 32 ? 64u : m <= 64 ? 16u * KAIO_SK4_VEC : 64u; }
-// split-K configuration for 64 < m <= 128: row tiles per wave, waves per workgroup
-#ifndef KAIO_SK8_RT
-#define KAIO_SK8_RT 2
-#endif
-#ifndef KAIO_SK8_WAVES
-#define KAIO_SK8_WAVES 8
-#endif
+constexpr uint32_t decode_bn(uint32_t m) { return m <= 32 ? 64u : 16u * KAIO_SK4_VEC; }
 constexpr uint32_t kGemmBM = 256;
 constexpr uint32_t kGemmBN = 256;
 constexpr uint64_t kMaxWorkgroups = (1ull << 24) - 1;  // 1-D grid limit at 256 threads

@@ -1,4 +1,4 @@
-// W4A16 fused tri-output QKV projection -- split-K kernel for small m (m <= 128).
+// W4A16 fused tri-output QKV projection -- split-K kernel for small m (m <= 64).
 //
 // Operation: kaio-candle 0.2.0, src/qkv_project_int4.rs (module doc and the
 // doc comment of qkv_project_int4); same contract as the tile kernel.
@@ -40,7 +40,8 @@
 // are chosen per m so that the register file holds two chunks plus the
 // accumulators without spilling and the reduction buffer stays at 64 KiB
 // (plus 68 KiB of x slices): m <= 16: 1 x 1, 64, 16 (8 x rows kept when
-// m <= 8); m <= 32: 2 x 1, 64, 8; m <= 64: 2 x 2, 64, 8; m <= 128: 2 x 4, 64, 8.
+// m <= 8); m <= 32: 2 x 1, 64, 8; m <= 64: 2 x 2, 64, 8.  Larger m runs the tile
+// kernel, which unpacks each word once per tile of 96 or 128 rows.
 
 #include <type_traits>
 
@@ -68,13 +69,14 @@ template <> struct WordVec<4> { using T = u32x4; };
 // 108 -> 100 VGPRs, 7.47 -> 7.20 us; W8A16 fits 16 waves without spilling).
 // The 8-wave configurations loop over their groups, and rebuilding
 // descriptors there cost 12-20%: they keep global loads.  Buffer offsets stay
-// below 2^32 by the host-side limits (k < 2^24, n < 2^26, m <= 128): x rows
-// <= 127 of 2k bytes; weights < 8 packed rows of 4n bytes.
+// below 2^32 by the host-side limits (k < 2^24, n < 2^26, m <= 64): x rows
+// <= 63 of 2k bytes; weights < 8 packed rows of 4n bytes.
 // Packed weights that one wave alone reads (rows not split across waves) carry
 // the non-temporal hint: they stream past the caches instead of displacing the
 // small x that every workgroup re-reads (n = k = 4096: m = 8 7.94 -> 7.37 us,
 // m = 16 8.94 -> 8.25, m = 32 12.37 -> 11.76).  When RSPLIT waves read the
-// same words (m > 32) the hint would defeat that reuse (m = 128: +6%), and
+// same words (m > 32) the hint would defeat that reuse (+6% with the rows
+// split four ways), and
 // the scales are faster without it.
 template <bool kOnce, typename T>
 __device__ __forceinline__ T load_w(const T* p) {
@@ -527,17 +529,14 @@ hipError_t launch_decode_bits(const QkvProblem& p, hipStream_t stream) {
   if (p.m <= 8) return launch_split_k<BITS, 1, 1, 4, kSmallWaves, 8>(p, stream);
   if (p.m <= 16) return launch_split_k<BITS, 1, 1, 4, kSmallWaves>(p, stream);
   if (p.m <= 32) return launch_split_k<BITS, 2, 1, 4, 8>(p, stream);
-  if (p.m <= 64)
-    return launch_split_k<BITS, KAIO_SK4_RT, 4 / KAIO_SK4_RT, KAIO_SK4_VEC, KAIO_SK4_WAVES>(p, stream);
-  return launch_split_k<BITS, KAIO_SK8_RT, 8 / KAIO_SK8_RT, 4, KAIO_SK8_WAVES>(p, stream);
+  return launch_split_k<BITS, KAIO_SK4_RT, 4 / KAIO_SK4_RT, KAIO_SK4_VEC, KAIO_SK4_WAVES>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_qkv_decode(const QkvProblem& p, hipStream_t stream) {
-  static_assert(kDecodeMaxM <= 128, "the widest configuration covers 128 rows");
-  static_assert(decode_bn(16) == 64 && decode_bn(32) == 64 && decode_bn(64) == 16 * KAIO_SK4_VEC &&
-                    decode_bn(128) == 64,
+  static_assert(kDecodeMaxM <= 64, "the widest configuration covers 64 rows");
+  static_assert(decode_bn(16) == 64 && decode_bn(32) == 64 && decode_bn(64) == 16 * KAIO_SK4_VEC,
                 "strip widths must match the host-side grid computation");
   return p.bits == 8 ? launch_decode_bits<8>(p, stream) : launch_decode_bits<4>(p, stream);
 }

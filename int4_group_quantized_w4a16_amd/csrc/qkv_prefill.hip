@@ -1,4 +1,4 @@
-// W4A16 fused tri-output QKV projection -- MFMA tile kernel (m > 128).
+// W4A16 fused tri-output QKV projection -- MFMA tile kernel (m > 64).
 //
 // Operation: kaio-candle 0.2.0, src/qkv_project_int4.rs (module doc and the
 // doc comment of qkv_project_int4): one launch computes Q, K and V f16[M,N]
@@ -76,8 +76,9 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // of XDIST+1 slots), the packed weights one group ahead (WSLOTS slots), and
 // the scales SCHUNK groups at a time:
 //   x  [XDIST+1][X_CHUNKS]            swizzled rows of x
-//   w  [WSLOTS][3][WAVES][PR][16] u32 packed rows x columns of output q, wave w
-//   s  [3][WAVES][SCHUNK][16] f16     scales of the wave's 16 columns (n % 8 == 0)
+//   w  [WSLOTS][NQ][WAVES][PR][16] u32 packed rows x columns of output q, wave w
+//   s  [NQ][WAVES][SCHUNK][16] f16     scales of the wave's 16 columns (n % 8 == 0)
+// NQ = outputs per workgroup: 3 (Q, K and V) or 1.
 // PR = 16 packed rows per group for INT4, 32 for INT8.  A wave reads only the
 // words it loaded itself and has consumed (unpacked into registers) the words
 // of group g before the barrier that starts group g, after which it loads
@@ -85,7 +86,7 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // that the ring fits in LDS.  INT4 keeps two, or one in a tight ring.
 // TIGHT: one weight slot and 8-group scale chunks, for two rings of 128-row
 // tiles in one workgroup.
-template <int BITS, int WAVES, int XDIST, int BM, bool TIGHT = false>
+template <int BITS, int WAVES, int XDIST, int BM, int NQ, bool TIGHT = false>
 struct RingLayout {
   static constexpr int X_CHUNKS = BM * KC;                // 16-byte chunks of x per stage
   static constexpr int kXSlots = XDIST + 1;
@@ -93,15 +94,15 @@ struct RingLayout {
   static constexpr int kSChunk = TIGHT ? 8 : 32;         // SCHUNK
   static constexpr int kWWords = 256 * (BITS / 4);       // words per output per wave per group
   static constexpr int kWBase = kXSlots * X_CHUNKS;
-  static constexpr int kWSize = 3 * WAVES * kWWords / 4;
+  static constexpr int kWSize = NQ * WAVES * kWWords / 4;
   static constexpr int kSBase = kWBase + kWSlots * kWSize;
-  static constexpr int kSize = kSBase + 3 * WAVES * kSChunk * 16 * 2 / 16;   // uint4
+  static constexpr int kSize = kSBase + NQ * WAVES * kSChunk * 16 * 2 / 16;   // uint4
 };
 constexpr int kLdsBytes = 160 * 1024;   // per workgroup
 // the ring of one set of waves: tight when two of the usual ones would not fit
-template <int BITS, int WAVES, int XDIST, int BM, int KS>
-using SetRing = RingLayout<BITS, WAVES, XDIST, BM,
-                           (KS == 2 && 2 * RingLayout<BITS, WAVES, XDIST, BM>::kSize * 16 > kLdsBytes)>;
+template <int BITS, int WAVES, int XDIST, int BM, int KS, int NQ>
+using SetRing = RingLayout<BITS, WAVES, XDIST, BM, NQ,
+                           (KS == 2 && 2 * RingLayout<BITS, WAVES, XDIST, BM, NQ>::kSize * 16 > kLdsBytes)>;
 
 // LDS row position of packed row r within a wave's [PR][16] word block.  INT8
 // B operands take rows 8ks + 2kb + j (k-step ks, 8-k block kb, word j), which
@@ -152,9 +153,10 @@ __device__ __forceinline__ void lane_rows(const uint4* __restrict__ xs, uint32_t
 // acc += p * s with the f16 scale converted inside the FMA (v_fma_mix_f32):
 // the accumulators hold 2^-9 times the result (the unpacked weights carry
 // that factor), which the epilogue takes back exactly.
-__device__ __forceinline__ void fold(floatx4 (&acc)[3], const floatx4 (&pb)[3], const _Float16 (&sf)[3]) {
+template <int NQ>
+__device__ __forceinline__ void fold(floatx4 (&acc)[NQ], const floatx4 (&pb)[NQ], const _Float16 (&sf)[NQ]) {
 #pragma unroll
-  for (int q = 0; q < 3; ++q)
+  for (int q = 0; q < NQ; ++q)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[q][i] = __builtin_fmaf(pb[q][i], (float)sf[q], acc[q][i]);
 }
@@ -173,15 +175,15 @@ __device__ __forceinline__ void fold(floatx4 (&acc)[3], const floatx4 (&pb)[3], 
 // stalling the start of the next group.  `next_w` points at this wave's
 // next-group words in LDS, `next_s[q]` at its scales; the wait before the
 // tail covers them (XPENDING = the x loads issued after them).
-template <int BITS, int WAVES, int XPENDING, int RT, typename IssueX>
-__device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3][4], _Float16 (&sf)[3],
+template <int BITS, int WAVES, int XPENDING, int RT, int NQ, typename IssueX>
+__device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][NQ], half8_t (&bq)[NQ][4], _Float16 (&sf)[NQ],
                                           const uint4* __restrict__ xs, const uint32_t* __restrict__ next_w,
-                                          const uint16_t* const (&next_s)[3], uint32_t l16, uint32_t kb,
+                                          const uint16_t* const (&next_s)[NQ], uint32_t l16, uint32_t kb,
                                           uint32_t lane, IssueX issue_x_part) {
   // A fragments two tiles ahead (three buffers); tiles RT-2 and RT-1 land
   // in buffers (RT-2) % 3 and (RT-1) % 3 during tiles RT-4 and RT-3.
   half8_t abuf[3][4];
-  floatx4 pbuf[2][3];
+  floatx4 pbuf[2][NQ];
   const uint4* xl[4];
   lane_rows(xs, l16, kb, xl);
   x_lanes(xl, abuf[0], 0);
@@ -196,7 +198,7 @@ __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int q = 0; q < 3; ++q)
+      for (int q = 0; q < NQ; ++q)
         pbuf[r & 1][q] = mfma16x16x32(abuf[r % 3][ks], bq[q][ks],
                                       ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : pbuf[r & 1][q]);
     if (r > 0) fold(acc[r - 1], pbuf[(r - 1) & 1], sf);
@@ -212,33 +214,33 @@ __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3
   // LDS latency passes under the MFMAs instead of in front of each unpack
   constexpr int WPK = BITS / 4;
   constexpr int WW = 256 * WPK;
-  uint32_t nw[3][4][WPK];
-  uint16_t ns16[3];
+  uint32_t nw[NQ][4][WPK];
+  uint16_t ns16[NQ];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int q = 0; q < 3; ++q)
+    for (int q = 0; q < NQ; ++q)
 #pragma unroll
       for (int j = 0; j < WPK; ++j)
         nw[q][ks][j] = next_w[q * WAVES * WW + wrow_pos<BITS>(WPK * (4 * ks + kb) + j) * 16 + l16];
 #pragma unroll
-  for (int q = 0; q < 3; ++q) ns16[q] = *next_s[q];
+  for (int q = 0; q < NQ; ++q) ns16[q] = *next_s[q];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int q = 0; q < 3; ++q)
+      for (int q = 0; q < NQ; ++q)
         pbuf[t][q] = mfma16x16x32(abuf[t == 0 ? T0 : T1][ks], bq[q][ks],
                                   ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : pbuf[t][q]);
 #pragma unroll
-    for (int q = 0; q < 3; ++q) bq[q][ks] = unpack_b_scaled<BITS>(nw[q][ks]);
+    for (int q = 0; q < NQ; ++q) bq[q][ks] = unpack_b_scaled<BITS>(nw[q][ks]);
     __builtin_amdgcn_sched_barrier(0);
   }
   fold(acc[RT - 2], pbuf[0], sf);
   fold(acc[RT - 1], pbuf[1], sf);
 #pragma unroll
-  for (int q = 0; q < 3; ++q) sf[q] = __builtin_bit_cast(_Float16, ns16[q]);
+  for (int q = 0; q < NQ; ++q) sf[q] = __builtin_bit_cast(_Float16, ns16[q]);
 }
 
 // BITS = 4 (W4A16) or 8 (W8A16: two packed words per 8 k of a column).
@@ -249,7 +251,10 @@ __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][3], half8_t (&bq)[3
 // waves share each SIMD and hide each other's waits); the second set's
 // accumulators are added to the first's through LDS before the epilogue, in
 // one fixed order.  Needs an even group count.
-template <int BITS, int WAVES, int XDIST, bool kAligned, int BM, int KS>
+// NQ = 3: each workgroup computes its tile of Q, K and V; NQ = 1: of one of
+// them (three times the workgroups, for grids too small to fill the compute
+// units otherwise; x is then staged once per output).
+template <int BITS, int WAVES, int XDIST, bool kAligned, int BM, int KS, int NQ>
 __global__ void __launch_bounds__(KS * WAVES * 64, 1)
 qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   constexpr int THREADS = WAVES * 64;            // threads of one set
@@ -258,7 +263,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   constexpr int WPK = BITS / 4;                  // packed words per 8 k of a column
   constexpr int PR = 16 * WPK;                   // packed rows per group
   constexpr int BN = 16 * WAVES;
-  using L = SetRing<BITS, WAVES, XDIST, BM, KS>;
+  using L = SetRing<BITS, WAVES, XDIST, BM, KS, NQ>;
   constexpr int SCHUNK = L::kSChunk;
   constexpr int X_CHUNKS = L::X_CHUNKS;
   constexpr int XPER = X_CHUNKS / THREADS;       // x loads per thread per stage
@@ -269,7 +274,8 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   static_assert(BN % 64 == 0, "the epilogue's column swizzle stays inside the tile row");
   static_assert(XPER < 64, "vmcnt range");
   static_assert(KS == 1 || KS == 2, "one or two sets of waves");
-  static_assert(KS == 1 || WAVES * RT * 12 * 64 * 4 <= KS * L::kSize * 16, "the second set's sums must fit in LDS");
+  static_assert(KS == 1 || WAVES * RT * NQ * 4 * 64 * 4 <= KS * L::kSize * 16, "the second set's sums must fit in LDS");
+  static_assert(NQ == 1 || NQ == 3, "one output per workgroup, or all three");
   static_assert(KS * L::kSize * 16 <= kLdsBytes, "rings must fit in LDS");
   extern __shared__ uint4 smem[];
 
@@ -282,16 +288,24 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   const uint32_t kb = lane >> 4;          // 8-k block of the 32-k MFMA step
   const uint32_t l16 = lane & 15;
 
+  // NQ = 1: the remapped ids run through the tiles of Q, then K, then V
+  const uint32_t ntiles = (p.n + BN - 1) / BN;
+  const uint32_t t = xcd_remap(blockIdx.x, gridDim.x);
+  const uint32_t q0 = NQ == 1 ? t / (mtiles * ntiles) : 0;   // first output of this workgroup
   uint32_t tm, tn;
-  tile_of<KAIO_PREFILL_SM, KAIO_PREFILL_SN>(blockIdx.x, gridDim.x, mtiles, (p.n + BN - 1) / BN, tm, tn);
+  tile_at<KAIO_PREFILL_SM, KAIO_PREFILL_SN>(NQ == 1 ? t % (mtiles * ntiles) : t, mtiles, ntiles, tm, tn);
   const uint32_t m0 = tm * BM;
   const uint32_t n0 = tn * BN;
   const uint32_t M = p.m, N = p.n, K = p.k;
   const uint32_t G = K / kGroup / KS;            // groups of this set
   const uint32_t g0 = set * G;                   // its first group
-  const uint32_t* const wsrc[3] = {p.w[0] + (size_t)g0 * PR * N, p.w[1] + (size_t)g0 * PR * N,
-                                   p.w[2] + (size_t)g0 * PR * N};
-  const uint16_t* const ssrc[3] = {p.s[0] + (size_t)g0 * N, p.s[1] + (size_t)g0 * N, p.s[2] + (size_t)g0 * N};
+  const uint32_t* wsrc[NQ];
+  const uint16_t* ssrc[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    wsrc[q] = p.w[q0 + q] + (size_t)g0 * PR * N;
+    ssrc[q] = p.s[q0 + q] + (size_t)g0 * N;
+  }
 
   // ---- per-lane DMA sources -----------------------------------------------------
   // Each source address is a wave-uniform base plus a 32-bit per-lane byte
@@ -338,7 +352,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
     const uint32_t gc = g < G ? g : G - 1;
     uint32_t* wst = reinterpret_cast<uint32_t*>(wslot(g)) + wave * WW;
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       const char* wg = uniform(reinterpret_cast<const char*>(wsrc[q] + (size_t)gc * PR * N));
       if (kAligned) {
 #pragma unroll
@@ -361,7 +375,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
     const uint32_t off = (gi * N + s8c) * 2;
     if (SCHUNK == 32 || lane < 2 * SCHUNK) {
 #pragma unroll
-      for (int q = 0; q < 3; ++q)
+      for (int q = 0; q < NQ; ++q)
         dma_to_lds(uniform(reinterpret_cast<const char*>(ssrc[q] + (size_t)c0 * N)), off,
                    sbuf + (q * WAVES + wave) * SCHUNK * 16, 1);
     }
@@ -377,22 +391,22 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
     for (int i = 0; i < XPER; ++i) issue_x_one(g, i);
   };
   // where group g's scales for this lane's column are read from
-  auto scale_src = [&](uint32_t g, const uint16_t* (&ns)[3]) {
+  auto scale_src = [&](uint32_t g, const uint16_t* (&ns)[NQ]) {
 #pragma unroll
-    for (int q = 0; q < 3; ++q)
+    for (int q = 0; q < NQ; ++q)
       ns[q] = kAligned ? sbuf + ((q * WAVES + wave) * SCHUNK + g % SCHUNK) * 16 + l16
                        : ssrc[q] + (size_t)(g < G ? g : G - 1) * N + colc;
   };
 
-  floatx4 acc[RT][3];
+  floatx4 acc[RT][NQ];
 #pragma unroll
   for (int r = 0; r < RT; ++r)
 #pragma unroll
-    for (int q = 0; q < 3; ++q) acc[r][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < NQ; ++q) acc[r][q] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // Prologue: x of groups 0 .. XDIST-1 in flight, group 0 in place and unpacked.
-  half8_t bq[3][4];
-  _Float16 sf[3];
+  half8_t bq[NQ][4];
+  _Float16 sf[NQ];
   if (kAligned) issue_s(0);
   issue_w(0);
 #pragma unroll
@@ -401,7 +415,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   {
     const uint32_t* w0 = wave_words(0);
 #pragma unroll
-    for (int q = 0; q < 3; ++q)
+    for (int q = 0; q < NQ; ++q)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         uint32_t words[WPK];
@@ -409,10 +423,10 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
         for (int j = 0; j < WPK; ++j) words[j] = w0[q * WAVES * WW + wrow_pos<BITS>(WPK * (4 * ks + kb) + j) * 16 + l16];
         bq[q][ks] = unpack_b_scaled<BITS>(words);
       }
-    const uint16_t* ns[3];
+    const uint16_t* ns[NQ];
     scale_src(0, ns);
 #pragma unroll
-    for (int q = 0; q < 3; ++q) sf[q] = __builtin_bit_cast(_Float16, *ns[q]);
+    for (int q = 0; q < NQ; ++q) sf[q] = __builtin_bit_cast(_Float16, *ns[q]);
   }
 
   // Per group g, after one barrier: weights of g+1 and x of g+XDIST are
@@ -437,10 +451,10 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
     // the next scale chunk replaces this one once the tail of g-1 has read
     // the last scale it needed (the scale of g, before the barrier)
     if (kAligned && (g + 1) % SCHUNK == 0 && g + 1 < G) issue_s(g + 1);
-    const uint16_t* ns[3];
+    const uint16_t* ns[NQ];
     scale_src(g + 1, ns);
     // x of g + XDIST goes out one load per row tile, between MFMAs
-    group_mma<BITS, WAVES, XPER, RT>(acc, bq, sf, xslot(g), wave_words(g + 1), ns, l16, kb, lane,
+    group_mma<BITS, WAVES, XPER, RT, NQ>(acc, bq, sf, xslot(g), wave_words(g + 1), ns, l16, kb, lane,
                            [&](int i) { issue_x_one(g + XDIST, i); });
   }
   wait_vm_barrier<0>();   // no load is still writing the ring the epilogue reuses
@@ -449,25 +463,25 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   // Wave w of set 1 holds the same accumulator elements, lane for lane, as
   // wave w of set 0: one f32 per lane and element, lane-contiguous.
   if constexpr (KS == 2) {
-    constexpr int E = RT * 3 * 4;
+    constexpr int E = RT * NQ * 4;
     float* const red = reinterpret_cast<float*>(smem) + wave * E * 64 + lane;
     __syncthreads();   // rings no longer read
     if (set == 1) {
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int q = 0; q < 3; ++q)
+        for (int q = 0; q < NQ; ++q)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) red[((r * 3 + q) * 4 + i) * 64] = acc[r][q][i];
+          for (int i = 0; i < 4; ++i) red[((r * NQ + q) * 4 + i) * 64] = acc[r][q][i];
     }
     __syncthreads();
     if (set == 0) {
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int q = 0; q < 3; ++q)
+        for (int q = 0; q < NQ; ++q)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[r][q][i] += red[((r * 3 + q) * 4 + i) * 64];
+          for (int i = 0; i < 4; ++i) acc[r][q][i] += red[((r * NQ + q) * 4 + i) * 64];
     }
   }
 
@@ -475,7 +489,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   constexpr int TT = KS * THREADS;               // every thread of the workgroup stores
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
-  for (int q = 0; q < 3; ++q) {
+  for (int q = 0; q < NQ; ++q) {
     __syncthreads();   // ring (or the sums, or the previous output's tile) no longer read
     // D layout of a 16x16 MFMA tile: lane holds column (lane & 15), rows 4*(lane >> 4) + i.
     // Column c of tile row t sits at c ^ (16 * ((t >> 2) & 3)): the four row
@@ -490,7 +504,7 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
               __builtin_bit_cast(uint16_t, (_Float16)(acc[r][q][i] * kUnpackScaledInv));
     }
     __syncthreads();
-    uint16_t* out = p.out[q];
+    uint16_t* out = p.out[q0 + q];
     if (kAligned) {
       constexpr int CPR = BN / 8;                    // 16-byte chunks per tile row
       constexpr int NCH = BM * CPR;                  // 16-byte chunks of the tile
@@ -513,14 +527,14 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   }
 }
 
-template <int BITS, int WAVES, int XDIST, bool kAligned, int BM, int KS>
+template <int BITS, int WAVES, int XDIST, bool kAligned, int BM, int KS, int NQ>
 hipError_t launch_variant(const QkvProblem& p, hipStream_t stream) {
   constexpr int BN = 16 * WAVES;
   const uint32_t mtiles = (p.m + BM - 1) / BM;
   const uint32_t ntiles = (p.n + BN - 1) / BN;
-  const size_t lds = (size_t)KS * SetRing<BITS, WAVES, XDIST, BM, KS>::kSize * 16;
-  const dim3 grid(mtiles * ntiles), block(KS * WAVES * 64);
-  auto* kern = &qkv_prefill_kernel<BITS, WAVES, XDIST, kAligned, BM, KS>;
+  const size_t lds = (size_t)KS * SetRing<BITS, WAVES, XDIST, BM, KS, NQ>::kSize * 16;
+  const dim3 grid(mtiles * ntiles * (NQ == 1 ? 3 : 1)), block(KS * WAVES * 64);
+  auto* kern = &qkv_prefill_kernel<BITS, WAVES, XDIST, kAligned, BM, KS, NQ>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
@@ -528,34 +542,36 @@ hipError_t launch_variant(const QkvProblem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BITS, int WAVES, int BM, int KS>
+template <int BITS, int WAVES, int BM, int KS, int NQ = 3>
 hipError_t launch_aligned_or_not(const QkvProblem& p, hipStream_t stream) {
   // 16-byte output rows and f16-pair scale loads need n % 8 == 0
-  return p.n % 8 == 0 ? launch_variant<BITS, WAVES, KAIO_PREFILL_XDIST, true, BM, KS>(p, stream)
-                      : launch_variant<BITS, WAVES, KAIO_PREFILL_XDIST, false, BM, KS>(p, stream);
+  return p.n % 8 == 0 ? launch_variant<BITS, WAVES, KAIO_PREFILL_XDIST, true, BM, KS, NQ>(p, stream)
+                      : launch_variant<BITS, WAVES, KAIO_PREFILL_XDIST, false, BM, KS, NQ>(p, stream);
 }
 
-// the form prefill_form() picks for this problem
-constexpr uint32_t form_code(uint32_t waves, uint32_t bm, uint32_t sets) { return (waves * 1000 + bm) * 10 + sets; }
+constexpr uint32_t form_code(PrefillForm f) { return ((f.waves * 1000 + f.bm) * 10 + f.sets) * 10 + f.outs; }
 
-// the form prefill_form() picks for this problem
+// the form tile_form() picks for this problem
 template <int BITS>
 hipError_t launch_prefill_bits(const QkvProblem& p, hipStream_t stream) {
-  const PrefillForm f = prefill_form(p.m, p.n, p.k, BITS);
-  switch (form_code(f.waves, f.bm, f.sets)) {
-    case form_code(8, 128, 1): return launch_aligned_or_not<BITS, 8, 128, 1>(p, stream);
-    case form_code(8, 96, 1): return launch_aligned_or_not<BITS, 8, 96, 1>(p, stream);
-    case form_code(4, 128, 2):
+  switch (form_code(tile_form(p.m, p.n, p.k, BITS))) {
+    case form_code({8, 128, 1, 3}): return launch_aligned_or_not<BITS, 8, 128, 1>(p, stream);
+    case form_code({8, 96, 1, 3}): return launch_aligned_or_not<BITS, 8, 96, 1>(p, stream);
+    case form_code({4, 128, 2, 3}):
       if constexpr (BITS == 4) return launch_aligned_or_not<BITS, 4, 128, 2>(p, stream);
       break;
-    case form_code(4, 96, 2): return launch_aligned_or_not<BITS, 4, 96, 2>(p, stream);
-    case form_code(4, 64, 2): return launch_aligned_or_not<BITS, 4, 64, 2>(p, stream);
-    case form_code(4, 128, 1): return launch_aligned_or_not<BITS, 4, 128, 1>(p, stream);
-    case form_code(4, 96, 1): return launch_aligned_or_not<BITS, 4, 96, 1>(p, stream);
-    case form_code(4, 64, 1): return launch_aligned_or_not<BITS, 4, 64, 1>(p, stream);
+    case form_code({4, 96, 2, 3}): return launch_aligned_or_not<BITS, 4, 96, 2>(p, stream);
+    case form_code({4, 64, 2, 3}): return launch_aligned_or_not<BITS, 4, 64, 2>(p, stream);
+    case form_code({4, 128, 1, 3}): return launch_aligned_or_not<BITS, 4, 128, 1>(p, stream);
+    case form_code({4, 96, 1, 3}): return launch_aligned_or_not<BITS, 4, 96, 1>(p, stream);
+    case form_code({4, 64, 1, 3}): return launch_aligned_or_not<BITS, 4, 64, 1>(p, stream);
+    case form_code({4, 128, 2, 1}): return launch_aligned_or_not<BITS, 4, 128, 2, 1>(p, stream);
+    case form_code({4, 96, 2, 1}): return launch_aligned_or_not<BITS, 4, 96, 2, 1>(p, stream);
+    case form_code({4, 128, 1, 1}): return launch_aligned_or_not<BITS, 4, 128, 1, 1>(p, stream);
+    case form_code({4, 96, 1, 1}): return launch_aligned_or_not<BITS, 4, 96, 1, 1>(p, stream);
     default: break;
   }
-  return hipErrorInvalidValue;   // a form without a kernel (prefill_form_ok rules it out)
+  return hipErrorInvalidValue;   // a form without a kernel (tile_form never picks one)
 }
 
 }  // namespace

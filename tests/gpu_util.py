@@ -29,7 +29,13 @@ def qkv_on_gpu(x, w, s, bits=4, **kw):
 
 
 # Forms of the tile kernel (waves per set, rows per tile, sets of waves), as kaio_qkv_plan reports them.
-TILE_FORMS = [(8, 128, 1), (8, 96, 1), (4, 128, 2), (4, 96, 2), (4, 64, 2), (4, 128, 1), (4, 96, 1), (4, 64, 1)]
+# (waves per set, rows per tile, sets of waves, outputs per workgroup)
+TILE_FORMS = [(8, 128, 1, 3), (8, 96, 1, 3), (4, 128, 2, 3), (4, 96, 2, 3), (4, 64, 2, 3), (4, 128, 1, 3),
+              (4, 96, 1, 3), (4, 64, 1, 3), (4, 128, 2, 1), (4, 96, 2, 1), (4, 128, 1, 1), (4, 96, 1, 1)]
+
+
+def form_of(plan):
+    return (plan["waves"], plan["rows"], plan["sets"], plan["outputs"])
 
 
 def shape_for_form(form, bits, aligned, ks=(256, 384, 512, 640)):
@@ -41,11 +47,11 @@ def shape_for_form(form, bits, aligned, ks=(256, 384, 512, 640)):
     for k in ks:
         for j in range(1, 33):
             n = 64 * j if aligned else 64 * j - 3
-            for m in range(129, 2601, 13):
+            for m in range(65, 2601, 13):
                 if best is not None and m * n * k >= best[0]:
                     break
                 p = kaio.kaio_qkv_plan(m, n, k, bits)
-                if (p["waves"], p["rows"], p["sets"]) == tuple(form):
+                if p["kernel"] != "split_k" and form_of(p) == tuple(form):
                     best = (m * n * k, m, n, k)
                     break
     return None if best is None else best[1:]

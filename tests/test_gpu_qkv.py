@@ -14,7 +14,7 @@ from oracle import compare
 from oracle.int4 import pack_int4, unpack_int4
 from oracle.qkv import qkv_project
 from tests.conftest import load_golden
-from tests.gpu_util import DEV, TILE_FORMS, qkv_on_gpu, shape_for_form, to_dev, to_host
+from tests.gpu_util import DEV, TILE_FORMS, form_of, qkv_on_gpu, shape_for_form, to_dev, to_host
 from tests.test_oracle_qkv import build_x
 
 pytestmark = pytest.mark.gpu
@@ -44,8 +44,9 @@ def test_golden_handworked_bitwise():
                 rows = [np.array([int(h, 16) for h in g], dtype=np.uint32) for g in case["per_group_words"][p]]
                 w.append(np.concatenate([np.tile(r, (16, 1)) for r in rows]))
             s.append(np.array(case["scales"][p], dtype=np.float16))
-        # pad 20 runs the split-K kernel with two row tiles per wave, pad 140 the tile kernel (m > 128)
-        for pad in (0, 20, 140):
+        # pad 20 runs the split-K kernel with two row tiles per wave, pad 80 the tile kernel with one
+        # output per workgroup (64 < m <= 128), pad 140 the tile kernel with all three (m > 128)
+        for pad in (0, 20, 80, 140):
             xx = np.concatenate([x, np.zeros((pad, K), np.float16)]) if pad else x
             outs = qkv_on_gpu(xx, w, s)
             for p, o in zip("qkv", outs):
@@ -65,7 +66,8 @@ def test_tiny_config_all_outputs():
     (64, 4, 128), (3, 4099, 256), (200, 1000, 1024),
     # more than 32 groups: the tile kernel reloads its per-chunk scales
     (33, 72, 4480), (129, 136, 8320), (20, 12, 4224),
-    # split-K row-tile boundaries (1, 2 and 4 row tiles), full and ragged strips, then the tile kernel
+    # split-K row-tile boundaries (1 and 2 row tiles, 1 and 2 row blocks), full and ragged strips,
+    # then the tile kernel with one output per workgroup (96- and 128-row tiles), then with three
     (16, 128, 512), (17, 64, 256), (24, 200, 384), (32, 130, 384), (33, 64, 512), (48, 96, 1152),
     (63, 40, 256), (64, 200, 256), (65, 64, 256), (96, 136, 384), (127, 72, 256), (128, 64, 640),
     (129, 64, 256),
@@ -113,25 +115,23 @@ def test_prefill_config_all_outputs():
     (1024, 4096, 1024),   # 8-wave tile kernel: 8 x 32 tiles of 128 x 128, walked in 4 x 8 super-blocks
 ])
 def test_tile_kernel_super_block_grids_all_outputs(M, N, K):
-    plan = kaio.kaio_qkv_plan(M, N, K)
-    assert (plan["waves"], plan["rows"], plan["sets"]) == {256: (4, 64, 2), 200: (4, 64, 2), 512: (4, 128, 2),
-                                                           1024: (8, 128, 1)}[M]
+    assert form_of(kaio.kaio_qkv_plan(M, N, K)) == {256: (4, 64, 2, 3), 200: (4, 64, 2, 3), 512: (4, 128, 2, 3),
+                                                    1024: (8, 128, 1, 3)}[M]
     inp = workloads.qkv_inputs(M, N, K, seed=M + N + K)
     worst = check(qkv_on_gpu(inp.x, inp.w, inp.s), inp)
     print(f"{M}x{N}x{K} (all outputs): max |d|/tol = {worst:.3f}")
 
 
 @pytest.mark.parametrize("aligned", [True, False], ids=["n%8==0", "n%8!=0"])
-@pytest.mark.parametrize("form", TILE_FORMS, ids=lambda f: f"{f[0]}w-{f[1]}rows-{f[2]}sets")
+@pytest.mark.parametrize("form", TILE_FORMS, ids=lambda f: f"{f[0]}w-{f[1]}rows-{f[2]}sets-{f[3]}outs")
 def test_every_tile_form(form, aligned):
     # the smallest problem of a coarse grid that the plan runs in this form: m ragged against the
     # tile height, n ragged against the tile width
     shape = shape_for_form(form, 4, aligned)
     assert shape is not None, f"no problem selects {form}"
     M, N, K = shape
-    plan = kaio.kaio_qkv_plan(M, N, K)
-    assert (plan["waves"], plan["rows"], plan["sets"]) == form
-    inp = workloads.qkv_inputs(M, N, K, seed=M * 7 + N * 3 + K + form[1])
+    assert form_of(kaio.kaio_qkv_plan(M, N, K)) == form
+    inp = workloads.qkv_inputs(M, N, K, seed=M * 7 + N * 3 + K + form[1] + form[3])
     worst = check(qkv_on_gpu(inp.x, inp.w, inp.s), inp)
     print(f"{form} {M}x{N}x{K}: max |d|/tol = {worst:.3f}")
 
@@ -277,9 +277,10 @@ def test_errors_on_device():
         kaio.kaio_qkv_w4a16(x, w, w, w[:, :8].contiguous(), s, s, s)
 
 
-@pytest.mark.parametrize("M", [16, 32, 64, 128])
+@pytest.mark.parametrize("M", [16, 32, 64, 96, 128])
 def test_batched_decode_full_size(M):
-    # the split-K kernel at the decode width (N = K = 4096), every output checked
+    # the split-K kernel (m <= 64) and the one-output tile kernel (96 and 128 rows) at the decode
+    # width (N = K = 4096), every output checked
     N = K = 4096
     inp = workloads.qkv_inputs(M, N, K, seed=4000 + M)
     check(qkv_on_gpu(inp.x, inp.w, inp.s), inp)

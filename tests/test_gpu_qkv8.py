@@ -14,7 +14,7 @@ from oracle import compare
 from oracle.int8 import pack_int8
 from oracle.qkv import qkv_project
 from tests.conftest import load_golden
-from tests.gpu_util import DEV, TILE_FORMS, qkv_on_gpu, shape_for_form, to_dev, to_host
+from tests.gpu_util import DEV, TILE_FORMS, form_of, qkv_on_gpu, shape_for_form, to_dev, to_host
 from tests.test_oracle_qkv8 import golden_inputs
 
 pytestmark = pytest.mark.gpu
@@ -38,8 +38,9 @@ def test_golden_handworked_bitwise():
     for case in load_golden("qkv8_handworked.json")["cases"]:
         x, w, s = golden_inputs(case)
         M, K = x.shape
-        # pad 0: split-K kernel, one row tile; 20: two row tiles; 140: the tile kernel (m > 128)
-        for pad in (0, 20, 140):
+        # pad 0: split-K kernel, one row tile; 20: two row tiles; 80: the tile kernel with one
+        # output per workgroup (64 < m <= 128); 140: with all three (m > 128)
+        for pad in (0, 20, 80, 140):
             xx = np.concatenate([x, np.zeros((pad, K), np.float16)]) if pad else x
             outs = run(xx, w, s)
             for p, o in zip("qkv", outs):
@@ -73,16 +74,15 @@ def test_ragged_shapes(M, N, K):
 
 
 @pytest.mark.parametrize("aligned", [True, False], ids=["n%8==0", "n%8!=0"])
-@pytest.mark.parametrize("form", [f for f in TILE_FORMS if f != (4, 128, 2)],
-                         ids=lambda f: f"{f[0]}w-{f[1]}rows-{f[2]}sets")
+@pytest.mark.parametrize("form", [f for f in TILE_FORMS if f != (4, 128, 2, 3)],
+                         ids=lambda f: f"{f[0]}w-{f[1]}rows-{f[2]}sets-{f[3]}outs")
 def test_every_tile_form(form, aligned):
-    # as for W4A16; INT8 has no two-set 128-row form (two such rings do not fit in LDS)
+    # as for W4A16; INT8 has no two-set 128-row three-output form (two such rings do not fit in LDS)
     shape = shape_for_form(form, 8, aligned)
     assert shape is not None, f"no problem selects {form}"
     M, N, K = shape
-    plan = kaio.kaio_qkv_plan(M, N, K, 8)
-    assert (plan["waves"], plan["rows"], plan["sets"]) == form
-    inp = workloads.qkv8_inputs(M, N, K, M * 7 + N * 3 + K + form[1] + 1)
+    assert form_of(kaio.kaio_qkv_plan(M, N, K, 8)) == form
+    inp = workloads.qkv8_inputs(M, N, K, M * 7 + N * 3 + K + form[1] + form[3] + 1)
     worst = check(run(inp.x, inp.w, inp.s), inp)
     print(f"W8A16 {form} {M}x{N}x{K}: max |d|/tol = {worst:.3f}")
 
