@@ -418,11 +418,25 @@ def vendor_dense(m, n, k, out_f32, steps, stream, dev, clock=False):
 
 
 def summarize(dirs):
-    """Per-kernel summary of rocprofv3 CSV output (kernel_stats.csv or counter_collection.csv)."""
+    """Per-kernel summary of rocprofv3 CSV output: kernel_stats.csv, kernel_trace.csv (dispatches
+    grouped by kernel and grid, with the median duration) and counter_collection.csv."""
     import csv
     import collections
     import glob
+    import statistics
     for d in dirs:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)):
+            groups = collections.defaultdict(list)
+            for r in csv.DictReader(open(f)):
+                wg = max(int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"]), 1)
+                grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]) // wg
+                groups[(r["Kernel_Name"], grid, wg)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            print(f"## {f} (dispatches grouped by kernel and grid)")
+            print("| kernel | grid | calls | avg us | min us | median us | max us |")
+            print("|---|---|---|---|---|---|---|")
+            for (name, grid, wg), us in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+                print(f"| {name.replace('(anonymous namespace)::', '')[:100]} | {grid} x {wg} | {len(us)} | {sum(us) / len(us):.2f} | {min(us):.2f} | "
+                      f"{statistics.median(us):.2f} | {max(us):.2f} |")
         for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
             print(f"## {f}")
             print("| kernel | calls | avg us | min us | max us | share |")

@@ -94,3 +94,20 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_trace_summary_groups_by_kernel_and_grid(tmp_path, capsys):
+    cols = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Workgroup_Size_X", "Workgroup_Size_Y",
+            "Workgroup_Size_Z", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"]
+    rows = [("k<1>", 0, 5000, 256, 1, 1, 256 * 192, 1, 1), ("k<1>", 0, 7000, 256, 1, 1, 256 * 192, 1, 1),
+            ("k<1>", 0, 6000, 256, 1, 1, 256 * 192, 1, 1), ("k<1>", 0, 9000, 256, 1, 1, 256 * 384, 1, 1)]
+    os.makedirs(tmp_path / "t")
+    with open(tmp_path / "t" / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(cols)
+        w.writerows(rows)
+    bench.summarize([str(tmp_path / "t")])
+    out = capsys.readouterr().out
+    # the three 192-workgroup dispatches: mean 6.00, min 5.00, median 6.00, max 7.00 us; the other grid apart
+    assert "| k<1> | 192 x 256 | 3 | 6.00 | 5.00 | 6.00 | 7.00 |" in out
+    assert "| k<1> | 384 x 256 | 1 | 9.00 | 9.00 | 9.00 | 9.00 |" in out
