@@ -83,7 +83,8 @@ typedef enum kaio_dtype {
  * INVALID_ARGUMENT; device -> DEVICE; launch -> LAUNCH.  k == 0 writes
  * zeros.  m <= 64 runs the memory-bound split-K kernel (decode and batched
  * decode), larger m the MFMA tile kernel (up to m = 128 with one output per
- * workgroup); all obey this contract.
+ * workgroup, and so from m = 33 when k / 128 is a multiple of 4); all obey
+ * this contract.
  */
 kaio_status kaio_qkv_w4a16(const void* x,
                            const uint32_t* w_q, const uint32_t* w_k, const uint32_t* w_v,
@@ -110,8 +111,8 @@ kaio_status kaio_qkv_w4a16(const void* x,
  *   q, k_out, v  f16[m, n]   outputs, f32 accumulation rounded once to f16 (RNE)
  *   group_size  must be 128
  *
- * Validation order, limits, dispatch (m <= 64 split-K kernel, else the tile
- * kernel) and error behaviour: exactly as kaio_qkv_w4a16.
+ * Validation order, limits and error behaviour: exactly as kaio_qkv_w4a16;
+ * m <= 64 runs the split-K kernel, larger m the tile kernel.
  */
 kaio_status kaio_qkv_w8a16(const void* x,
                            const uint32_t* w_q, const uint32_t* w_k, const uint32_t* w_v,

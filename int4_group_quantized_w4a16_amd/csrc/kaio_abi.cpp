@@ -187,7 +187,7 @@ kaio_status qkv(const char* op, uint32_t bits, const void* x, const uint32_t* w_
   if (m == 0 || n == 0) return ok();
 
   uint64_t out_bytes = 0, x_bytes = 0, w_bytes = 0, s_bytes = 0;
-  const bool decode = m <= kaio::kDecodeMaxM;
+  const bool decode = kaio::qkv_split_k(m, k, bits);
   const uint64_t wgs = decode ? 3ull * ((n + kaio::decode_bn(m) - 1) / kaio::decode_bn(m))
                               : kaio::prefill_wgs(kaio::tile_form(m, n, k, bits), m, n);
   if (!bytes_of(m, n, 2, &out_bytes) || !bytes_of(m, k, 2, &x_bytes) || !bytes_of(k / (32 / bits), n, 4, &w_bytes) ||
@@ -367,7 +367,7 @@ kaio_status kaio_qkv_plan(uint32_t m, uint32_t n, uint32_t k, uint32_t bits, uin
     return fail(KAIO_ERR_INVALID_PROBLEM, op, "K (%u) must be a multiple of group_size (128)", k);
   for (int i = 0; i < 5; ++i) plan[i] = 0;
   if (m == 0 || n == 0) return ok();
-  if (m <= kaio::kDecodeMaxM) {
+  if (kaio::qkv_split_k(m, k, bits)) {
     const uint32_t bn = kaio::decode_bn(m);
     plan[2] = bn;
     plan[3] = 1;

@@ -41,10 +41,10 @@ struct PrefillFormCost {
 constexpr PrefillFormCost kPrefillForms[] = {
     {{8, 128, 1, 3}, 1000}, {{8, 96, 1, 3}, 780}, {{4, 128, 2, 3}, 555}, {{4, 96, 2, 3}, 450},
     {{4, 64, 2, 3}, 355},   {{4, 128, 1, 3}, 640}, {{4, 96, 1, 3}, 520}, {{4, 64, 1, 3}, 400}};
-// two sets need an even group count; two three-output INT8 rings of 128-row
-// tiles do not fit in LDS
+// s sets need a group count divisible by s; two three-output INT8 rings of
+// 128-row tiles do not fit in LDS
 constexpr bool prefill_form_ok(PrefillForm f, uint32_t k, uint32_t bits) {
-  return f.sets == 1 || ((k / 128) % 2 == 0 && (bits == 4 || f.bm <= 96 || f.outs == 1));
+  return f.sets == 1 || ((k / 128) % f.sets == 0 && (bits == 4 || f.bm <= 96 || f.outs == 1));
 }
 constexpr uint64_t prefill_wgs(PrefillForm f, uint32_t m, uint32_t n) {
   return (uint64_t)((m + f.bm - 1) / f.bm) * ((n + 16 * f.waves - 1) / (16 * f.waves)) * (f.outs == 1 ? 3 : 1);
@@ -75,7 +75,20 @@ constexpr uint32_t kMaxK = 1u << 24;
 #ifndef KAIO_SK_MAXM
 #define KAIO_SK_MAXM 64
 #endif
-constexpr uint32_t kDecodeMaxM = KAIO_SK_MAXM;   // m <= this runs the split-K kernel
+constexpr uint32_t kDecodeMaxM = KAIO_SK_MAXM;   // the split-K kernel covers m <= this
+// INT4 at 32 < m <= 64 with a group count divisible by 4 runs the tile kernel
+// instead: one output per workgroup, 4 waves x 16 columns, 64-row tiles, four
+// sets of waves (16 waves, four per SIMD) each over a quarter of the groups
+// in a tight ring (148 KiB of LDS for the four; INT8's would not fit).  The
+// four sets' independent load streams hide the latency that one group of
+// lead leaves exposed.  Same-box graph replay over rotated weights, N = K =
+// 4096, us (split-K -> four sets): m = 40 16.3 -> 15.3, 48 16.7 -> 15.5, 64
+// 17.4 -> 15.7 (bit-identical: both split K into the same four parts); at
+// m <= 32 it was slower (m = 32 11.8 -> 15.4), and at m > 64, where 64-row
+// tiles double the grid, too (m = 80 20.2 -> 27.9).
+constexpr bool qkv_split_k(uint32_t m, uint32_t k, uint32_t bits) {
+  return m <= kDecodeMaxM && !(m > 32 && bits == 4 && (k / 128) % 4 == 0);
+}
 // Above it and up to kOneOutMaxM rows the tile kernel runs with one output per
 // workgroup: 4 waves x 16 columns, 96-row tiles up to 96 rows and 128-row
 // tiles beyond, the groups split over two sets of waves when their count is
@@ -88,8 +101,9 @@ constexpr uint32_t kDecodeMaxM = KAIO_SK_MAXM;   // m <= this runs the split-K k
 // 64-row tiles (32.5-32.9).  Its groups are short (32 MFMAs per wave), so
 // the weights' memory latency, covered only one group ahead, bounds it.
 constexpr uint32_t kOneOutMaxM = 128;
-// the form of the tile kernel for m > kDecodeMaxM
+// the form of the tile kernel where qkv_split_k is false
 constexpr PrefillForm tile_form(uint32_t m, uint32_t n, uint32_t k, uint32_t bits) {
+  if (m <= kDecodeMaxM) return PrefillForm{4, 64, 4, 1};
   if (m <= kOneOutMaxM) return PrefillForm{4, m <= 96 ? 96u : 128u, (k / 128) % 2 == 0 ? 2u : 1u, 1};
   return prefill_form(m, n, k, bits);
 }

@@ -1,4 +1,5 @@
-// W4A16 fused tri-output QKV projection -- MFMA tile kernel (m > 64).
+// W4A16 fused tri-output QKV projection -- MFMA tile kernel (m > 64; INT4 from
+// m > 32 when the group count divides by 4).
 //
 // Operation: kaio-candle 0.2.0, src/qkv_project_int4.rs (module doc and the
 // doc comment of qkv_project_int4): one launch computes Q, K and V f16[M,N]
@@ -102,7 +103,7 @@ constexpr int kLdsBytes = 160 * 1024;   // per workgroup
 // the ring of one set of waves: tight when two of the usual ones would not fit
 template <int BITS, int WAVES, int XDIST, int BM, int KS, int NQ>
 using SetRing = RingLayout<BITS, WAVES, XDIST, BM, NQ,
-                           (KS == 2 && 2 * RingLayout<BITS, WAVES, XDIST, BM, NQ>::kSize * 16 > kLdsBytes)>;
+                           (KS > 1 && KS * RingLayout<BITS, WAVES, XDIST, BM, NQ>::kSize * 16 > kLdsBytes)>;
 
 // LDS row position of packed row r within a wave's [PR][16] word block.  INT8
 // B operands take rows 8ks + 2kb + j (k-step ks, 8-k block kb, word j), which
@@ -246,11 +247,11 @@ __device__ __forceinline__ void group_mma(floatx4 (&acc)[RT][NQ], half8_t (&bq)[
 // BITS = 4 (W4A16) or 8 (W8A16: two packed words per 8 k of a column).
 // BM = rows of x per workgroup: 128, 96 or 64 (see prefill_form: smaller
 // tiles where a grid of larger ones would fill the compute units badly).
-// KS = 1, or 2: the workgroup holds two sets of WAVES waves, each with its
-// own ring, that run the same loop over the two halves of the groups (so two
-// waves share each SIMD and hide each other's waits); the second set's
+// KS = 1, 2 or 4: the workgroup holds KS sets of WAVES waves, each with its
+// own ring, that run the same loop over their share of the groups (so KS
+// waves share each SIMD and hide each other's waits); the other sets'
 // accumulators are added to the first's through LDS before the epilogue, in
-// one fixed order.  Needs an even group count.
+// one fixed order.  Needs a group count divisible by KS.
 // NQ = 3: each workgroup computes its tile of Q, K and V; NQ = 1: of one of
 // them (three times the workgroups, for grids too small to fill the compute
 // units otherwise; x is then staged once per output).
@@ -273,8 +274,9 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   static_assert(BM * OUT_LD * 2 <= L::kSize * 16, "epilogue tile must fit in the ring");
   static_assert(BN % 64 == 0, "the epilogue's column swizzle stays inside the tile row");
   static_assert(XPER < 64, "vmcnt range");
-  static_assert(KS == 1 || KS == 2, "one or two sets of waves");
-  static_assert(KS == 1 || WAVES * RT * NQ * 4 * 64 * 4 <= KS * L::kSize * 16, "the second set's sums must fit in LDS");
+  static_assert(KS == 1 || KS == 2 || KS == 4, "one, two or four sets of waves");
+  static_assert(KS == 1 || (KS - 1) * WAVES * RT * NQ * 4 * 64 * 4 <= KS * L::kSize * 16,
+                "the other sets' sums must fit in LDS");
   static_assert(NQ == 1 || NQ == 3, "one output per workgroup, or all three");
   static_assert(KS * L::kSize * 16 <= kLdsBytes, "rings must fit in LDS");
   extern __shared__ uint4 smem[];
@@ -459,29 +461,33 @@ qkv_prefill_kernel(QkvProblem p, uint32_t mtiles) {
   }
   wait_vm_barrier<0>();   // no load is still writing the ring the epilogue reuses
 
-  // ---- the second set's sums into the first's (KS = 2) -------------------------
-  // Wave w of set 1 holds the same accumulator elements, lane for lane, as
-  // wave w of set 0: one f32 per lane and element, lane-contiguous.
-  if constexpr (KS == 2) {
+  // ---- the other sets' sums into the first's (KS > 1) -------------------------
+  // Wave w of set s holds the same accumulator elements, lane for lane, as
+  // wave w of set 0: one f32 per lane and element, lane-contiguous, in the
+  // region of set s; set 0 adds them in set order.
+  if constexpr (KS > 1) {
     constexpr int E = RT * NQ * 4;
     float* const red = reinterpret_cast<float*>(smem) + wave * E * 64 + lane;
     __syncthreads();   // rings no longer read
-    if (set == 1) {
+    if (set > 0) {
+      float* const mine = red + (set - 1) * WAVES * E * 64;
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) red[((r * NQ + q) * 4 + i) * 64] = acc[r][q][i];
+          for (int i = 0; i < 4; ++i) mine[((r * NQ + q) * 4 + i) * 64] = acc[r][q][i];
     }
     __syncthreads();
     if (set == 0) {
 #pragma unroll
-      for (int r = 0; r < RT; ++r)
+      for (int o = 0; o < KS - 1; ++o)
 #pragma unroll
-        for (int q = 0; q < NQ; ++q)
+        for (int r = 0; r < RT; ++r)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[r][q][i] += red[((r * NQ + q) * 4 + i) * 64];
+          for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[r][q][i] += red[o * WAVES * E * 64 + ((r * NQ + q) * 4 + i) * 64];
     }
   }
 
@@ -569,6 +575,9 @@ hipError_t launch_prefill_bits(const QkvProblem& p, hipStream_t stream) {
     case form_code({4, 96, 2, 1}): return launch_aligned_or_not<BITS, 4, 96, 2, 1>(p, stream);
     case form_code({4, 128, 1, 1}): return launch_aligned_or_not<BITS, 4, 128, 1, 1>(p, stream);
     case form_code({4, 96, 1, 1}): return launch_aligned_or_not<BITS, 4, 96, 1, 1>(p, stream);
+    case form_code({4, 64, 4, 1}):
+      if constexpr (BITS == 4) return launch_aligned_or_not<BITS, 4, 64, 4, 1>(p, stream);
+      break;
     default: break;
   }
   return hipErrorInvalidValue;   // a form without a kernel (tile_form never picks one)

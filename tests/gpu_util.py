@@ -31,7 +31,10 @@ def qkv_on_gpu(x, w, s, bits=4, **kw):
 # Forms of the tile kernel (waves per set, rows per tile, sets of waves), as kaio_qkv_plan reports them.
 # (waves per set, rows per tile, sets of waves, outputs per workgroup)
 TILE_FORMS = [(8, 128, 1, 3), (8, 96, 1, 3), (4, 128, 2, 3), (4, 96, 2, 3), (4, 64, 2, 3), (4, 128, 1, 3),
-              (4, 96, 1, 3), (4, 64, 1, 3), (4, 128, 2, 1), (4, 96, 2, 1), (4, 128, 1, 1), (4, 96, 1, 1)]
+              (4, 96, 1, 3), (4, 64, 1, 3), (4, 128, 2, 1), (4, 96, 2, 1), (4, 128, 1, 1), (4, 96, 1, 1),
+              (4, 64, 4, 1)]
+# forms the INT8 kernels do not have (their rings would not fit in LDS)
+NO_INT8_FORMS = [(4, 128, 2, 3), (4, 64, 4, 1)]
 
 
 def form_of(plan):
@@ -47,7 +50,7 @@ def shape_for_form(form, bits, aligned, ks=(256, 384, 512, 640)):
     for k in ks:
         for j in range(1, 33):
             n = 64 * j if aligned else 64 * j - 3
-            for m in range(65, 2601, 13):
+            for m in range(33, 2601, 13):
                 if best is not None and m * n * k >= best[0]:
                     break
                 p = kaio.kaio_qkv_plan(m, n, k, bits)

@@ -289,10 +289,16 @@ def test_qkv_plan_validation_and_forms():
     assert L.kaio_qkv_plan(256, 64, 256, 4, None) == 1 and "plan is null" in kaio.kaio_last_error()
     assert L.kaio_qkv_plan(256, 64, 200, 4, plan) == 2 and "multiple of group_size" in kaio.kaio_last_error()
     assert L.kaio_qkv_plan(0, 64, 256, 4, plan) == 0 and list(plan) == [0, 0, 0, 0, 0]
-    # m <= 64: the split-K kernel, 3 outputs x strips
-    for m in (8, 64):
+    # m <= 32, and m <= 64 where the four-set tile form does not apply (INT8, or a group count
+    # not divisible by 4): the split-K kernel, 3 outputs x strips
+    for m, k, bits in ((8, 4096, 4), (32, 4096, 4), (64, 4096, 8), (64, 384, 4), (40, 640, 4)):
+        p = kaio.kaio_qkv_plan(m, 4096, k, bits)
+        assert p["kernel"] == "split_k" and p["workgroups"] == 3 * 4096 // p["rows"], (m, k, bits)
+    # INT4, 32 < m <= 64, k / 128 divisible by 4: one output per workgroup, 64-row tiles, four sets
+    for m in (33, 64):
         p = kaio.kaio_qkv_plan(m, 4096, 4096)
-        assert p["kernel"] == "split_k" and p["workgroups"] == 3 * 4096 // p["rows"]
+        assert p["kernel"] == "tile_one_output" and (p["waves"], p["rows"], p["sets"]) == (4, 64, 4)
+        assert p["workgroups"] == 3 * 4096 // 64
     # 64 < m <= 128: the tile kernel with one output per workgroup, 96-row tiles up to 96 rows,
     # two sets when the group count is even
     for m, k, rows, sets in ((65, 4096, 96, 2), (96, 4224, 96, 1), (97, 4096, 128, 2), (128, 384, 128, 1)):
@@ -300,20 +306,20 @@ def test_qkv_plan_validation_and_forms():
         assert p["kernel"] == "tile_one_output" and (p["waves"], p["rows"], p["sets"], p["outputs"]) == (4, rows, sets, 1)
         assert p["workgroups"] == 3 * 4096 // 64
     assert kaio.kaio_qkv_plan(129, 4096, 4096)["kernel"] == "tile"
-    from tests.gpu_util import TILE_FORMS, form_of, shape_for_form
+    from tests.gpu_util import NO_INT8_FORMS, TILE_FORMS, form_of, shape_for_form
     for bits in (4, 8):
         for m, n, k in ((129, 4096, 4096), (777, 1000, 384), (2048, 4096, 4096), (5000, 12288, 4224),
                         (100, 1000, 384), (70, 4096, 4096)):
             p = kaio.kaio_qkv_plan(m, n, k, bits)
             assert p["kernel"] in ("tile", "tile_one_output") and form_of(p) in TILE_FORMS
             assert p["workgroups"] == -(-m // p["rows"]) * -(-n // (16 * p["waves"])) * (3 // p["outputs"])
-            if p["sets"] == 2:   # two sets split an even group count; no two three-output INT8 128-row rings
-                assert (k // 128) % 2 == 0 and not (bits == 8 and p["rows"] == 128 and p["outputs"] == 3)
+            if p["sets"] > 1:   # the sets split the group count evenly; no INT8 form its rings do not fit
+                assert (k // 128) % p["sets"] == 0 and not (bits == 8 and form_of(p) in NO_INT8_FORMS)
         # the prefill workload keeps the 8-wave 128-row form
         p = kaio.kaio_qkv_plan(2048, 4096, 4096, bits)
         assert form_of(p) == (8, 128, 1, 3)
-        # every form the kernels have is chosen for some problem (INT8 has no two-set 128-row
-        # three-output form)
+        # every form the kernels have is chosen for some problem (INT8 lacks the forms whose rings
+        # would not fit in LDS)
         for f in TILE_FORMS:
             found = shape_for_form(f, bits, True)
-            assert (found is None) == (bits == 8 and f == (4, 128, 2, 3)), (bits, f, found)
+            assert (found is None) == (bits == 8 and f in NO_INT8_FORMS), (bits, f, found)

@@ -67,7 +67,8 @@ def test_tiny_config_all_outputs():
     # more than 32 groups: the tile kernel reloads its per-chunk scales
     (33, 72, 4480), (129, 136, 8320), (20, 12, 4224),
     # split-K row-tile boundaries (1 and 2 row tiles, 1 and 2 row blocks), full and ragged strips,
-    # then the tile kernel with one output per workgroup (96- and 128-row tiles), then with three
+    # then the tile kernel with one output per workgroup (four sets of 64-row tiles where k / 128
+    # divides by 4, 96- and 128-row tiles), then with three
     (16, 128, 512), (17, 64, 256), (24, 200, 384), (32, 130, 384), (33, 64, 512), (48, 96, 1152),
     (63, 40, 256), (64, 200, 256), (65, 64, 256), (96, 136, 384), (127, 72, 256), (128, 64, 640),
     (129, 64, 256),
@@ -78,6 +79,9 @@ def test_tiny_config_all_outputs():
     # of waves (66 and 34 groups: 33 and 17 per set), and odd counts (97, 35: one set)
     (200, 520, 12416), (1100, 1000, 4480), (150, 264, 8448), (150, 261, 8448),
     (1100, 1000, 4352), (1100, 1001, 4352),
+    # four sets of waves over 64-row tiles, one output per workgroup: ragged rows and columns,
+    # n % 8 != 0, several groups per set
+    (33, 72, 512), (47, 130, 1024), (64, 61, 2048), (50, 4096, 1536),
     # split-K: waves with exactly two groups on ragged strips (the straight-line path), and
     # waves with three or more groups, odd counts included (the loop; 8 and 16 x rows kept)
     (6, 65, 4096), (15, 100, 4096), (5, 72, 8320), (8, 64, 6272), (12, 64, 6272), (40, 72, 4480),
@@ -279,8 +283,8 @@ def test_errors_on_device():
 
 @pytest.mark.parametrize("M", [16, 32, 64, 96, 128])
 def test_batched_decode_full_size(M):
-    # the split-K kernel (m <= 64) and the one-output tile kernel (96 and 128 rows) at the decode
-    # width (N = K = 4096), every output checked
+    # the split-K kernel (m <= 32), the one-output tile kernel with four sets (m = 64) and with
+    # 96 and 128 rows, at the decode width (N = K = 4096), every output checked
     N = K = 4096
     inp = workloads.qkv_inputs(M, N, K, seed=4000 + M)
     check(qkv_on_gpu(inp.x, inp.w, inp.s), inp)

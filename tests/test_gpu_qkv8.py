@@ -14,7 +14,7 @@ from oracle import compare
 from oracle.int8 import pack_int8
 from oracle.qkv import qkv_project
 from tests.conftest import load_golden
-from tests.gpu_util import DEV, TILE_FORMS, form_of, qkv_on_gpu, shape_for_form, to_dev, to_host
+from tests.gpu_util import DEV, NO_INT8_FORMS, TILE_FORMS, form_of, qkv_on_gpu, shape_for_form, to_dev, to_host
 from tests.test_oracle_qkv8 import golden_inputs
 
 pytestmark = pytest.mark.gpu
@@ -74,10 +74,10 @@ def test_ragged_shapes(M, N, K):
 
 
 @pytest.mark.parametrize("aligned", [True, False], ids=["n%8==0", "n%8!=0"])
-@pytest.mark.parametrize("form", [f for f in TILE_FORMS if f != (4, 128, 2, 3)],
+@pytest.mark.parametrize("form", [f for f in TILE_FORMS if f not in NO_INT8_FORMS],
                          ids=lambda f: f"{f[0]}w-{f[1]}rows-{f[2]}sets-{f[3]}outs")
 def test_every_tile_form(form, aligned):
-    # as for W4A16; INT8 has no two-set 128-row three-output form (two such rings do not fit in LDS)
+    # as for W4A16; INT8 lacks the forms whose rings would not fit in LDS
     shape = shape_for_form(form, 8, aligned)
     assert shape is not None, f"no problem selects {form}"
     M, N, K = shape

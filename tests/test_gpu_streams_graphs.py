@@ -43,8 +43,8 @@ def check_qkv(outs, inp):
         assert bad == 0, f"{bad} outside tolerance (max ratio {ratio:.3f})"
 
 
-# split-K kernel with 8 and 16 x rows kept, with two row tiles per wave (one and two row blocks:
-# m = 24, 40), then the tile kernel with one output per workgroup (m = 100) and with three
+# split-K kernel with 8 and 16 x rows kept, with two row tiles per wave (m = 24), then the tile
+# kernel with one output per workgroup (four sets at m = 40, two at m = 100) and with three
 @pytest.mark.parametrize("M", [5, 12, 24, 40, 100, 200])
 def test_qkv_side_stream_matches_default_stream(M):
     inp, x, w, s = qkv_case(M, 264, 512, 31 + M)
