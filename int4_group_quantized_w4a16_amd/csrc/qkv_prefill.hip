@@ -8,12 +8,13 @@
 //
 // gfx950 design
 // -------------
-// * Workgroup = WAVES waves, tile = BM (128, or 64 for small grids) rows of
-//   x by 16*WAVES columns of EACH output.  Wave w owns columns [16w, 16w+16)
-//   of all three outputs and all BM rows, so the waves share one x tile in
-//   LDS and never unpack the same weight twice.  Small grids of 4-wave tiles
-//   run two such sets of waves per workgroup, one per half of the groups,
-//   each with its own ring, their sums added in LDS at the end.
+// * Workgroup = WAVES waves, tile = BM (128, 96 or 64 for small grids) rows
+//   of x by 16*WAVES columns of EACH output.  Wave w owns columns
+//   [16w, 16w+16) of all three outputs and all BM rows, so the waves share
+//   one x tile in LDS and never unpack the same weight twice.  Small grids
+//   of 4-wave tiles run two (or four) such sets of waves per workgroup, each
+//   over its share of the groups with its own ring, their sums added in LDS
+//   at the end; the smallest grids compute one output per workgroup.
 // * Everything a group of 128 k needs is staged into LDS rings with direct
 //   global->LDS loads (no registers, no VALU): x and the packed weights one
 //   group ahead, the scales 32 (or 8) groups at a time.  Each address is a
