@@ -54,35 +54,59 @@ struct alignas(16) SmemGemm {
   uint4 b[BN * KCH];   // 32 KiB, [n][k-chunk] swizzled (B transposed)
 };
 
-// B^T swizzle: chunk kc of column n lives in slot n*8 + (kc ^ bswz(n)).
-// Operand reads (8 lanes = 8 consecutive n) and the transposing writes
-// (8 lanes = 8 consecutive n-blocks, same j) both hit 8 distinct bank groups.
-__device__ __forceinline__ uint32_t bswz(uint32_t n) { return (n ^ (n >> 3)) & 7; }
-
 __device__ __forceinline__ uint32_t lo_pair(uint32_t r0, uint32_t r1) { return (r0 & 0xFFFFu) | (r1 << 16); }
 __device__ __forceinline__ uint32_t hi_pair(uint32_t r0, uint32_t r1) { return (r0 >> 16) | (r1 & 0xFFFF0000u); }
 
-// kAligned: k % 8 == 0 and n % 8 == 0, so every 16-byte chunk is either fully
-// inside or fully outside the matrix and row starts are 16-byte aligned.
+__device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_out(uint16_t* p, float v) { *p = __builtin_bit_cast(uint16_t, (_Float16)v); }
+
+// Eight consecutive 16-bit elements base[outer * ld + inner .. + 7]; elements
+// at or past (outer_lim, inner_lim) read as zero.  kAligned: ld % 8 == 0 and
+// inner_lim % 8 == 0, so a chunk is wholly inside or outside the matrix and
+// starts 16 bytes aligned (one 16-byte load); otherwise element by element.
 template <bool kAligned>
-__device__ __forceinline__ uint4 load_chunk(const uint16_t* base, uint32_t rows, uint32_t cols,
-                                            uint32_t r, uint32_t c) {
-  if (r >= rows) return uint4{0u, 0u, 0u, 0u};
+__device__ __forceinline__ uint4 load8(const uint16_t* base, size_t ld, uint32_t outer, uint32_t outer_lim,
+                                       uint32_t inner, uint32_t inner_lim) {
+  if (outer >= outer_lim) return uint4{0u, 0u, 0u, 0u};
   if (kAligned) {
-    if (c >= cols) return uint4{0u, 0u, 0u, 0u};
-    return *reinterpret_cast<const uint4*>(base + (size_t)r * cols + c);
+    if (inner >= inner_lim) return uint4{0u, 0u, 0u, 0u};
+    return *reinterpret_cast<const uint4*>(base + (size_t)outer * ld + inner);
   }
   uint16_t h[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) h[i] = (c + i < cols) ? base[(size_t)r * cols + c + i] : (uint16_t)0;
+  for (int i = 0; i < 8; ++i) h[i] = (inner + i < inner_lim) ? base[(size_t)outer * ld + inner + i] : (uint16_t)0;
   return uint4{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
                h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16)};
 }
 
-template <bool kAligned>
+// LDS swizzle of an operand tile [256 indices][8 reduction chunks]: chunk kc
+// of index i sits in slot i*8 + (kc ^ swz(i)).  An operand staged from
+// reduction-contiguous rows is written one row of 8 chunks per 8 lanes
+// (i & 7 keeps those apart and the 16-row fragment reads too); one staged by
+// transposing 8x8 blocks in registers is written 8 rows at a time, the same
+// chunk of rows 8 apart from neighbouring lanes ((i ^ (i >> 3)) & 7 puts
+// them in distinct bank groups, as it does the fragment reads).
+template <bool kTransposed>
+__device__ __forceinline__ uint32_t tile_swz(uint32_t i) { return kTransposed ? ((i ^ (i >> 3)) & 7) : (i & 7); }
+
+// Register-staged product for shapes the direct-to-LDS kernel does not take:
+// C[Mo, No] = sum over R of A-operand x B-operand, f32 accumulation, OutT
+// float (f32 out) or uint16_t (f16 out, round to nearest even).
+//   kATr = false: A(i, r) at A[i * lda + r] (reduction contiguous);
+//          true:  A(i, r) at A[r * lda + i] (index contiguous).
+//   kBTr = true:  B(r, j) at B[r * ldb + j] (index contiguous);
+//          false: B(r, j) at B[j * ldb + r] (reduction contiguous).
+// A reduction-contiguous operand is staged in 16-byte chunks of 8 reduction
+// elements; an index-contiguous one in 8 x 8 blocks transposed in registers,
+// so that LDS holds both operands as [index][reduction] and every fragment is
+// one 16-byte read.  The forward product is <false, true, float>; the
+// backward products <false, false, f16> (grad_a) and <true, true, f16>
+// (grad_b).  kAligned: both strides and the contiguous extents are multiples
+// of 8 (16-byte chunk loads); any shape otherwise.
+template <bool kAligned, bool kATr, bool kBTr, typename OutT>
 __global__ void __launch_bounds__(THREADS, 1)
-gemm_f16f32_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
-                   float* __restrict__ C, uint32_t M, uint32_t N, uint32_t K, uint32_t mtiles) {
+gemm_reg_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __restrict__ B, uint32_t ldb,
+                OutT* __restrict__ C, uint32_t Mo, uint32_t No, uint32_t R, uint32_t mtiles) {
   __shared__ SmemGemm sm;
 
   const uint32_t tid = threadIdx.x;
@@ -96,49 +120,63 @@ gemm_f16f32_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
   const uint32_t m0 = (bidx % mtiles) * BM;
   const uint32_t n0 = (bidx / mtiles) * BN;
 
-  // staging assignment
-  // A: chunk c = i*256 + tid -> row c/8, k-chunk c%8
-  // B: thread -> 8x8 block: n-block nb = tid % 32, k-block kq = tid / 32
-  const uint32_t nb = tid & 31, kq = tid >> 5;
+  // Staging assignment.  Reduction-contiguous operand: chunk c = i*256 + tid
+  // -> index c / 8, reduction chunk c % 8.  Index-contiguous operand: thread
+  // -> 8x8 block of index block ib = tid % 32 and reduction block kq = tid / 32.
+  const uint32_t ib = tid & 31, kq = tid >> 5;
 
   uint4 ra[8], rb[8];
-  auto load_tiles = [&](uint32_t k0) {
+  // one operand's next tile into registers: base, stride, first index, index count
+  auto load_op = [&](auto tr, uint4 (&reg)[8], const uint16_t* base, uint32_t ld, uint32_t i0, uint32_t ilim,
+                     uint32_t k0) {
+    if constexpr (decltype(tr)::value) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t c = i * THREADS + tid;
-      const uint32_t row = c >> 3, kc = c & 7;
-      const uint32_t gr = m0 + row < M ? m0 + row : M - 1;
-      ra[i] = load_chunk<kAligned>(A, M, K, gr, k0 + kc * 8);
-    }
+      for (int i = 0; i < 8; ++i) reg[i] = load8<kAligned>(base, ld, k0 + kq * 8 + i, R, i0 + ib * 8, ilim);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      rb[i] = load_chunk<kAligned>(B, K, N, k0 + kq * 8 + i, n0 + nb * 8);
-  };
-  auto store_tiles = [&]() {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t c = i * THREADS + tid;
-      const uint32_t row = c >> 3, kc = c & 7;
-      sm.a[row * KCH + (kc ^ (row & 7))] = ra[i];
-    }
-    // transpose the 8x8 block: out[j] = column j, 8 consecutive k
-    uint32_t d[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) { d[i][0] = rb[i].x; d[i][1] = rb[i].y; d[i][2] = rb[i].z; d[i][3] = rb[i].w; }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int qd = j >> 1;
-      uint4 o;
-      if (j & 1) {
-        o = uint4{hi_pair(d[0][qd], d[1][qd]), hi_pair(d[2][qd], d[3][qd]),
-                  hi_pair(d[4][qd], d[5][qd]), hi_pair(d[6][qd], d[7][qd])};
-      } else {
-        o = uint4{lo_pair(d[0][qd], d[1][qd]), lo_pair(d[2][qd], d[3][qd]),
-                  lo_pair(d[4][qd], d[5][qd]), lo_pair(d[6][qd], d[7][qd])};
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t c = i * THREADS + tid;
+        const uint32_t row = c >> 3, kc = c & 7;
+        const uint32_t gi = i0 + row < ilim ? i0 + row : ilim - 1;   // indices past the end: any valid one
+        reg[i] = load8<kAligned>(base, ld, gi, ilim, k0 + kc * 8, R);
       }
-      const uint32_t n = nb * 8 + j;
-      sm.b[n * KCH + (kq ^ bswz(n))] = o;
     }
+  };
+  auto store_op = [&](auto tr, const uint4 (&reg)[8], uint4* dst) {
+    constexpr bool kT = decltype(tr)::value;
+    if constexpr (kT) {
+      // transpose the 8x8 block: out[j] = index j of the block, 8 consecutive reduction elements
+      uint32_t d[8][4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { d[i][0] = reg[i].x; d[i][1] = reg[i].y; d[i][2] = reg[i].z; d[i][3] = reg[i].w; }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int qd = j >> 1;
+        uint4 o;
+        if (j & 1) {
+          o = uint4{hi_pair(d[0][qd], d[1][qd]), hi_pair(d[2][qd], d[3][qd]),
+                    hi_pair(d[4][qd], d[5][qd]), hi_pair(d[6][qd], d[7][qd])};
+        } else {
+          o = uint4{lo_pair(d[0][qd], d[1][qd]), lo_pair(d[2][qd], d[3][qd]),
+                    lo_pair(d[4][qd], d[5][qd]), lo_pair(d[6][qd], d[7][qd])};
+        }
+        const uint32_t idx = ib * 8 + j;
+        dst[idx * KCH + (kq ^ tile_swz<true>(idx))] = o;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t c = i * THREADS + tid;
+        const uint32_t row = c >> 3, kc = c & 7;
+        dst[row * KCH + (kc ^ tile_swz<false>(row))] = reg[i];
+      }
+    }
+  };
+  using ATr = std::integral_constant<bool, kATr>;
+  using BT = std::integral_constant<bool, kBTr>;
+  auto load_tiles = [&](uint32_t k0) {
+    load_op(ATr{}, ra, A, lda, m0, Mo, k0);
+    load_op(BT{}, rb, B, ldb, n0, No, k0);
   };
 
   floatx4 acc[TT][TT];
@@ -147,11 +185,12 @@ gemm_f16f32_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
 #pragma unroll
     for (int c = 0; c < TT; ++c) acc[r][c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const uint32_t nk = (K + BK - 1) / BK;
+  const uint32_t nk = (R + BK - 1) / BK;
   if (nk > 0) load_tiles(0);
   for (uint32_t it = 0; it < nk; ++it) {
     __syncthreads();            // previous tile fully consumed
-    store_tiles();
+    store_op(ATr{}, ra, sm.a);
+    store_op(BT{}, rb, sm.b);
     __syncthreads();            // tile visible
     if (it + 1 < nk) load_tiles((it + 1) * BK);
 #pragma unroll
@@ -161,12 +200,12 @@ gemm_f16f32_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
 #pragma unroll
       for (int c = 0; c < TT; ++c) {
         const uint32_t n = wn * WT + c * 16 + l16;
-        bf[c] = __builtin_bit_cast(half8_t, sm.b[n * KCH + (kc ^ bswz(n))]);
+        bf[c] = __builtin_bit_cast(half8_t, sm.b[n * KCH + (kc ^ tile_swz<kBTr>(n))]);
       }
 #pragma unroll
       for (int r = 0; r < TT; ++r) {
         const uint32_t row = wm * WT + r * 16 + l16;
-        const half8_t af = __builtin_bit_cast(half8_t, sm.a[row * KCH + (kc ^ (row & 7))]);
+        const half8_t af = __builtin_bit_cast(half8_t, sm.a[row * KCH + (kc ^ tile_swz<kATr>(row))]);
 #pragma unroll
         for (int c = 0; c < TT; ++c) acc[r][c] = mfma16x16x32(af, bf[c], acc[r][c]);
       }
@@ -181,7 +220,7 @@ gemm_f16f32_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t gr = m0 + wm * WT + r * 16 + 4 * kb + i;
-        if (gr < M && gc < N) C[(size_t)gr * N + gc] = acc[r][c][i];
+        if (gr < Mo && gc < No) store_out(C + (size_t)gr * No + gc, acc[r][c][i]);
       }
     }
 }
@@ -358,9 +397,6 @@ __device__ __forceinline__ void hazard_guard(floatx4 (&acc)[TM][TN]) {
                    : "i"(NOP));
   }
 }
-
-__device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
-__device__ __forceinline__ void store_out(uint16_t* p, float v) { *p = __builtin_bit_cast(uint16_t, (_Float16)v); }
 
 // C[Mo, No] = sum over R of A-operand x B-operand, f32 accumulation; OutT is
 // float (f32 out) or uint16_t (f16 out, rounded to nearest even).  A is read
@@ -548,22 +584,6 @@ gemm_dma_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
     }
 }
 
-// Any-shape fallback of the backward products: one output per thread,
-// element (i, j) = sum_r A[i*a_i + r*a_r] * B[r*b_r + j*b_j] in f32.
-template <typename OutT>
-__global__ void __launch_bounds__(256)
-gemm_strided_kernel(const uint16_t* __restrict__ A, size_t a_i, size_t a_r, const uint16_t* __restrict__ B,
-                    size_t b_r, size_t b_j, OutT* __restrict__ C, uint32_t Mo, uint32_t No, uint32_t R) {
-  const size_t total = (size_t)Mo * No;
-  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
-    const size_t i = e / No, j = e % No;
-    float acc = 0.f;
-    for (uint32_t r = 0; r < R; ++r)
-      acc = __builtin_fmaf(h2f(A[i * a_i + r * a_r]), h2f(B[r * b_r + j * b_j]), acc);
-    store_out(C + e, acc);
-  }
-}
-
 // f32 -> f16, round to nearest even (the cast of the output gradient)
 __global__ void __launch_bounds__(256)
 cast_f16_kernel(const float* __restrict__ src, uint16_t* __restrict__ dst, size_t n, bool vec) {
@@ -619,34 +639,34 @@ hipError_t launch_dma_any(const uint16_t* a, uint32_t lda, const uint16_t* b, ui
 }
 }  // namespace
 
+namespace {
+// The register-staged kernel.  kAligned needs both strides and the
+// contiguous extents (the reduction for a reduction-contiguous operand, its
+// index count for an index-contiguous one) to be multiples of 8.
+template <bool kATr, bool kBTr, typename OutT>
+hipError_t launch_reg(const uint16_t* a, uint32_t lda, const uint16_t* b, uint32_t ldb, OutT* c, uint32_t mo,
+                      uint32_t no, uint32_t r, hipStream_t stream) {
+  const uint32_t mtiles = (mo + BM - 1) / BM, ntiles = (no + BN - 1) / BN;
+  const bool aligned = lda % 8 == 0 && ldb % 8 == 0 && (kATr ? mo : r) % 8 == 0 && (kBTr ? no : r) % 8 == 0;
+  if (aligned)
+    hipLaunchKernelGGL((gemm_reg_kernel<true, kATr, kBTr, OutT>), dim3(mtiles * ntiles), dim3(THREADS), 0, stream,
+                       a, lda, b, ldb, c, mo, no, r, mtiles);
+  else
+    hipLaunchKernelGGL((gemm_reg_kernel<false, kATr, kBTr, OutT>), dim3(mtiles * ntiles), dim3(THREADS), 0, stream,
+                       a, lda, b, ldb, c, mo, no, r, mtiles);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_gemm_f16f32(const uint16_t* a, const uint16_t* b, float* c,
                               uint32_t m, uint32_t n, uint32_t k, hipStream_t stream) {
-  const uint32_t mtiles = (m + BM - 1) / BM;
-  const uint32_t ntiles = (n + BN - 1) / BN;
-  const dim3 grid(mtiles * ntiles), block(THREADS);
   // Direct-to-LDS path: A's 16-byte reduction chunks need k % 8 == 0 (a chunk
   // never straddles the end of the reduction), B's index chunks n % 8 == 0;
   // 32-bit per-lane byte offsets need 256 * k * 2 and 64 * n * 2 below 2^31.
   if (k > 0 && k % 8 == 0 && n % 8 == 0 && k < (1u << 22) && n < (1u << 24))
     return launch_dma_any<false, true, float>(a, k, b, n, c, m, n, k, stream);
-  if (k % 8 == 0 && n % 8 == 0)
-    hipLaunchKernelGGL(gemm_f16f32_kernel<true>, grid, block, 0, stream, a, b, c, m, n, k, mtiles);
-  else
-    hipLaunchKernelGGL(gemm_f16f32_kernel<false>, grid, block, 0, stream, a, b, c, m, n, k, mtiles);
-  return hipGetLastError();
+  return launch_reg<false, true, float>(a, k, b, n, c, m, n, k, stream);
 }
-
-namespace {
-hipError_t launch_strided_f16out(const uint16_t* a, size_t a_i, size_t a_r, const uint16_t* b, size_t b_r,
-                                 size_t b_j, uint16_t* c, uint32_t mo, uint32_t no, uint32_t r, hipStream_t stream) {
-  const size_t total = (size_t)mo * no;
-  size_t blocks = (total + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(gemm_strided_kernel<uint16_t>, dim3((uint32_t)blocks), dim3(256), 0, stream, a, a_i, a_r, b,
-                     b_r, b_j, c, mo, no, r);
-  return hipGetLastError();
-}
-}  // namespace
 
 hipError_t launch_gemm_f16f32_bwd(const uint16_t* a, const uint16_t* b, const float* grad, uint16_t* grad_a,
                                   uint16_t* grad_b, uint16_t* grad16, uint32_t m, uint32_t n, uint32_t k,
@@ -665,14 +685,14 @@ hipError_t launch_gemm_f16f32_bwd(const uint16_t* a, const uint16_t* b, const fl
   if (n % 8 == 0 && n < (1u << 22))
     e = launch_dma_any<false, false, uint16_t>(grad16, n, b, n, grad_a, m, k, n, stream);
   else
-    e = launch_strided_f16out(grad16, n, 1, b, 1, n, grad_a, m, k, n, stream);
+    e = launch_reg<false, false, uint16_t>(grad16, n, b, n, grad_a, m, k, n, stream);
   if (e != hipSuccess) return e;
   // grad_b[k, n] = a[m, k]^T . grad16[m, n]: both operands index contiguous;
   // any m (whole reduction rows past m read as zeros)
   if (k % 8 == 0 && n % 8 == 0 && k < (1u << 24) && n < (1u << 24))
     e = launch_dma_any<true, true, uint16_t>(a, k, grad16, n, grad_b, k, n, m, stream);
   else
-    e = launch_strided_f16out(a, 1, k, grad16, n, 1, grad_b, k, n, m, stream);
+    e = launch_reg<true, true, uint16_t>(a, k, grad16, n, grad_b, k, n, m, stream);
   return e;
 }
 

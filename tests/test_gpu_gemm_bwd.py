@@ -4,7 +4,8 @@ grad_a = f16(f16(G) . B^T), grad_b = f16(A^T . f16(G)); tolerance per element
 |d - Y*| <= ulp16(Y*) + 1e-5 * T against the unrounded float64 oracle value.
 Cases whose exact results are representable in f16 are compared bit for bit.
 Shapes cover the direct-to-LDS paths (strides multiples of 8; whole 64-k stages and a
-ragged last stage) and the any-shape fallback for each gradient (n or k not a multiple of 8).
+ragged last stage) and the register-staged MFMA kernel that takes any shape, for each gradient
+(n or k not a multiple of 8), over one tile and over several.
 """
 import numpy as np
 import pytest
@@ -53,7 +54,10 @@ def test_golden_handworked_bitwise():
     (300, 128, 136),      # grad_a direct, grad_b direct with a ragged last stage (m % 64 != 0)
     (192, 72, 264),       # grad_a direct with a ragged last stage (n % 64 != 0), grad_b direct
     (1000, 520, 776), (37, 200, 64), (65, 72, 80), (2, 8, 8),   # both ragged
-    (5, 7, 9), (1, 64, 1), (64, 64, 8), (130, 64, 3),           # n or k % 8 != 0: the strided fallback
+    (5, 7, 9), (1, 64, 1), (64, 64, 8), (130, 64, 3),           # n or k % 8 != 0: the register-staged kernel
+    # the register-staged kernel over several 256 x 256 tiles and 64-k stages: both gradients
+    # (n % 8 != 0), grad_b alone (k % 8 != 0), both with every extent odd
+    (270, 1030, 512), (520, 600, 260), (300, 1001, 515),
 ])
 def test_shapes(M, N, K):
     a, b, g = inputs(M, N, K, M * 31 + N * 7 + K)
@@ -82,6 +86,32 @@ def test_ragged_exact_integers_bitwise():
     ga, gb = run(a, b, g)
     (da, _), (db, _) = gemm_bwd(a, b, g)
     assert np.array_equal(ga, da.astype(np.float16)) and np.array_equal(gb, db.astype(np.float16))
+
+
+def test_any_shape_exact_integers_bitwise():
+    # n and k odd: both gradients on the register-staged kernel, exact small-integer sums
+    rng = np.random.default_rng(25)
+    M, N, K = 100, 275, 333
+    a = rng.integers(-4, 5, size=(M, K)).astype(np.float16)
+    b = rng.integers(-4, 5, size=(K, N)).astype(np.float16)
+    g = rng.integers(-4, 5, size=(M, N)).astype(np.float32)
+    ga, gb = run(a, b, g)
+    (da, _), (db, _) = gemm_bwd(a, b, g)
+    assert np.array_equal(ga, da.astype(np.float16)) and np.array_equal(gb, db.astype(np.float16))
+
+
+def test_large_odd_sampled():
+    # every extent odd at a large size (4 x 8 and 5 x 8 output tiles, 16-33 stages)
+    M, N, K = 1025, 2047, 1279
+    a, b, g = inputs(M, N, K, 4244)
+    ga, gb = run(a, b, g)
+    rng = np.random.default_rng(4245)
+    ra, ca = rng.integers(0, M, 2048), rng.integers(0, K, 2048)
+    rb, cb = rng.integers(0, K, 2048), rng.integers(0, N, 2048)
+    (pa, ta), (pb, tb) = gemm_bwd_at(a, b, g, ra, ca, rb, cb)
+    for name, x, y, t in (("grad_a", ga[ra, ca], pa, ta), ("grad_b", gb[rb, cb], pb, tb)):
+        bad, ratio = compare.excess(x, y, compare.f16_tolerance(y, t))
+        assert bad == 0, f"{name}: {bad} outside tolerance, max ratio {ratio:.3f}"
 
 
 def test_large_ragged_sampled():
