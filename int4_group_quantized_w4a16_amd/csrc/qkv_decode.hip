@@ -167,311 +167,338 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   }
   RedT& red = *red_p;
 
-  const uint32_t tid = threadIdx.x;
-  const uint32_t lane = tid & 63;
-  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t kb = lane >> 4;
-  const uint32_t l16 = lane & 15;
+  // The body.  kF: whole-vector loads of each lane's VEC columns (16-byte
+  // weights, 8-byte scales; aligned when n % 4 == 0).  kG: the strip's last
+  // columns may lie past N: stores are guarded, and with kF a lane whose
+  // columns lie past N (with n % 4 == 0 all four do, or none) loads the last
+  // VEC columns instead -- valid memory; MFMA columns do not mix and those
+  // outputs are never stored.  Without kF, every column load is guarded.  A
+  // kernel built for n % BN != 0 thus runs whole-vector loads on every strip
+  // when n % 4 == 0, and the column-guarded loads only otherwise.
+  auto body = [&](auto full_tag, auto guard_tag) {
+    constexpr bool kF = decltype(full_tag)::value;
+    constexpr bool kG = decltype(guard_tag)::value;
+    static_assert(kF || kG, "guarded loads go with guarded stores");
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t kb = lane >> 4;
+    const uint32_t l16 = lane & 15;
 
-  const uint32_t q = blockIdx.x / nstrips;
-  const uint32_t n0 = (blockIdx.x % nstrips) * BN;
-  const uint32_t M = p.m, N = p.n, K = p.k;
-  const uint32_t G = K / kGroup;
-  const uint32_t rblk = wave % RSPLIT, kpart = wave / RSPLIT;
-  const uint32_t g_begin = (uint32_t)(((uint64_t)kpart * G) / KSPLIT);
-  const uint32_t g_end = (uint32_t)(((uint64_t)(kpart + 1) * G) / KSPLIT);
+    const uint32_t q = blockIdx.x / nstrips;
+    const uint32_t n0 = (blockIdx.x % nstrips) * BN;
+    const uint32_t M = p.m, N = p.n, K = p.k;
+    const uint32_t G = K / kGroup;
+    const uint32_t rblk = wave % RSPLIT, kpart = wave / RSPLIT;
+    const uint32_t g_begin = (uint32_t)(((uint64_t)kpart * G) / KSPLIT);
+    const uint32_t g_end = (uint32_t)(((uint64_t)(kpart + 1) * G) / KSPLIT);
 
-  const uint32_t* w = q == 0 ? p.w[0] : (q == 1 ? p.w[1] : p.w[2]);
-  const uint16_t* s = q == 0 ? p.s[0] : (q == 1 ? p.s[1] : p.s[2]);
-  const uint32_t colv = n0 + VEC * l16;     // first of the lane's VEC columns
-  // x of a group reaches the MFMAs through a wave-private LDS slice: load j
-  // brings rows 4j .. 4j+3 of the wave's row block, 256 contiguous bytes each
-  // (lane l: row 4j + l/16, 16-byte chunk l % 16), and each A fragment is read
-  // back from there.  Loading the fragments straight from memory would make
-  // every load touch 16 rows 2*K bytes apart with 64 bytes each, and the
-  // whole chip reads this same x: that costs ~1.5 us per call at m = 8,
-  // n = k = 4096.  Rows are padded to 17 chunks, so a fragment read (16 rows,
-  // one chunk each) is free of bank conflicts.
-  // Rows past M repeat row M-1 (their outputs are never stored, and MFMA rows
-  // do not mix).  Every load is issued, whatever M (repeated rows read the same
-  // addresses): a load under a branch would make the compiler wait for all
-  // loads in flight, the next group's included, before the first LDS write.
-  const uint32_t xbase = 16 * RT * rblk;
-  const uint32_t xvalid = M > xbase ? (M - xbase < (uint32_t)XROWS ? M - xbase : XROWS) : 1;  // rows kept
-  // element offset of load j's chunk within a group's x columns (computed at
-  // each load: few registers are free in the widest configuration)
-  auto xoff = [&](int j) {
-    const uint32_t lr = 4 * j + kb;
-    const uint32_t row = xbase + (lr < xvalid ? lr : xvalid - 1);
-    return (row < M ? row : M - 1) * K + l16 * 8;
-  };
-  uint32_t xfrag[RT];       // LDS row of the lane's A fragment in row tile r
-#pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    const uint32_t lr = 16 * r + l16;
-    xfrag[r] = (lr < xvalid ? lr : xvalid - 1) * XLD + kb;
-  }
-  uint4* const xw = xl_base + wave * (NG == 0 ? XROWS * XLD : NG * XROWS * 16);
-  // lane (kb, c) of k-step ks holds packed rows WPK*(4ks + kb) + j, j < WPK:
-  // the 8 consecutive k of its B operand.  Byte offset from the row
-  // PR*g + 4*WPK*ks + j of the load's base:
-  const uint32_t woff = ((WPK * kb) * N + colv) * 4;
-  const uint32_t* wlane = w + (size_t)(WPK * kb) * N + colv;   // the same, as an address
-  constexpr int kWPolicy = RSPLIT == 1 ? 2 : 0;   // non-temporal when one wave reads each word
-  constexpr bool kBuf = WAVES == 16;              // buffer loads (see above)
-  using ScT = std::conditional_t<kBuf, uint16_t, uint32_t>;
-
-  floatx4 acc[VEC][RT];
-#pragma unroll
-  for (int t = 0; t < VEC; ++t)
-#pragma unroll
-    for (int r = 0; r < RT; ++r) acc[t][r] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  struct Chunk {
-    uint32_t wv[GCHUNK][4][WPK][VEC];
-    uint4 xs[GCHUNK][XROWS / 4];     // x rows 4j .. 4j+3 of the group, 16 bytes per lane
-    // f16 bits of the scales: packed two per register in the 16-wave
-    // configurations (register budget), one per register otherwise (1-2% faster there)
-    ScT sc[GCHUNK][VEC];
-  };
-  // Loads of GCHUNK groups starting at g0.  Groups past the wave's range are
-  // clamped to its last group (loaded, never used) so that every chunk issues
-  // the same loads and the compiler can keep the next chunk in flight.  With
-  // kTrim, the weight loads of such a group go through a zero-range
-  // descriptor instead: a repeat of streamed (non-temporal) words was often
-  // fetched from memory again (n = 4096, k = 8192, m = 8: 1.17x the
-  // algorithmic bytes).
-  auto load_chunk = [&](uint32_t g0, Chunk& c, bool checked) {
-#pragma unroll
-    for (int gi = 0; gi < GCHUNK; ++gi) {
-      const bool live = !checked || g0 + gi < g_end;   // checked = false: inside the range
-      const uint32_t g = live ? g0 + gi : g_end - 1;
-      // x first: loads complete in issue order, so the LDS copy of x (needed
-      // before any MFMA) need not wait for the weights of later k-steps
-      if constexpr (kBuf) {
-        const __amdgpu_buffer_rsrc_t xr = rsrc_of(p.x + (size_t)g * kGroup);
-#pragma unroll
-        for (int j = 0; j < XROWS / 4; ++j)
-          c.xs[gi][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff(j) * 2, 0, 0));
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int j = 0; j < WPK; ++j) {
-            const __amdgpu_buffer_rsrc_t wr =
-                rsrc_of(w + ((size_t)g * PR + ks * 4 * WPK + j) * N, kTrim && kFull && !live ? 0 : -1);
-            if (kFull) {
-              const WV v = buf_words<VEC, kWPolicy>(wr, woff);
-              __builtin_memcpy(c.wv[gi][ks][j], &v, sizeof(v));
-            } else {
-#pragma unroll
-              for (int t = 0; t < VEC; ++t)
-                c.wv[gi][ks][j][t] = (colv + t < N) ? buf_words<1, kWPolicy>(wr, woff + 4 * t) : 0u;
-            }
-          }
-        const __amdgpu_buffer_rsrc_t sr = rsrc_of(s + (size_t)g * N);
-        if (kFull) {
-          const auto sv = buf_halves<VEC>(sr, colv * 2);
-          __builtin_memcpy(c.sc[gi], &sv, sizeof(sv));
-        } else {
-#pragma unroll
-          for (int t = 0; t < VEC; ++t)
-            c.sc[gi][t] = (colv + t < N) ? buf_halves<1>(sr, (colv + t) * 2) : (uint16_t)0;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < XROWS / 4; ++j)
-          c.xs[gi][j] = *reinterpret_cast<const uint4*>(p.x + xoff(j) + (size_t)g * kGroup);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int j = 0; j < WPK; ++j) {
-            const size_t roff = ((size_t)g * PR + ks * 4 * WPK + j) * N;
-            if (kFull) {
-              const WV v = load_w<RSPLIT == 1>(reinterpret_cast<const WV*>(wlane + roff));
-              __builtin_memcpy(c.wv[gi][ks][j], &v, sizeof(v));
-            } else {
-#pragma unroll
-              for (int t = 0; t < VEC; ++t)
-                c.wv[gi][ks][j][t] = (colv + t < N) ? load_w<RSPLIT == 1>(wlane + roff + t) : 0u;
-            }
-          }
-        if (kFull) {
-          using HV = typename HalfVec<VEC>::T;
-          const HV sv = *reinterpret_cast<const HV*>(s + (size_t)g * N + colv);
-          uint16_t sh[VEC];
-          __builtin_memcpy(sh, &sv, sizeof(sv));
-#pragma unroll
-          for (int t = 0; t < VEC; ++t) c.sc[gi][t] = sh[t];
-        } else {
-#pragma unroll
-          for (int t = 0; t < VEC; ++t) c.sc[gi][t] = (colv + t < N) ? s[(size_t)g * N + colv + t] : (uint16_t)0;
-        }
-      }
-    }
-  };
-  auto compute_chunk = [&](uint32_t g0, const Chunk& c, bool checked) {
-#pragma unroll
-    for (int gi = 0; gi < GCHUNK; ++gi) {
-      if (!checked || g0 + gi < g_end) {   // wave-uniform
-        // LDS accesses of one wave execute in order: these writes follow the
-        // previous group's fragment reads, and the reads below follow them;
-        // the empty asm statements keep the compiler from reordering them.
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int j = 0; j < XROWS / 4; ++j) xw[(4 * j + kb) * XLD + l16] = c.xs[gi][j];
-        asm volatile("" ::: "memory");
-        floatx4 part[VEC][RT];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          half8_t a[RT];
-#pragma unroll
-          for (int r = 0; r < RT; ++r)
-            a[r] = kNatural ? __builtin_bit_cast(half8_t, xw[xfrag[r] + 4 * ks])
-                            : permute_x_like_int4x8(xw[xfrag[r] + 4 * ks]);
-#pragma unroll
-          for (int t = 0; t < VEC; ++t) {
-            half8_t b;
-            if constexpr (kNatural) {
-              uint32_t words[WPK];
-#pragma unroll
-              for (int j = 0; j < WPK; ++j) words[j] = c.wv[gi][ks][j][t];
-              b = unpack_b_scaled<BITS>(words);
-            } else {
-              b = unpack_int4x8_interleaved(c.wv[gi][ks][0][t]);
-            }
-#pragma unroll
-            for (int r = 0; r < RT; ++r)
-              part[t][r] = mfma16x16x32(a[r], b, ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : part[t][r]);
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < VEC; ++t) {
-          const float sf = kNatural ? h2f((uint16_t)c.sc[gi][t]) * kUnpackScaledInv : h2f((uint16_t)c.sc[gi][t]);
-#pragma unroll
-          for (int r = 0; r < RT; ++r)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[t][r][i] = __builtin_fmaf(part[t][r][i], sf, acc[t][r][i]);
-        }
-      }
-    }
-  };
-
-  if constexpr (NG > 0) {
-    // Every group of the wave in flight at once: first the x of every group,
-    // two direct loads each (rows 4j .. 4j+3, 16 chunks each, into slice gi;
-    // the chunk of row r at position c sits at c ^ r, so that a fragment read
-    // of 8 rows hits 8 distinct 16-byte bank groups), then per group four
-    // weight loads and one scale load.  x goes first because the compiler
-    // makes the first read of any slice wait for every direct load issued
-    // before it (it cannot tell the slices apart), so x issued per group
-    // would hold group 0's compute until later groups' x had landed.  Groups
-    // past the wave's range load through zero-range descriptors.
-    struct WChunk {
-      uint32_t wv[4][VEC];
-      uint16_t sc[VEC];
+    const uint32_t* w = q == 0 ? p.w[0] : (q == 1 ? p.w[1] : p.w[2]);
+    const uint16_t* s = q == 0 ? p.s[0] : (q == 1 ? p.s[1] : p.s[2]);
+    const uint32_t colv = n0 + VEC * l16;     // first of the lane's VEC columns
+    const uint32_t colv_ld = kF && kG && colv >= N ? N - VEC : colv;   // the columns it loads
+    // without kF, column by column: columns past N load column N-1 instead
+    // (no load sits under a branch, which would make the compiler's waits
+    // conservative; those outputs are never stored)
+    auto col_of = [&](int t) { return colv + t < N ? colv + t : N - 1; };
+    // x of a group reaches the MFMAs through a wave-private LDS slice: load j
+    // brings rows 4j .. 4j+3 of the wave's row block, 256 contiguous bytes each
+    // (lane l: row 4j + l/16, 16-byte chunk l % 16), and each A fragment is read
+    // back from there.  Loading the fragments straight from memory would make
+    // every load touch 16 rows 2*K bytes apart with 64 bytes each, and the
+    // whole chip reads this same x: that costs ~1.5 us per call at m = 8,
+    // n = k = 4096.  Rows are padded to 17 chunks, so a fragment read (16 rows,
+    // one chunk each) is free of bank conflicts.
+    // Rows past M repeat row M-1 (their outputs are never stored, and MFMA rows
+    // do not mix).  Every load is issued, whatever M (repeated rows read the same
+    // addresses): a load under a branch would make the compiler wait for all
+    // loads in flight, the next group's included, before the first LDS write.
+    const uint32_t xbase = 16 * RT * rblk;
+    const uint32_t xvalid = M > xbase ? (M - xbase < (uint32_t)XROWS ? M - xbase : XROWS) : 1;  // rows kept
+    // element offset of load j's chunk within a group's x columns (computed at
+    // each load: few registers are free in the widest configuration)
+    auto xoff = [&](int j) {
+      const uint32_t lr = 4 * j + kb;
+      const uint32_t row = xbase + (lr < xvalid ? lr : xvalid - 1);
+      return (row < M ? row : M - 1) * K + l16 * 8;
     };
-    WChunk c[NG];
-#pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-      const bool live = g_begin + gi < g_end;
-      const uint32_t g = live ? g_begin + gi : g_begin;
-      const __amdgpu_buffer_rsrc_t xr = rsrc_of(p.x + (size_t)g * kGroup, live ? -1 : 0);
-#pragma unroll
-      for (int j = 0; j < XROWS / 4; ++j) {
-        const uint32_t lr = 4 * j + kb;                 // LDS row of this lane's chunk
-        const uint32_t row = xbase + (lr < xvalid ? lr : xvalid - 1);
-        const uint32_t off = ((row < M ? row : M - 1) * K + (l16 ^ lr) * 8) * 2;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            xr, (__attribute__((address_space(3))) void*)(xw + (gi * XROWS + 4 * j) * 16), 16, off, 0, 0, 0);
-      }
+    uint32_t xfrag[RT];       // LDS row of the lane's A fragment in row tile r
+  #pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const uint32_t lr = 16 * r + l16;
+      xfrag[r] = (lr < xvalid ? lr : xvalid - 1) * XLD + kb;
     }
-    // the load order the waits below count on: all x, then the weights and scales group by group
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-      const bool live = g_begin + gi < g_end;
-      const uint32_t g = live ? g_begin + gi : g_begin;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const __amdgpu_buffer_rsrc_t wr = rsrc_of(w + ((size_t)g * PR + ks * 4) * N, live ? -1 : 0);
-        const WV v = buf_words<VEC, kWPolicy>(wr, woff);
-        __builtin_memcpy(c[gi].wv[ks], &v, sizeof(v));
-      }
-      const auto sv = buf_halves<VEC>(rsrc_of(s + (size_t)g * N), colv * 2);
-      __builtin_memcpy(c[gi].sc, &sv, sizeof(sv));
-      asm volatile("" ::: "memory");
-    }
-    const uint32_t frow = l16 < xvalid ? l16 : xvalid - 1;   // the lane's A row (rows past m repeat)
-#pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-      if (g_begin + gi < g_end) {   // wave-uniform
-        // every x has landed, and group gi's weights and scales, once at most
-        // the later groups' 5 loads each are outstanding; loads complete in
-        // issue order
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 * (NG - 1 - gi)) : "memory");
-        floatx4 part[VEC];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const uint32_t ch = 4 * ks + kb;
-          const half8_t a = permute_x_like_int4x8(xw[(gi * XROWS + frow) * 16 + (ch ^ frow)]);
-#pragma unroll
-          for (int t = 0; t < VEC; ++t) {
-            const half8_t b = unpack_int4x8_interleaved(c[gi].wv[ks][t]);
-            part[t] = mfma16x16x32(a, b, ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : part[t]);
+    uint4* const xw = xl_base + wave * (NG == 0 ? XROWS * XLD : NG * XROWS * 16);
+    // lane (kb, c) of k-step ks holds packed rows WPK*(4ks + kb) + j, j < WPK:
+    // the 8 consecutive k of its B operand.  Byte offset from the row
+    // PR*g + 4*WPK*ks + j of the load's base:
+    const uint32_t woff = ((WPK * kb) * N + colv_ld) * 4;
+    const uint32_t* wlane = w + (size_t)(WPK * kb) * N + colv_ld;   // the same, as an address
+    constexpr int kWPolicy = RSPLIT == 1 ? 2 : 0;   // non-temporal when one wave reads each word
+    constexpr bool kBuf = WAVES == 16;              // buffer loads (see above)
+    using ScT = std::conditional_t<kBuf, uint16_t, uint32_t>;
+
+    floatx4 acc[VEC][RT];
+  #pragma unroll
+    for (int t = 0; t < VEC; ++t)
+  #pragma unroll
+      for (int r = 0; r < RT; ++r) acc[t][r] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    struct Chunk {
+      uint32_t wv[GCHUNK][4][WPK][VEC];
+      uint4 xs[GCHUNK][XROWS / 4];     // x rows 4j .. 4j+3 of the group, 16 bytes per lane
+      // f16 bits of the scales: packed two per register in the 16-wave
+      // configurations (register budget), one per register otherwise (1-2% faster there)
+      ScT sc[GCHUNK][VEC];
+    };
+    // Loads of GCHUNK groups starting at g0.  Groups past the wave's range are
+    // clamped to its last group (loaded, never used) so that every chunk issues
+    // the same loads and the compiler can keep the next chunk in flight.  With
+    // kTrim, the weight loads of such a group go through a zero-range
+    // descriptor instead: a repeat of streamed (non-temporal) words was often
+    // fetched from memory again (n = 4096, k = 8192, m = 8: 1.17x the
+    // algorithmic bytes).
+    auto load_chunk = [&](uint32_t g0, Chunk& c, bool checked) {
+  #pragma unroll
+      for (int gi = 0; gi < GCHUNK; ++gi) {
+        const bool live = !checked || g0 + gi < g_end;   // checked = false: inside the range
+        const uint32_t g = live ? g0 + gi : g_end - 1;
+        // x first: loads complete in issue order, so the LDS copy of x (needed
+        // before any MFMA) need not wait for the weights of later k-steps
+        if constexpr (kBuf) {
+          const __amdgpu_buffer_rsrc_t xr = rsrc_of(p.x + (size_t)g * kGroup);
+  #pragma unroll
+          for (int j = 0; j < XROWS / 4; ++j)
+            c.xs[gi][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff(j) * 2, 0, 0));
+  #pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+  #pragma unroll
+            for (int j = 0; j < WPK; ++j) {
+              const __amdgpu_buffer_rsrc_t wr =
+                  rsrc_of(w + ((size_t)g * PR + ks * 4 * WPK + j) * N, kTrim && kF && !live ? 0 : -1);
+              if (kF) {
+                const WV v = buf_words<VEC, kWPolicy>(wr, woff);
+                __builtin_memcpy(c.wv[gi][ks][j], &v, sizeof(v));
+              } else {
+  #pragma unroll
+                for (int t = 0; t < VEC; ++t)
+                  c.wv[gi][ks][j][t] = buf_words<1, kWPolicy>(wr, ((WPK * kb) * N + col_of(t)) * 4);
+              }
+            }
+          const __amdgpu_buffer_rsrc_t sr = rsrc_of(s + (size_t)g * N);
+          if (kF) {
+            const auto sv = buf_halves<VEC>(sr, colv_ld * 2);
+            __builtin_memcpy(c.sc[gi], &sv, sizeof(sv));
+          } else {
+  #pragma unroll
+            for (int t = 0; t < VEC; ++t) c.sc[gi][t] = buf_halves<1>(sr, col_of(t) * 2);
+          }
+        } else {
+  #pragma unroll
+          for (int j = 0; j < XROWS / 4; ++j)
+            c.xs[gi][j] = *reinterpret_cast<const uint4*>(p.x + xoff(j) + (size_t)g * kGroup);
+  #pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+  #pragma unroll
+            for (int j = 0; j < WPK; ++j) {
+              const size_t roff = ((size_t)g * PR + ks * 4 * WPK + j) * N;
+              if (kF) {
+                const WV v = load_w<RSPLIT == 1>(reinterpret_cast<const WV*>(wlane + roff));
+                __builtin_memcpy(c.wv[gi][ks][j], &v, sizeof(v));
+              } else {
+  #pragma unroll
+                for (int t = 0; t < VEC; ++t)
+                  c.wv[gi][ks][j][t] = load_w<RSPLIT == 1>(w + (size_t)(WPK * kb) * N + roff + col_of(t));
+              }
+            }
+          if (kF) {
+            using HV = typename HalfVec<VEC>::T;
+            const HV sv = *reinterpret_cast<const HV*>(s + (size_t)g * N + colv_ld);
+            uint16_t sh[VEC];
+            __builtin_memcpy(sh, &sv, sizeof(sv));
+  #pragma unroll
+            for (int t = 0; t < VEC; ++t) c.sc[gi][t] = sh[t];
+          } else {
+  #pragma unroll
+            for (int t = 0; t < VEC; ++t) c.sc[gi][t] = s[(size_t)g * N + col_of(t)];
           }
         }
-#pragma unroll
-        for (int t = 0; t < VEC; ++t) {
-          const float sf = h2f(c[gi].sc[t]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[t][0][i] = __builtin_fmaf(part[t][i], sf, acc[t][0][i]);
+      }
+    };
+    auto compute_chunk = [&](uint32_t g0, const Chunk& c, bool checked) {
+  #pragma unroll
+      for (int gi = 0; gi < GCHUNK; ++gi) {
+        if (!checked || g0 + gi < g_end) {   // wave-uniform
+          // LDS accesses of one wave execute in order: these writes follow the
+          // previous group's fragment reads, and the reads below follow them;
+          // the empty asm statements keep the compiler from reordering them.
+          asm volatile("" ::: "memory");
+  #pragma unroll
+          for (int j = 0; j < XROWS / 4; ++j) xw[(4 * j + kb) * XLD + l16] = c.xs[gi][j];
+          asm volatile("" ::: "memory");
+          floatx4 part[VEC][RT];
+  #pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            half8_t a[RT];
+  #pragma unroll
+            for (int r = 0; r < RT; ++r)
+              a[r] = kNatural ? __builtin_bit_cast(half8_t, xw[xfrag[r] + 4 * ks])
+                              : permute_x_like_int4x8(xw[xfrag[r] + 4 * ks]);
+  #pragma unroll
+            for (int t = 0; t < VEC; ++t) {
+              half8_t b;
+              if constexpr (kNatural) {
+                uint32_t words[WPK];
+  #pragma unroll
+                for (int j = 0; j < WPK; ++j) words[j] = c.wv[gi][ks][j][t];
+                b = unpack_b_scaled<BITS>(words);
+              } else {
+                b = unpack_int4x8_interleaved(c.wv[gi][ks][0][t]);
+              }
+  #pragma unroll
+              for (int r = 0; r < RT; ++r)
+                part[t][r] = mfma16x16x32(a[r], b, ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : part[t][r]);
+            }
+          }
+  #pragma unroll
+          for (int t = 0; t < VEC; ++t) {
+            const float sf = kNatural ? h2f((uint16_t)c.sc[gi][t]) * kUnpackScaledInv : h2f((uint16_t)c.sc[gi][t]);
+  #pragma unroll
+            for (int r = 0; r < RT; ++r)
+  #pragma unroll
+              for (int i = 0; i < 4; ++i) acc[t][r][i] = __builtin_fmaf(part[t][r][i], sf, acc[t][r][i]);
+          }
+        }
+      }
+    };
+
+    if constexpr (NG > 0) {
+      // Every group of the wave in flight at once: first the x of every group,
+      // two direct loads each (rows 4j .. 4j+3, 16 chunks each, into slice gi;
+      // the chunk of row r at position c sits at c ^ r, so that a fragment read
+      // of 8 rows hits 8 distinct 16-byte bank groups), then per group four
+      // weight loads and one scale load.  x goes first because the compiler
+      // makes the first read of any slice wait for every direct load issued
+      // before it (it cannot tell the slices apart), so x issued per group
+      // would hold group 0's compute until later groups' x had landed.  Groups
+      // past the wave's range load through zero-range descriptors.
+      struct WChunk {
+        uint32_t wv[4][VEC];
+        uint16_t sc[VEC];
+      };
+      WChunk c[NG];
+  #pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        const bool live = g_begin + gi < g_end;
+        const uint32_t g = live ? g_begin + gi : g_begin;
+        const __amdgpu_buffer_rsrc_t xr = rsrc_of(p.x + (size_t)g * kGroup, live ? -1 : 0);
+  #pragma unroll
+        for (int j = 0; j < XROWS / 4; ++j) {
+          const uint32_t lr = 4 * j + kb;                 // LDS row of this lane's chunk
+          const uint32_t row = xbase + (lr < xvalid ? lr : xvalid - 1);
+          const uint32_t off = ((row < M ? row : M - 1) * K + (l16 ^ lr) * 8) * 2;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              xr, (__attribute__((address_space(3))) void*)(xw + (gi * XROWS + 4 * j) * 16), 16, off, 0, 0, 0);
+        }
+      }
+      // the load order the waits below count on: all x, then the weights and scales group by group
+      asm volatile("" ::: "memory");
+  #pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        const bool live = g_begin + gi < g_end;
+        const uint32_t g = live ? g_begin + gi : g_begin;
+  #pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const __amdgpu_buffer_rsrc_t wr = rsrc_of(w + ((size_t)g * PR + ks * 4) * N, live ? -1 : 0);
+          const WV v = buf_words<VEC, kWPolicy>(wr, woff);
+          __builtin_memcpy(c[gi].wv[ks], &v, sizeof(v));
+        }
+        const auto sv = buf_halves<VEC>(rsrc_of(s + (size_t)g * N), colv_ld * 2);
+        __builtin_memcpy(c[gi].sc, &sv, sizeof(sv));
+        asm volatile("" ::: "memory");
+      }
+      const uint32_t frow = l16 < xvalid ? l16 : xvalid - 1;   // the lane's A row (rows past m repeat)
+  #pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        if (g_begin + gi < g_end) {   // wave-uniform
+          // every x has landed, and group gi's weights and scales, once at most
+          // the later groups' 5 loads each are outstanding; loads complete in
+          // issue order
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 * (NG - 1 - gi)) : "memory");
+          floatx4 part[VEC];
+  #pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const uint32_t ch = 4 * ks + kb;
+            const half8_t a = permute_x_like_int4x8(xw[(gi * XROWS + frow) * 16 + (ch ^ frow)]);
+  #pragma unroll
+            for (int t = 0; t < VEC; ++t) {
+              const half8_t b = unpack_int4x8_interleaved(c[gi].wv[ks][t]);
+              part[t] = mfma16x16x32(a, b, ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : part[t]);
+            }
+          }
+  #pragma unroll
+          for (int t = 0; t < VEC; ++t) {
+            const float sf = h2f(c[gi].sc[t]);
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][0][i] = __builtin_fmaf(part[t][i], sf, acc[t][0][i]);
+          }
+        }
+      }
+      __syncthreads();   // every wave is done with its x slices before the reduction reuses them
+    } else if (g_begin < g_end) {
+      // two register buffers used ping-pong: chunk c+1 is in flight while
+      // chunk c computes.  Every load is issued unconditionally (past the
+      // wave's range they repeat its last group, which the cache holds): a load
+      // under a branch leaves the compiler's wait counts conservative where the
+      // paths meet, and it would wait for chunk c+1 before computing chunk c.
+      Chunk ca, cb;
+      if (g_end - g_begin == 2 * GCHUNK) {
+        // exactly two chunks (every wave at m <= 16, k = 4096): straight-line
+        load_chunk(g_begin, ca, false);
+        load_chunk(g_begin + GCHUNK, cb, false);
+        compute_chunk(g_begin, ca, false);
+        compute_chunk(g_begin + GCHUNK, cb, false);
+      } else {
+        load_chunk(g_begin, ca, true);
+        load_chunk(g_begin + GCHUNK, cb, true);
+        for (uint32_t g0 = g_begin; g0 < g_end; g0 += 2 * GCHUNK) {
+          compute_chunk(g0, ca, true);
+          load_chunk(g0 + 2 * GCHUNK, ca, true);
+          compute_chunk(g0 + GCHUNK, cb, true);
+          load_chunk(g0 + 3 * GCHUNK, cb, true);
         }
       }
     }
-    __syncthreads();   // every wave is done with its x slices before the reduction reuses them
-  } else if (g_begin < g_end) {
-    // two register buffers used ping-pong: chunk c+1 is in flight while
-    // chunk c computes.  Every load is issued unconditionally (past the
-    // wave's range they repeat its last group, which the cache holds): a load
-    // under a branch leaves the compiler's wait counts conservative where the
-    // paths meet, and it would wait for chunk c+1 before computing chunk c.
-    Chunk ca, cb;
-    if (g_end - g_begin == 2 * GCHUNK) {
-      // exactly two chunks (every wave at m <= 16, k = 4096): straight-line
-      load_chunk(g_begin, ca, false);
-      load_chunk(g_begin + GCHUNK, cb, false);
-      compute_chunk(g_begin, ca, false);
-      compute_chunk(g_begin + GCHUNK, cb, false);
-    } else {
-      load_chunk(g_begin, ca, true);
-      load_chunk(g_begin + GCHUNK, cb, true);
-      for (uint32_t g0 = g_begin; g0 < g_end; g0 += 2 * GCHUNK) {
-        compute_chunk(g0, ca, true);
-        load_chunk(g0 + 2 * GCHUNK, ca, true);
-        compute_chunk(g0 + GCHUNK, cb, true);
-        load_chunk(g0 + 3 * GCHUNK, cb, true);
-      }
+
+    // lane holds rows 16r + 4*kb + i of its row block, MFMA column l16 = output column VEC*l16 + t
+  #pragma unroll
+    for (int t = 0; t < VEC; ++t)
+  #pragma unroll
+      for (int r = 0; r < RT; ++r)
+  #pragma unroll
+        for (int i = 0; i < 4; ++i)
+          red[kpart][16 * RT * rblk + 16 * r + 4 * kb + i][VEC * l16 + t] = acc[t][r][i];
+    __syncthreads();
+
+    uint16_t* __restrict__ out = q == 0 ? p.out[0] : (q == 1 ? p.out[1] : p.out[2]);
+    for (uint32_t e = tid; e < M * BN; e += THREADS) {
+      const uint32_t row = e / BN, c = e % BN;
+      float sum = 0.f;
+  #pragma unroll
+      for (int kp = 0; kp < KSPLIT; ++kp) sum += red[kp][row][c];
+      const uint32_t gc = n0 + c;
+      if (!kG || gc < N) out[(size_t)row * N + gc] = __builtin_bit_cast(uint16_t, (_Float16)sum);
     }
-  }
-
-  // lane holds rows 16r + 4*kb + i of its row block, MFMA column l16 = output column VEC*l16 + t
-#pragma unroll
-  for (int t = 0; t < VEC; ++t)
-#pragma unroll
-    for (int r = 0; r < RT; ++r)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        red[kpart][16 * RT * rblk + 16 * r + 4 * kb + i][VEC * l16 + t] = acc[t][r][i];
-  __syncthreads();
-
-  uint16_t* __restrict__ out = q == 0 ? p.out[0] : (q == 1 ? p.out[1] : p.out[2]);
-  for (uint32_t e = tid; e < M * BN; e += THREADS) {
-    const uint32_t row = e / BN, c = e % BN;
-    float sum = 0.f;
-#pragma unroll
-    for (int kp = 0; kp < KSPLIT; ++kp) sum += red[kp][row][c];
-    const uint32_t gc = n0 + c;
-    if (kFull || gc < N) out[(size_t)row * N + gc] = __builtin_bit_cast(uint16_t, (_Float16)sum);
+  };
+  if constexpr (kFull) {
+    body(std::true_type{}, std::false_type{});
+  } else {
+    if (p.n % 4 != 0)
+      body(std::false_type{}, std::true_type{});
+    else if ((blockIdx.x % nstrips + 1) * BN <= p.n)
+      body(std::true_type{}, std::false_type{});
+    else
+      body(std::true_type{}, std::true_type{});
   }
 }
 

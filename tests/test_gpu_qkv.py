@@ -79,6 +79,11 @@ def test_tiny_config_all_outputs():
     # of waves (66 and 34 groups: 33 and 17 per set), and odd counts (97, 35: one set)
     (200, 520, 12416), (1100, 1000, 4480), (150, 264, 8448), (150, 261, 8448),
     (1100, 1000, 4352), (1100, 1001, 4352),
+    # split-K with n % 64 != 0 but n % 4 == 0: whole-vector loads on every strip, the last strip's
+    # lanes past n loading the last valid columns (decode width, and K > 4096)
+    (8, 4088, 4096), (5, 1000, 4096), (16, 4040, 4608), (30, 1004, 512),
+    # n % 4 != 0: column-by-column loads, columns past n loading column n - 1
+    (8, 4095, 4096), (13, 1001, 640), (40, 999, 384),
     # four sets of waves over 64-row tiles, one output per workgroup: ragged rows and columns,
     # n % 8 != 0, several groups per set
     (33, 72, 512), (47, 130, 1024), (64, 61, 2048), (50, 4096, 1536),
