@@ -121,10 +121,10 @@ __device__ __forceinline__ typename HalfVec<V>::T buf_halves(__amdgpu_buffer_rsr
 // BITS = 4 (W4A16: one packed word per 8 k of a column) or 8 (W8A16: two).
 // kTrim: some wave's group range is not exactly two chunks (its loop runs
 // past the range), and the weight loads past it go through a zero-range
-// descriptor (16-wave buffer-load configurations, whole strips).
+// descriptor (16-wave buffer-load configurations, n % 4 == 0).
 // NG > 0: every wave issues the loads of all its groups (at most NG) at once
 // and x goes to LDS by direct loads, which frees the registers that holding
-// x would take (16 waves, whole strips, m <= 8, at most NG groups per wave).
+// x would take (16 waves, n % 4 == 0, m <= 8, at most NG groups per wave).
 template <int BITS, int RT, int RSPLIT, int VEC, int WAVES, bool kFull, int XR, bool kTrim = false, int NG = 0>
 __global__ void __launch_bounds__(WAVES * 64, 1)
 qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
@@ -146,7 +146,7 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
   constexpr bool kNatural = RT >= 2 || BITS == 8;
   static_assert(XR % 4 == 0 && XR <= 16 * RT, "x rows per wave");
   constexpr int XLD = kGroup / 8 + 1;           // 16-byte chunks per padded LDS row of x
-  static_assert(NG == 0 || (WAVES == 16 && kFull && RT == 1 && XR == 8 && BITS == 4 && NG <= 4),
+  static_assert(NG == 0 || (WAVES == 16 && RT == 1 && XR == 8 && BITS == 4 && NG <= 4),
                 "all groups in flight: the 16-wave m <= 8 configuration only");
   // LDS: the reduction buffer, and per wave either one padded x slice (x
   // staged through registers) or NG unpadded, swizzled ones (direct loads;
@@ -490,15 +490,24 @@ qkv_decode_kernel(QkvProblem p, uint32_t nstrips) {
       if (!kG || gc < N) out[(size_t)row * N + gc] = __builtin_bit_cast(uint16_t, (_Float16)sum);
     }
   };
+  // Kernels with trimmed loads or all groups in flight are launched for n % 4 == 0 only and
+  // do not build the column-by-column body.
   if constexpr (kFull) {
     body(std::true_type{}, std::false_type{});
   } else {
-    if (p.n % 4 != 0)
-      body(std::false_type{}, std::true_type{});
-    else if ((blockIdx.x % nstrips + 1) * BN <= p.n)
-      body(std::true_type{}, std::false_type{});
-    else
-      body(std::true_type{}, std::true_type{});
+    bool done = false;
+    if constexpr (NG == 0 && !kTrim) {
+      if (p.n % 4 != 0) {
+        body(std::false_type{}, std::true_type{});
+        done = true;
+      }
+    }
+    if (!done) {
+      if ((blockIdx.x % nstrips + 1) * BN <= p.n)
+        body(std::true_type{}, std::false_type{});
+      else
+        body(std::true_type{}, std::true_type{});
+    }
   }
 }
 
@@ -517,6 +526,13 @@ hipError_t launch_split_k(const QkvProblem& p, hipStream_t stream) {
                          p, nstrips);
       return hipGetLastError();
     }
+    if constexpr (!kOnlyFull) {
+      if (p.n % 4 == 0 && !straight) {
+        hipLaunchKernelGGL((qkv_decode_kernel<BITS, RT, RSPLIT, VEC, WAVES, false, XR, true>), grid, block, 0,
+                           stream, p, nstrips);
+        return hipGetLastError();
+      }
+    }
   }
   if (kOnlyFull || p.n % BN == 0)
     hipLaunchKernelGGL((qkv_decode_kernel<BITS, RT, RSPLIT, VEC, WAVES, true, XR>), grid, block, 0, stream, p,
@@ -527,13 +543,17 @@ hipError_t launch_split_k(const QkvProblem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// m <= 8, whole 64-column strips, 16 waves owning 3 or 4 groups each: all of
-// a wave's groups in flight, x through direct LDS loads
+// m <= 8, n % 4 == 0, 16 waves owning 3 or 4 groups each: all of a wave's
+// groups in flight, x through direct LDS loads
 template <int NG>
 hipError_t launch_all_groups(const QkvProblem& p, hipStream_t stream) {
-  const uint32_t nstrips = p.n / 64;
-  hipLaunchKernelGGL((qkv_decode_kernel<4, 1, 1, 4, 16, true, 8, false, NG>), dim3(3 * nstrips), dim3(16 * kWave), 0,
-                     stream, p, nstrips);
+  const uint32_t nstrips = (p.n + 63) / 64;
+  if (p.n % 64 == 0)
+    hipLaunchKernelGGL((qkv_decode_kernel<4, 1, 1, 4, 16, true, 8, false, NG>), dim3(3 * nstrips),
+                       dim3(16 * kWave), 0, stream, p, nstrips);
+  else
+    hipLaunchKernelGGL((qkv_decode_kernel<4, 1, 1, 4, 16, false, 8, false, NG>), dim3(3 * nstrips),
+                       dim3(16 * kWave), 0, stream, p, nstrips);
   return hipGetLastError();
 }
 
@@ -544,7 +564,7 @@ hipError_t launch_decode_bits(const QkvProblem& p, hipStream_t stream) {
     // n = 4096: k = 5120 11.9 -> 11.1 us, 6144 12.7 -> 11.6, 8192 15.1 ->
     // 14.7); from 33 to 39 groups most waves own two and it gains nothing.
     const uint32_t groups = p.k / kGroup;
-    if (p.m <= 8 && p.n % 64 == 0 && groups >= 40 && groups <= 64)
+    if (p.m <= 8 && p.n % 4 == 0 && groups >= 40 && groups <= 64)
       return groups <= 48 ? launch_all_groups<3>(p, stream) : launch_all_groups<4>(p, stream);
   }
   // INT8 words are twice the registers per group: 16-wave workgroups fit

@@ -82,6 +82,9 @@ def test_tiny_config_all_outputs():
     # split-K with n % 64 != 0 but n % 4 == 0: whole-vector loads on every strip, the last strip's
     # lanes past n loading the last valid columns (decode width, and K > 4096)
     (8, 4088, 4096), (5, 1000, 4096), (16, 4040, 4608), (30, 1004, 512),
+    # the same with trimmed loads past a wave's groups (m <= 16, k > 4096) and with every group of a
+    # wave in flight (m <= 8, 40 to 64 groups)
+    (8, 1004, 4480), (16, 1000, 4480), (5, 1000, 6144), (8, 4088, 8192), (1, 100, 7168),
     # n % 4 != 0: column-by-column loads, columns past n loading column n - 1
     (8, 4095, 4096), (13, 1001, 640), (40, 999, 384),
     # four sets of waves over 64-row tiles, one output per workgroup: ragged rows and columns,
