@@ -28,8 +28,8 @@ def qkv_on_gpu(x, w, s, bits=4, **kw):
     return [to_host(o) for o in outs]
 
 
-# Forms of the tile kernel (waves per set, rows per tile, sets of waves), as kaio_qkv_plan reports them.
-# (waves per set, rows per tile, sets of waves, outputs per workgroup)
+# Forms of the tile kernel as kaio_qkv_plan reports them: (waves per set, rows per tile, sets of
+# waves, outputs per workgroup)
 TILE_FORMS = [(8, 128, 1, 3), (8, 96, 1, 3), (4, 128, 2, 3), (4, 96, 2, 3), (4, 64, 2, 3), (4, 128, 1, 3),
               (4, 96, 1, 3), (4, 64, 1, 3), (4, 128, 2, 1), (4, 96, 2, 1), (4, 128, 1, 1), (4, 96, 1, 1),
               (4, 64, 4, 1)]

@@ -148,6 +148,22 @@ def test_every_tile_form(form, aligned):
     print(f"{form} {M}x{N}x{K}: max |d|/tol = {worst:.3f}")
 
 
+@pytest.mark.parametrize("M,N,K", [(8, 4088, 4096), (8, 4095, 4096), (16, 1000, 4480), (8, 4088, 8192),
+                                   (5, 1004, 6144), (30, 996, 512)])
+def test_ragged_columns_match_the_padded_problem(M, N, K):
+    # split-K on a partial last strip (n % 64 != 0; whole-vector loads with the lanes past n
+    # loading the last columns, or column-by-column loads for n % 4 != 0, on the two-chunk,
+    # trimmed and all-groups forms): the columns below n are bit-identical to those of the same
+    # problem padded to whole strips (MFMA columns do not mix and the reduction order does not
+    # depend on n)
+    Np = (N + 63) // 64 * 64
+    full = workloads.qkv_inputs(M, Np, K, seed=M * 13 + N + K)
+    ragged = qkv_on_gpu(full.x, [a[:, :N] for a in full.w], [a[:, :N] for a in full.s])
+    padded = qkv_on_gpu(full.x, full.w, full.s)
+    for r, p in zip(ragged, padded):
+        assert np.array_equal(r.view(np.uint16), p[:, :N].view(np.uint16))
+
+
 @pytest.mark.parametrize("M", [8, 40, 200])
 def test_non_finite_inputs_stay_in_their_rows(M):
     # IEEE propagation, row by row: a NaN in x row 1 makes that row NaN everywhere; +inf in row 2
