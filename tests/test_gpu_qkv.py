@@ -164,6 +164,20 @@ def test_ragged_columns_match_the_padded_problem(M, N, K):
         assert np.array_equal(r.view(np.uint16), p[:, :N].view(np.uint16))
 
 
+@pytest.mark.parametrize("M,N,K", [(2048, 4095, 1024), (100, 4092, 4096), (40, 4090, 4096), (300, 1001, 512)])
+def test_tile_columns_match_the_padded_problem(M, N, K):
+    # the tile kernel with n % 8 != 0 (4-byte weight loads, column-guarded scales and stores) in the
+    # three-output, one-output and four-set forms: the columns below n are bit-identical to those
+    # of the same problem padded to n % 128 == 0, which runs the same form with 16-byte loads
+    Np = (N + 127) // 128 * 128
+    assert form_of(kaio.kaio_qkv_plan(M, N, K)) == form_of(kaio.kaio_qkv_plan(M, Np, K))
+    full = workloads.qkv_inputs(M, Np, K, seed=M * 17 + N + K)
+    ragged = qkv_on_gpu(full.x, [a[:, :N] for a in full.w], [a[:, :N] for a in full.s])
+    padded = qkv_on_gpu(full.x, full.w, full.s)
+    for r, p in zip(ragged, padded):
+        assert np.array_equal(r.view(np.uint16), p[:, :N].view(np.uint16))
+
+
 @pytest.mark.parametrize("M", [8, 40, 200])
 def test_non_finite_inputs_stay_in_their_rows(M):
     # IEEE propagation, row by row: a NaN in x row 1 makes that row NaN everywhere; +inf in row 2
