@@ -89,7 +89,7 @@ constexpr uint32_t kDecodeMaxM = KAIO_SK_MAXM;   // the split-K kernel covers m 
 constexpr bool qkv_split_k(uint32_t m, uint32_t k, uint32_t bits) {
   return m <= kDecodeMaxM && !(m > 32 && bits == 4 && (k / 128) % 4 == 0);
 }
-// Above it and up to kOneOutMaxM rows the tile kernel runs with one output per
+// Above kDecodeMaxM and up to kOneOutMaxM rows the tile kernel runs with one output per
 // workgroup: 4 waves x 16 columns, 96-row tiles up to 96 rows and 128-row
 // tiles beyond, the groups split over two sets of waves when their count is
 // even.  At n = k = 4096 that is 192 workgroups where the three-output forms
