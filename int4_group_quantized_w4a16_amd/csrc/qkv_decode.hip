@@ -24,8 +24,10 @@
 //   m = 8, n = k = 4096.
 // * Split-K across the waves (wave w takes groups [wG/W, (w+1)G/W)); each
 //   wave streams its groups GCHUNK at a time through two register buffers,
-//   the next chunk's loads in flight while the current chunk computes.  No
-//   load sits under a branch (see the main loop).
+//   the next chunk's loads in flight while the current chunk computes, or,
+//   from 40 to 64 groups at m <= 8, issues all of its groups' loads at once
+//   with x in LDS by direct loads.  No load sits under a branch (see the main
+//   loop); a partial last strip loads clamped columns (see the body).
 // * INT4 unpack once per word whatever RT is: with one row tile, in
 //   nibble-interleaved k order (9 VALU ops per word) with the x fragments
 //   permuted to the same order in registers; with two or more, in k order
@@ -40,8 +42,9 @@
 // are chosen per m so that the register file holds two chunks plus the
 // accumulators without spilling and the reduction buffer stays at 64 KiB
 // (plus 68 KiB of x slices): m <= 16: 1 x 1, 64, 16 (8 x rows kept when
-// m <= 8); m <= 32: 2 x 1, 64, 8; m <= 64: 2 x 2, 64, 8.  Larger m runs the tile
-// kernel, which unpacks each word once per tile of 96 or 128 rows.
+// m <= 8); m <= 32: 2 x 1, 64, 8; m <= 64: 2 x 2, 64, 8.  Larger m (and INT4
+// from m = 33 when the group count divides by 4) runs the tile kernel, which
+// unpacks each word once per tile of 64, 96 or 128 rows.
 
 #include <type_traits>
 
