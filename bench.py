@@ -12,9 +12,9 @@ line carries:
                    the fraction against the peak at that clock, and against
                    MFMA work alone timed the same way (``mfma_alone``: the rate
                    the matrix cores sustain at the power limit);
-* ``secondary``    decode (8 rows, weights rotated over 21 sets so every call
-                   streams from HBM) next to a plain streaming read of the same
-                   bytes, batched decode, the W8A16 sibling (decode and
+* ``secondary``    the tiny 16x512x512 QKV (latency), decode (8 rows, weights
+                   rotated over 21 sets so every call streams from HBM) next to
+                   a plain streaming read of the same bytes, batched decode, the W8A16 sibling (decode and
                    prefill), the dense 4096^3 GEMM and its backward, and the
                    dequant backward (f32 and bf16, [16384, 8192], g=128) next to
                    a plain copy of the same bytes -- each against its own roof,
@@ -614,6 +614,23 @@ def main():
     })
     del x, w, s, outs
 
+    # ---- tiny QKV (16 x 512 x 512): a latency figure, calls replayed from a HIP graph -----------
+    if args.only in ("all", "decode"):
+        c = workloads.QKV_TINY
+        tin = workloads.qkv_inputs(c["M"], c["N"], c["K"], c["seed"])
+        xt, wt, stt = t(tin.x), [t(a) for a in tin.w], [t(a) for a in tin.s]
+        ot = [torch.empty((c["M"], c["N"]), dtype=torch.float16, device=dev) for _ in range(3)]
+        tms = timed_graph(lambda i: kaio.kaio_qkv_w4a16(xt, *wt, *stt, *ot), 64, replays, stream)
+        host["tiny"] = [o.cpu().numpy() for o in ot]
+        pl = kaio.kaio_qkv_plan(c["M"], c["N"], c["K"])
+        log(f"[bench] tiny QKV 16x512x512: {tms * 1e3:.2f} us/call")
+        secondary["qkv_tiny"] = {
+            "workload": "x f16[16,512], 3x packed int4 u32[64,512], 3x f16 scales [4,512] -> Q,K,V f16[16,512]",
+            "us_per_call": round(tms * 1e3, 3), "bound": "latency",
+            "tflops": round(2.0 * c["M"] * c["N"] * c["K"] * 3 / (tms * 1e-3) / 1e12, 3),
+            "form": pl["kernel"], "timing": "64 calls per HIP graph replay"}
+        del xt, wt, stt, ot
+
     # ---- decode, rotated weights, and the plain read of the same bytes ----------------
     if args.only in ("all", "decode", "batched"):
         c = workloads.QKV_DECODE
@@ -828,12 +845,17 @@ def cpu_leg(result, secondary, host, inp, workloads):
     if "prefill" in host:
         result["roofline"]["parity"] = qkv_parity(host["prefill"], inp)
         log(f"[bench] prefill parity (all outputs): {result['roofline']['parity']}")
-    # tiny QKV: the oracle only (the GPU side is latency, covered by the tests)
+    # tiny QKV: the oracle on the full problem, and the GPU's outputs against it
     c = workloads.QKV_TINY
     tin = workloads.qkv_inputs(c["M"], c["N"], c["K"], c["seed"])
     sec, _ = best_of(lambda: qkv_project(tin.x, tin.w, tin.s, with_abs=False), 3)
-    secondary["qkv_tiny_cpu_oracle"] = oracle_entry(2.0 * c["M"] * c["N"] * c["K"] * 3 / sec / 1e9, "GFLOP/s", sec,
-                                                   "tiny QKV 16x512x512, full problem, best of 3")
+    tiny_oracle = oracle_entry(2.0 * c["M"] * c["N"] * c["K"] * 3 / sec / 1e9, "GFLOP/s", sec,
+                               "tiny QKV 16x512x512, full problem, best of 3")
+    if "tiny" in host:
+        secondary["qkv_tiny"]["cpu_oracle"] = tiny_oracle
+        secondary["qkv_tiny"]["parity"] = qkv_parity(host["tiny"], tin)
+    else:
+        secondary["qkv_tiny_cpu_oracle"] = tiny_oracle
     if "decode" in host:
         c = workloads.QKV_DECODE
         dinp = workloads.qkv_inputs(c["M"], c["N"], c["K"], c["seed"])
