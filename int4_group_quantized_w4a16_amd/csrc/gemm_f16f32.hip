@@ -101,9 +101,10 @@ __device__ __forceinline__ uint32_t tile_swz(uint32_t i) { return kTransposed ? 
 // so that LDS holds both operands as [index][reduction] and every fragment is
 // one 16-byte read.  The forward product is <false, true, float>; the
 // backward products <false, false, f16> (grad_a) and <true, true, f16>
-// (grad_b).  kAligned: both strides and the contiguous extents are multiples
-// of 8 (16-byte chunk loads); any shape otherwise.
-template <bool kAligned, bool kATr, bool kBTr, typename OutT>
+// (grad_b).  kAAligned / kBAligned: that operand's stride and contiguous
+// extent are multiples of 8 (16-byte chunk loads); any shape otherwise (so
+// an odd n leaves a reduction-contiguous A with k % 8 == 0 on chunk loads).
+template <bool kAAligned, bool kBAligned, bool kATr, bool kBTr, typename OutT>
 __global__ void __launch_bounds__(THREADS, 1)
 gemm_reg_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __restrict__ B, uint32_t ldb,
                 OutT* __restrict__ C, uint32_t Mo, uint32_t No, uint32_t R, uint32_t mtiles) {
@@ -127,18 +128,19 @@ gemm_reg_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
 
   uint4 ra[8], rb[8];
   // one operand's next tile into registers: base, stride, first index, index count
-  auto load_op = [&](auto tr, uint4 (&reg)[8], const uint16_t* base, uint32_t ld, uint32_t i0, uint32_t ilim,
-                     uint32_t k0) {
+  auto load_op = [&](auto tr, auto al, uint4 (&reg)[8], const uint16_t* base, uint32_t ld, uint32_t i0,
+                     uint32_t ilim, uint32_t k0) {
+    constexpr bool kAl = decltype(al)::value;
     if constexpr (decltype(tr)::value) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) reg[i] = load8<kAligned>(base, ld, k0 + kq * 8 + i, R, i0 + ib * 8, ilim);
+      for (int i = 0; i < 8; ++i) reg[i] = load8<kAl>(base, ld, k0 + kq * 8 + i, R, i0 + ib * 8, ilim);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint32_t c = i * THREADS + tid;
         const uint32_t row = c >> 3, kc = c & 7;
         const uint32_t gi = i0 + row < ilim ? i0 + row : ilim - 1;   // indices past the end: any valid one
-        reg[i] = load8<kAligned>(base, ld, gi, ilim, k0 + kc * 8, R);
+        reg[i] = load8<kAl>(base, ld, gi, ilim, k0 + kc * 8, R);
       }
     }
   };
@@ -175,8 +177,8 @@ gemm_reg_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
   using ATr = std::integral_constant<bool, kATr>;
   using BT = std::integral_constant<bool, kBTr>;
   auto load_tiles = [&](uint32_t k0) {
-    load_op(ATr{}, ra, A, lda, m0, Mo, k0);
-    load_op(BT{}, rb, B, ldb, n0, No, k0);
+    load_op(ATr{}, std::integral_constant<bool, kAAligned>{}, ra, A, lda, m0, Mo, k0);
+    load_op(BT{}, std::integral_constant<bool, kBAligned>{}, rb, B, ldb, n0, No, k0);
   };
 
   floatx4 acc[TT][TT];
@@ -640,20 +642,29 @@ hipError_t launch_dma_any(const uint16_t* a, uint32_t lda, const uint16_t* b, ui
 }  // namespace
 
 namespace {
-// The register-staged kernel.  kAligned needs both strides and the
-// contiguous extents (the reduction for a reduction-contiguous operand, its
-// index count for an index-contiguous one) to be multiples of 8.
+// The register-staged kernel.  An operand loads 16-byte chunks when its
+// stride and contiguous extent (the reduction for a reduction-contiguous
+// operand, its index count for an index-contiguous one) are multiples of 8.
+template <bool kAAl, bool kBAl, bool kATr, bool kBTr, typename OutT>
+void launch_reg_form(const uint16_t* a, uint32_t lda, const uint16_t* b, uint32_t ldb, OutT* c, uint32_t mo,
+                     uint32_t no, uint32_t r, uint32_t mtiles, uint32_t ntiles, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_reg_kernel<kAAl, kBAl, kATr, kBTr, OutT>), dim3(mtiles * ntiles), dim3(THREADS), 0,
+                     stream, a, lda, b, ldb, c, mo, no, r, mtiles);
+}
 template <bool kATr, bool kBTr, typename OutT>
 hipError_t launch_reg(const uint16_t* a, uint32_t lda, const uint16_t* b, uint32_t ldb, OutT* c, uint32_t mo,
                       uint32_t no, uint32_t r, hipStream_t stream) {
   const uint32_t mtiles = (mo + BM - 1) / BM, ntiles = (no + BN - 1) / BN;
-  const bool aligned = lda % 8 == 0 && ldb % 8 == 0 && (kATr ? mo : r) % 8 == 0 && (kBTr ? no : r) % 8 == 0;
-  if (aligned)
-    hipLaunchKernelGGL((gemm_reg_kernel<true, kATr, kBTr, OutT>), dim3(mtiles * ntiles), dim3(THREADS), 0, stream,
-                       a, lda, b, ldb, c, mo, no, r, mtiles);
+  const bool a_al = lda % 8 == 0 && (kATr ? mo : r) % 8 == 0;
+  const bool b_al = ldb % 8 == 0 && (kBTr ? no : r) % 8 == 0;
+  if (a_al && b_al)
+    launch_reg_form<true, true, kATr, kBTr>(a, lda, b, ldb, c, mo, no, r, mtiles, ntiles, stream);
+  else if (a_al)
+    launch_reg_form<true, false, kATr, kBTr>(a, lda, b, ldb, c, mo, no, r, mtiles, ntiles, stream);
+  else if (b_al)
+    launch_reg_form<false, true, kATr, kBTr>(a, lda, b, ldb, c, mo, no, r, mtiles, ntiles, stream);
   else
-    hipLaunchKernelGGL((gemm_reg_kernel<false, kATr, kBTr, OutT>), dim3(mtiles * ntiles), dim3(THREADS), 0, stream,
-                       a, lda, b, ldb, c, mo, no, r, mtiles);
+    launch_reg_form<false, false, kATr, kBTr>(a, lda, b, ldb, c, mo, no, r, mtiles, ntiles, stream);
   return hipGetLastError();
 }
 }  // namespace
