@@ -60,15 +60,34 @@ __device__ __forceinline__ uint32_t hi_pair(uint32_t r0, uint32_t r1) { return (
 __device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(uint16_t* p, float v) { *p = __builtin_bit_cast(uint16_t, (_Float16)v); }
 
-// Eight consecutive 16-bit elements base[outer * ld + inner .. + 7]; elements
-// at or past (outer_lim, inner_lim) read as zero.  kAligned: ld % 8 == 0 and
-// inner_lim % 8 == 0, so a chunk is wholly inside or outside the matrix and
-// starts 16 bytes aligned (one 16-byte load); otherwise element by element.
-template <bool kAligned>
+// How an operand's 8-element chunks are read.
+//   kLoadAligned: ld % 8 == 0 and the contiguous extent % 8 == 0: a chunk is
+//     wholly inside or outside the matrix and starts 16 bytes aligned.
+//   kLoadClamped: contiguous extent >= 8, any ld: every chunk is one 16-byte
+//     load (2-byte aligned; gfx950 runs with unaligned access enabled and the
+//     compiler emits a single dwordx4 load) from a start clamped into the
+//     matrix; fix8 then moves the wanted elements into place and zeroes those
+//     past the end, once the data has landed.  No load sits under a branch,
+//     so the next stage's loads stay in flight over the MFMAs.
+//   kLoadElement: element by element (contiguous extent < 8).
+constexpr int kLoadElement = 0, kLoadClamped = 1, kLoadAligned = 2;
+
+// Eight consecutive 16-bit elements base[outer * ld + inner .. + 7]; under
+// kLoadAligned and kLoadElement, elements at or past (outer_lim, inner_lim)
+// read as zero; under kLoadClamped the raw load of the clamped chunk, which
+// fix8 with the same indices turns into that.
+template <int kMode>
 __device__ __forceinline__ uint4 load8(const uint16_t* base, size_t ld, uint32_t outer, uint32_t outer_lim,
                                        uint32_t inner, uint32_t inner_lim) {
+  if constexpr (kMode == kLoadClamped) {
+    const uint32_t o = outer < outer_lim ? outer : outer_lim - 1;
+    const uint32_t st = inner + 8 <= inner_lim ? inner : inner_lim - 8;
+    uint4 v;
+    __builtin_memcpy(&v, base + (size_t)o * ld + st, 16);
+    return v;
+  }
   if (outer >= outer_lim) return uint4{0u, 0u, 0u, 0u};
-  if (kAligned) {
+  if constexpr (kMode == kLoadAligned) {
     if (inner >= inner_lim) return uint4{0u, 0u, 0u, 0u};
     return *reinterpret_cast<const uint4*>(base + (size_t)outer * ld + inner);
   }
@@ -77,6 +96,26 @@ __device__ __forceinline__ uint4 load8(const uint16_t* base, size_t ld, uint32_t
   for (int i = 0; i < 8; ++i) h[i] = (inner + i < inner_lim) ? base[(size_t)outer * ld + inner + i] : (uint16_t)0;
   return uint4{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
                h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16)};
+}
+
+// The chunk (outer, inner) from what load8<kLoadClamped> read for it: unchanged
+// inside the matrix; past the end of a row the load started at inner_lim - 8,
+// so the wanted elements sit inner + 8 - inner_lim places up and are shifted
+// down, zeros filling the positions past inner_lim.
+__device__ __forceinline__ uint4 fix8(uint4 v, uint32_t outer, uint32_t outer_lim, uint32_t inner,
+                                      uint32_t inner_lim) {
+  if (outer >= outer_lim || inner >= inner_lim) return uint4{0u, 0u, 0u, 0u};
+  if (inner + 8 <= inner_lim) return v;
+  const uint32_t sh = 16u * (inner + 8 - inner_lim);   // 16 .. 112 bits
+  uint64_t lo = v.x | ((uint64_t)v.y << 32), hi = v.z | ((uint64_t)v.w << 32);
+  if (sh >= 64) {
+    lo = hi >> (sh - 64);
+    hi = 0;
+  } else {
+    lo = (lo >> sh) | (hi << (64 - sh));
+    hi >>= sh;
+  }
+  return uint4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
 }
 
 // LDS swizzle of an operand tile [256 indices][8 reduction chunks]: chunk kc
@@ -101,10 +140,8 @@ __device__ __forceinline__ uint32_t tile_swz(uint32_t i) { return kTransposed ? 
 // so that LDS holds both operands as [index][reduction] and every fragment is
 // one 16-byte read.  The forward product is <false, true, float>; the
 // backward products <false, false, f16> (grad_a) and <true, true, f16>
-// (grad_b).  kAAligned / kBAligned: that operand's stride and contiguous
-// extent are multiples of 8 (16-byte chunk loads); any shape otherwise (so
-// an odd n leaves a reduction-contiguous A with k % 8 == 0 on chunk loads).
-template <bool kAAligned, bool kBAligned, bool kATr, bool kBTr, typename OutT>
+// (grad_b).  kAMode / kBMode: how each operand's chunks are read (kLoad*).
+template <int kAMode, int kBMode, bool kATr, bool kBTr, typename OutT>
 __global__ void __launch_bounds__(THREADS, 1)
 gemm_reg_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __restrict__ B, uint32_t ldb,
                 OutT* __restrict__ C, uint32_t Mo, uint32_t No, uint32_t R, uint32_t mtiles) {
@@ -130,7 +167,7 @@ gemm_reg_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
   // one operand's next tile into registers: base, stride, first index, index count
   auto load_op = [&](auto tr, auto al, uint4 (&reg)[8], const uint16_t* base, uint32_t ld, uint32_t i0,
                      uint32_t ilim, uint32_t k0) {
-    constexpr bool kAl = decltype(al)::value;
+    constexpr int kAl = decltype(al)::value;
     if constexpr (decltype(tr)::value) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) reg[i] = load8<kAl>(base, ld, k0 + kq * 8 + i, R, i0 + ib * 8, ilim);
@@ -176,9 +213,23 @@ gemm_reg_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
   };
   using ATr = std::integral_constant<bool, kATr>;
   using BT = std::integral_constant<bool, kBTr>;
+  using AMode = std::integral_constant<int, kAMode>;
+  using BMode = std::integral_constant<int, kBMode>;
   auto load_tiles = [&](uint32_t k0) {
-    load_op(ATr{}, std::integral_constant<bool, kAAligned>{}, ra, A, lda, m0, Mo, k0);
-    load_op(BT{}, std::integral_constant<bool, kBAligned>{}, rb, B, ldb, n0, No, k0);
+    load_op(ATr{}, AMode{}, ra, A, lda, m0, Mo, k0);
+    load_op(BT{}, BMode{}, rb, B, ldb, n0, No, k0);
+  };
+  // the clamped loads' fixes, same indices as load_op, after the data landed
+  auto fix_op = [&](auto tr, auto mode, uint4 (&reg)[8], uint32_t i0, uint32_t ilim, uint32_t k0) {
+    if constexpr (decltype(mode)::value == kLoadClamped) {
+      if constexpr (decltype(tr)::value) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) reg[i] = fix8(reg[i], k0 + kq * 8 + i, R, i0 + ib * 8, ilim);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) reg[i] = fix8(reg[i], 0, 1, k0 + ((i * THREADS + tid) & 7) * 8, R);
+      }
+    }
   };
 
   floatx4 acc[TT][TT];
@@ -191,6 +242,8 @@ gemm_reg_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
   if (nk > 0) load_tiles(0);
   for (uint32_t it = 0; it < nk; ++it) {
     __syncthreads();            // previous tile fully consumed
+    fix_op(ATr{}, AMode{}, ra, m0, Mo, it * BK);
+    fix_op(BT{}, BMode{}, rb, n0, No, it * BK);
     store_op(ATr{}, ra, sm.a);
     store_op(BT{}, rb, sm.b);
     __syncthreads();            // tile visible
@@ -642,29 +695,34 @@ hipError_t launch_dma_any(const uint16_t* a, uint32_t lda, const uint16_t* b, ui
 }  // namespace
 
 namespace {
-// The register-staged kernel.  An operand loads 16-byte chunks when its
-// stride and contiguous extent (the reduction for a reduction-contiguous
-// operand, its index count for an index-contiguous one) are multiples of 8.
-template <bool kAAl, bool kBAl, bool kATr, bool kBTr, typename OutT>
+// The register-staged kernel.  An operand reads aligned 16-byte chunks when
+// its stride and contiguous extent (the reduction for a reduction-contiguous
+// operand, its index count for an index-contiguous one) are multiples of 8,
+// clamped 16-byte chunks when that extent is at least 8, and elements
+// otherwise (then both operands do, keeping the instantiations few).
+template <int kAM, int kBM, bool kATr, bool kBTr, typename OutT>
 void launch_reg_form(const uint16_t* a, uint32_t lda, const uint16_t* b, uint32_t ldb, OutT* c, uint32_t mo,
                      uint32_t no, uint32_t r, uint32_t mtiles, uint32_t ntiles, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_reg_kernel<kAAl, kBAl, kATr, kBTr, OutT>), dim3(mtiles * ntiles), dim3(THREADS), 0,
+  hipLaunchKernelGGL((gemm_reg_kernel<kAM, kBM, kATr, kBTr, OutT>), dim3(mtiles * ntiles), dim3(THREADS), 0,
                      stream, a, lda, b, ldb, c, mo, no, r, mtiles);
 }
 template <bool kATr, bool kBTr, typename OutT>
 hipError_t launch_reg(const uint16_t* a, uint32_t lda, const uint16_t* b, uint32_t ldb, OutT* c, uint32_t mo,
                       uint32_t no, uint32_t r, hipStream_t stream) {
   const uint32_t mtiles = (mo + BM - 1) / BM, ntiles = (no + BN - 1) / BN;
-  const bool a_al = lda % 8 == 0 && (kATr ? mo : r) % 8 == 0;
-  const bool b_al = ldb % 8 == 0 && (kBTr ? no : r) % 8 == 0;
-  if (a_al && b_al)
-    launch_reg_form<true, true, kATr, kBTr>(a, lda, b, ldb, c, mo, no, r, mtiles, ntiles, stream);
-  else if (a_al)
-    launch_reg_form<true, false, kATr, kBTr>(a, lda, b, ldb, c, mo, no, r, mtiles, ntiles, stream);
-  else if (b_al)
-    launch_reg_form<false, true, kATr, kBTr>(a, lda, b, ldb, c, mo, no, r, mtiles, ntiles, stream);
+  const uint32_t a_ext = kATr ? mo : r, b_ext = kBTr ? no : r;
+  const int a_mode = lda % 8 == 0 && a_ext % 8 == 0 ? kLoadAligned : (a_ext >= 8 ? kLoadClamped : kLoadElement);
+  const int b_mode = ldb % 8 == 0 && b_ext % 8 == 0 ? kLoadAligned : (b_ext >= 8 ? kLoadClamped : kLoadElement);
+  if (a_mode == kLoadElement || b_mode == kLoadElement)
+    launch_reg_form<kLoadElement, kLoadElement, kATr, kBTr>(a, lda, b, ldb, c, mo, no, r, mtiles, ntiles, stream);
+  else if (a_mode == kLoadAligned && b_mode == kLoadAligned)
+    launch_reg_form<kLoadAligned, kLoadAligned, kATr, kBTr>(a, lda, b, ldb, c, mo, no, r, mtiles, ntiles, stream);
+  else if (a_mode == kLoadAligned)
+    launch_reg_form<kLoadAligned, kLoadClamped, kATr, kBTr>(a, lda, b, ldb, c, mo, no, r, mtiles, ntiles, stream);
+  else if (b_mode == kLoadAligned)
+    launch_reg_form<kLoadClamped, kLoadAligned, kATr, kBTr>(a, lda, b, ldb, c, mo, no, r, mtiles, ntiles, stream);
   else
-    launch_reg_form<false, false, kATr, kBTr>(a, lda, b, ldb, c, mo, no, r, mtiles, ntiles, stream);
+    launch_reg_form<kLoadClamped, kLoadClamped, kATr, kBTr>(a, lda, b, ldb, c, mo, no, r, mtiles, ntiles, stream);
   return hipGetLastError();
 }
 }  // namespace

@@ -44,7 +44,10 @@ def test_identity_and_exact_integers():
                                    (300, 264, 128), (513, 136, 192), (40, 520, 64), (257, 8, 256),
                                    # k % 8 == 0, k % 64 != 0: the direct-to-LDS path with a ragged last stage
                                    (300, 264, 200), (257, 136, 72), (64, 64, 8), (1, 8, 8), (513, 520, 4104),
-                                   (40, 1024, 4000)])
+                                   (40, 1024, 4000),
+                                   # n and k both off multiples of 8 (both operands on clamped 16-byte
+                                   # chunk loads), down to a reduction of one partial chunk
+                                   (300, 259, 100), (70, 1001, 515), (33, 17, 9), (9, 8, 11)])
 def test_ragged_shapes(M, N, K):
     a, b = workloads.gemm_inputs(M, N, K, seed=M + N + K)
     c, t = gemm(a, b)
