@@ -219,9 +219,13 @@ gemm_reg_kernel(const uint16_t* __restrict__ A, uint32_t lda, const uint16_t* __
     load_op(ATr{}, AMode{}, ra, A, lda, m0, Mo, k0);
     load_op(BT{}, BMode{}, rb, B, ldb, n0, No, k0);
   };
-  // the clamped loads' fixes, same indices as load_op, after the data landed
+  // the clamped loads' fixes, same indices as load_op, after the data landed;
+  // only a stage that reaches past the reduction, or an index-contiguous
+  // operand's last tile, holds chunks to fix (a uniform branch elsewhere)
   auto fix_op = [&](auto tr, auto mode, uint4 (&reg)[8], uint32_t i0, uint32_t ilim, uint32_t k0) {
     if constexpr (decltype(mode)::value == kLoadClamped) {
+      static_assert(BM == 32 * 8 && BN == 32 * 8, "an index-contiguous tile is 32 lanes of 8 indices");
+      if (k0 + BK <= R && (!decltype(tr)::value || i0 + 32 * 8 <= ilim)) return;
       if constexpr (decltype(tr)::value) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) reg[i] = fix8(reg[i], k0 + kq * 8 + i, R, i0 + ib * 8, ilim);
